@@ -1,0 +1,189 @@
+/*
+ * vws.h -- C ABI of libvws, the MI355X (gfx950) vocab-wide softmax reductions.
+ *
+ * The operations are the per-row reductions of DeepSpeed PR #8838 "Add Triton
+ * kernels for vocab-parallel logprobs, entropy and KL" (first and second commit
+ * messages, PR description) and the fused linear-logp of RL-Kernel PR #208
+ * "[Feat][Kernel] Add TP Fused linear logp Triton" (PR body, "Implementation").
+ * Each row of logits z (length V) is reduced in one read to the online
+ * statistics m = max z, S = sum e^(z-m), and a max-centred weighted sum W, from
+ * which the per-token result is formed (second commit message of PR #8838):
+ *
+ *   log-probability   logp = (z_t - m) - log S
+ *   entropy           H    = log S - W_H / S,   W_H = sum e^(z-m) (z-m)
+ *   KL(A||B)          KL   = W_K / S_A - log S_A + log S_B,
+ *                     W_K  = sum e^(a-m_a) ((a-m_a) - (b-m_b)),
+ *                     and +inf when B is -inf on a column where A is not
+ *                     (support flag decided on the logits).
+ *
+ * Forward KL(B||A) is the same call with the arguments swapped.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All data pointers are DEVICE pointers on the current HIP device; the
+ *   caller owns every buffer. Work is enqueued on `stream` (a hipStream_t; NULL
+ *   is the null stream). No call synchronises, allocates device memory or
+ *   keeps state between calls; calls are reentrant.
+ * - Return value: VWS_OK (0) or a negative vws_status. Argument and layout
+ *   errors are detected on the host before anything is launched; VWS_EHIP
+ *   reports a failed launch. Data-dependent conditions never produce a status
+ *   (that would need a host synchronisation); they produce the values below.
+ * - N = 0 is a no-op returning VWS_OK. V must be >= 1.
+ * - Outputs (logp, H, kl) are fp32 [N]; `stats` is fp32 [N, 2] holding
+ *   (m, log S) per row, or [N, 4] holding (m_a, log S_A, m_b, log S_B) for KL.
+ *   The backward recomputes p = exp((z - m) - log S) from these, so it needs
+ *   exactly the stats its forward wrote (max-centred: m and log S are kept as
+ *   two numbers, never folded into one log-sum-exp).
+ * - Gradients are written contiguous [N, V] in the input dtype; a bf16 gradient
+ *   is the round-to-nearest-even of the fp32 value (review comment on
+ *   PR #8838). `g` is the fp32 upstream gradient, element r at g[r * g_stride]
+ *   (g_stride = 0 broadcasts one value, as an expanded scalar does).
+ * - Outputs must not alias inputs.
+ *
+ * Values for degenerate rows (readings of the pages; the pages list these
+ * cases but not their values):
+ * - a -inf entry has probability 0, adds nothing, and gets gradient 0
+ *   (zero-weight rule: the "0 x inf" review thread of PR #8838 and its fix);
+ * - a row with no entry above -inf, or with a NaN or +inf entry, gives NaN
+ *   outputs and NaN gradients;
+ * - logprobs: t == ignore_index gives 0 and a zero gradient row; any other t
+ *   outside [0, V) gives NaN and a NaN gradient row;
+ * - KL rows with the support flag set give +inf; their gradient w.r.t. A is
+ *   NaN in every column and their gradient w.r.t. B is g (p_B - p_A).
+ */
+#ifndef VWS_H
+#define VWS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(_WIN32)
+#define VWS_API
+#else
+#define VWS_API __attribute__((visibility("default")))
+#endif
+
+typedef enum vws_status {
+  VWS_OK = 0,
+  VWS_EINVAL = -1,     /* null pointer, negative or inconsistent size, bad op code */
+  VWS_EDTYPE = -2,     /* unknown dtype, or A and B of different dtypes */
+  VWS_ELAYOUT = -3,    /* col_stride != 1, negative stride, misaligned pointer, address overflow */
+  VWS_EWORKSPACE = -4, /* workspace smaller than vws_workspace_bytes() */
+  VWS_EHIP = -5        /* a HIP launch failed */
+} vws_status;
+
+typedef enum vws_dtype { VWS_F32 = 0, VWS_BF16 = 1 } vws_dtype;
+
+typedef enum vws_op { VWS_OP_LOGPROBS = 0, VWS_OP_ENTROPY = 1, VWS_OP_KL = 2 } vws_op;
+
+/*
+ * A logical [N, V] matrix of logits whose rows are addressed with up to two
+ * strides, so that a slice such as logits[:, :-1, :] is read in place (second
+ * commit message of PR #8838). Row r = r_o * n_inner + r_i (0 <= r_i < n_inner)
+ * starts at element  r_o * s_outer + r_i * s_inner  of `data`; columns are
+ * contiguous (col_stride must be 1; other layouts are copied by the caller).
+ * Strides are in elements and must be >= 0. `data` must be aligned to the
+ * element size. N = n_outer * n_inner.
+ */
+typedef struct vws_rows {
+  const void* data;
+  int32_t dtype; /* vws_dtype */
+  int64_t n_outer, n_inner;
+  int64_t s_outer, s_inner;
+  int64_t V;
+  int64_t col_stride;
+} vws_rows;
+
+/* int64 target ids with the same row decomposition: id of row r at
+ * data[r_o * s_outer + r_i * s_inner]. */
+typedef struct vws_ids {
+  const int64_t* data;
+  int64_t s_outer, s_inner;
+} vws_ids;
+
+/*
+ * Bytes of workspace the forward of `op` needs for N rows of V columns with the
+ * given split_hint. The forward splits each row's vocabulary over P workgroups
+ * when N is small (the pages' cross-shard combine -- MAX of m, re-centring of
+ * S and W on it, SUM -- done inside one GPU); the partial statistics go to
+ * the workspace and a second kernel merges them. split_hint: 0 = automatic,
+ * 1 = never split, P > 1 = split into P parts (capped at ceil(V/8)).
+ * Returns 0 when no workspace is needed, (size_t)-1 for invalid arguments.
+ */
+VWS_API size_t vws_workspace_bytes(int op, int64_t N, int64_t V, int split_hint);
+
+/* Number of vocabulary parts the forward uses for these sizes (1 = no split). */
+VWS_API int vws_split_parts(int op, int64_t N, int64_t V, int split_hint);
+
+/*
+ * Per-token log-probability of the target (first commit message of PR #8838;
+ * RL-Kernel PR #208 returns (logp, lse) from its forward).
+ *   z       logits [N, V]
+ *   t       target ids (same row decomposition as z)
+ *   logp    out fp32 [N]
+ *   stats   out fp32 [N, 2] = (m, log S)
+ *   ws      workspace of ws_bytes >= vws_workspace_bytes(VWS_OP_LOGPROBS, ...)
+ */
+VWS_API int vws_logprobs_fwd(const vws_rows* z, const vws_ids* t, int64_t ignore_index, float* logp,
+                             float* stats, void* ws, size_t ws_bytes, int split_hint, void* stream);
+
+/*
+ * dz_j = g (1[j = t] - p_j) (RL-Kernel PR #208, review nitpick on the chunked
+ * backward, which prints dz = -exp(logits - lse); dz[target] += 1; dz *= g).
+ *   stats   the [N, 2] stats written by vws_logprobs_fwd on the same z
+ *   dz      out [N, V] contiguous, dtype of z
+ */
+VWS_API int vws_logprobs_bwd(const vws_rows* z, const vws_ids* t, int64_t ignore_index, const float* stats,
+                             const float* g, int64_t g_stride, void* dz, void* stream);
+
+/*
+ * Entropy H = -sum p log p = log S - W_H / S in one read (second commit
+ * message of PR #8838).
+ *   H       out fp32 [N];   stats out fp32 [N, 2] = (m, log S)
+ */
+VWS_API int vws_entropy_fwd(const vws_rows* z, float* H, float* stats, void* ws, size_t ws_bytes, int split_hint,
+                            void* stream);
+
+/*
+ * dz_j = -g p_j (log p_j + H), derived from the definition of H (the pages do
+ * not print it); 0 where z_j = -inf.
+ *   stats, H   as written by vws_entropy_fwd;   dz out [N, V] contiguous
+ */
+VWS_API int vws_entropy_bwd(const vws_rows* z, const float* stats, const float* H, const float* g, int64_t g_stride,
+                            void* dz, void* stream);
+
+/*
+ * KL(A||B) = W_K / S_A - log S_A + log S_B in one read of both inputs, +inf
+ * when B masks a column that A supports (second commit message and review
+ * comment of PR #8838). A and B must have equal N, V and dtype; their strides
+ * may differ.
+ *   kl      out fp32 [N];   stats out fp32 [N, 4] = (m_a, log S_A, m_b, log S_B)
+ */
+VWS_API int vws_kl_fwd(const vws_rows* a, const vws_rows* b, float* kl, float* stats, void* ws, size_t ws_bytes,
+                       int split_hint, void* stream);
+
+/*
+ * da_j = g p_A,j (log p_A,j - log p_B,j - KL)  (0 where a_j = -inf),
+ * db_j = g (p_B,j - p_A,j); derived from the definition of KL (not printed on
+ * the pages). da or db may be NULL to skip that gradient (e.g. a frozen
+ * teacher).
+ *   stats, kl  as written by vws_kl_fwd;   da, db out [N, V] contiguous
+ */
+VWS_API int vws_kl_bwd(const vws_rows* a, const vws_rows* b, const float* stats, const float* kl, const float* g,
+                       int64_t g_stride, void* da, void* db, void* stream);
+
+/* Static description of a status code. */
+VWS_API const char* vws_strerror(int status);
+
+/* ABI version (major * 100 + minor). */
+VWS_API int vws_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VWS_H */

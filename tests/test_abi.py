@@ -1,0 +1,108 @@
+"""The C ABI on the host: symbols, pure host queries, argument validation (no GPU needed).
+
+Every call here either is a pure host function or fails validation before
+anything is launched, so it runs without a device.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from vocab_wide_softmax_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vws.h")
+
+EINVAL, EDTYPE, ELAYOUT, EWORKSPACE = -1, -2, -3, -4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"VWS_API\s+[\w\s\*]+?\b(vws_\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.vws_version() == 100
+
+
+def test_strerror(L):
+    for s in (0, EINVAL, EDTYPE, ELAYOUT, EWORKSPACE, -5):
+        assert len(B.strerror(s)) >= 2
+    assert B.strerror(-99) == "unknown status"
+
+
+def test_split_parts_and_workspace(L):
+    # long rows, few of them: split; many rows: no split
+    assert B.split_parts(B.OP_ENTROPY, 1024, 75968) == 8
+    assert B.split_parts(B.OP_ENTROPY, 8192, 75968) == 1
+    assert B.split_parts(B.OP_KL, 64, 1024, 4) == 4
+    assert B.split_parts(B.OP_KL, 64, 1024, 16) == 16
+    assert B.split_parts(B.OP_KL, 64, 1024, 1) == 1
+    assert B.split_parts(B.OP_KL, 3, 20, 64) == 3  # capped at ceil(V/8) groups
+    assert B.workspace_bytes(B.OP_ENTROPY, 8192, 75968) == 0
+    assert B.workspace_bytes(B.OP_ENTROPY, 1024, 75968) == 1024 * 8 * 3 * 4
+    assert B.workspace_bytes(B.OP_KL, 1024, 75968) == 1024 * 8 * 6 * 4
+    assert B.workspace_bytes(B.OP_KL, 0, 75968) == 0
+    with pytest.raises(ValueError):
+        B.workspace_bytes(7, 10, 10)
+    with pytest.raises(ValueError):
+        B.workspace_bytes(B.OP_KL, 10, 0)
+
+
+def _rows(data=0x1000, dtype=B.VWS_BF16, n_outer=4, n_inner=1, s_outer=64, s_inner=0, V=64, col_stride=1):
+    return B.vws_rows(data, dtype, n_outer, n_inner, s_outer, s_inner, V, col_stride)
+
+
+def _ent(L, r, out=0x2000, stats=0x3000, ws=None, nb=0, hint=0):
+    return L.vws_entropy_fwd(ctypes.byref(r), out, stats, ws, nb, hint, None)
+
+
+def test_forward_validation(L):
+    assert _ent(L, _rows(dtype=5)) == EDTYPE
+    assert _ent(L, _rows(V=0)) == EINVAL
+    assert _ent(L, _rows(n_outer=-1)) == EINVAL
+    assert _ent(L, _rows(col_stride=2)) == ELAYOUT
+    assert _ent(L, _rows(s_outer=-64)) == ELAYOUT
+    assert _ent(L, _rows(data=0x1001)) == ELAYOUT  # bf16 needs 2-byte alignment
+    assert _ent(L, _rows(data=0)) == EINVAL
+    assert _ent(L, _rows(), out=0) == EINVAL
+    assert _ent(L, _rows(), stats=0) == EINVAL
+    assert _ent(L, _rows(), out=0x2002) == ELAYOUT
+    assert _ent(L, _rows(), hint=-1) == EINVAL
+    assert _ent(L, _rows(s_outer=2 ** 62, n_outer=8)) == ELAYOUT  # address overflow
+    # empty batch: no-op, even with null pointers
+    assert _ent(L, _rows(n_outer=0, data=0), out=0, stats=0) == 0
+    # workspace too small / missing when a split is requested
+    assert _ent(L, _rows(V=4096, s_outer=4096), hint=4) == EWORKSPACE
+    assert _ent(L, _rows(V=4096, s_outer=4096), ws=0x4000, nb=16, hint=4) == EWORKSPACE
+
+
+def test_kl_and_logprobs_validation(L):
+    a, b = _rows(), _rows(dtype=B.VWS_F32)
+    assert L.vws_kl_fwd(ctypes.byref(a), ctypes.byref(b), 0x2000, 0x3000, None, 0, 0, None) == EDTYPE
+    b = _rows(V=32, s_outer=32)
+    assert L.vws_kl_fwd(ctypes.byref(a), ctypes.byref(b), 0x2000, 0x3000, None, 0, 0, None) == EINVAL
+    b = _rows(n_outer=3)
+    assert L.vws_kl_fwd(ctypes.byref(a), ctypes.byref(b), 0x2000, 0x3000, None, 0, 0, None) == EINVAL
+    # kl backward with neither gradient requested is a no-op
+    a = _rows()
+    assert L.vws_kl_bwd(ctypes.byref(a), ctypes.byref(a), 0x3000, 0x2000, 0x5000, 1, None, None, None) == 0
+    assert L.vws_kl_bwd(ctypes.byref(a), ctypes.byref(a), 0x3000, 0x2000, 0x5000, -1, 0x6000, None, None) == EINVAL
+    t = B.vws_ids(0, 1, 0)
+    assert L.vws_logprobs_fwd(ctypes.byref(a), ctypes.byref(t), -100, 0x2000, 0x3000, None, 0, 0, None) == EINVAL
+    t = B.vws_ids(0x7004, 1, 0)  # int64 ids need 8-byte alignment
+    assert L.vws_logprobs_fwd(ctypes.byref(a), ctypes.byref(t), -100, 0x2000, 0x3000, None, 0, 0, None) == ELAYOUT
+    assert L.vws_logprobs_bwd(ctypes.byref(a), None, -100, 0x3000, 0x5000, 1, 0x6000, None) == EINVAL
+    assert L.vws_entropy_bwd(ctypes.byref(a), 0x3000, 0, 0x5000, 1, 0x6000, None) == EINVAL  # H missing
+    assert L.vws_entropy_bwd(ctypes.byref(a), 0x3000, 0x2000, 0x5000, 1, 0x6001, None) == ELAYOUT

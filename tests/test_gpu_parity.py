@@ -1,0 +1,135 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Workloads (vocab_wide_softmax_amd.workloads):
+* tiny      64 x 1024 fp32 pair (row 0 offset +1e4, row 1 with 16 masked B
+            columns): every element, all four ops, forward and backward, with
+            the automatic launch and with the vocabulary forced into 4 and 16
+            parts (the in-GPU combine).
+* pair1024  1024 x 75968 bf16 pair (5% rows +1e4, 1% rows with 64 masked B
+            columns): every element of every output and gradient; the
+            automatic launch splits the vocabulary here.
+* pair8192  8192 x 75968 bf16 pair: the full launch the benchmark times,
+            checked on sampled rows (row 0, offset rows, masked rows, random).
+* shifted   [4, 2049, 75968] fp32 pair read through base[:, :-1, :]: the full
+            in-place strided launch, checked on sampled rows.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from parity import OPS, check_parity, f64, run_device, run_oracle
+from vocab_wide_softmax_amd import binding as B
+from vocab_wide_softmax_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _host_inputs(wl):
+    a, b, t = wl.views()
+    return f64(a.reshape(-1, a.shape[-1])), f64(b.reshape(-1, b.shape[-1])), t.reshape(-1).numpy()
+
+
+def _to_device(wl, device):
+    a_base = wl.a_base.to(device)
+    b_base = wl.b_base.to(device)
+    ids_base = wl.ids_base.to(device)
+    a, b, t = wl.views(a_base, b_base, ids_base)
+    return a, b, t
+
+
+@pytest.fixture(scope="module")
+def tiny(device):
+    wl = W.workload("tiny")
+    return wl, _to_device(wl, device), _host_inputs(wl)
+
+
+@pytest.mark.parametrize("split", [0, 4, 16])
+@pytest.mark.parametrize("op", OPS)
+def test_tiny_all_elements(tiny, op, split):
+    wl, (a, b, t), (ha, hb, ht) = tiny
+    g = wl.g[op]
+    print("tiny", op, "split", split, flush=True)
+    dev = run_device(op, a, b, t, g.to(a.device), split_hint=split)
+    ora = run_oracle(op, ha, hb, ht, g.double().numpy())
+    check_parity(dev, ora, "f32", "tiny %s split %d" % (op, split))
+
+
+@pytest.fixture(scope="module")
+def pair1024(device):
+    wl = W.workload("pair1024")
+    return wl, _to_device(wl, device), _host_inputs(wl)
+
+
+@pytest.mark.parametrize("op", OPS)
+def test_pair1024_all_elements(pair1024, op):
+    wl, (a, b, t), (ha, hb, ht) = pair1024
+    assert B.split_parts(B.OP_KL, a.shape[0], a.shape[1]) > 1  # the split-vocab path is what runs here
+    print("pair1024", op, flush=True)
+    dev = run_device(op, a, b, t, wl.g[op].to(a.device))
+    ora = run_oracle(op, ha, hb, ht, wl.g[op].double().numpy())
+    reps = check_parity(dev, ora, "bf16", "pair1024 " + op)
+    print({k: (v["strict_miss"], round(v["worst"], 3)) for k, v in reps.items()}, flush=True)
+
+
+def _sample_rows(wl, n, k=24, seed=5):
+    rng = np.random.default_rng(seed)
+    rows = {0, n - 1}
+    rows.update(wl.offset_rows[:8].tolist())
+    rows.update(wl.mask_rows[:8].tolist())
+    rows.update(rng.choice(n, size=k, replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+def _sampled_parity(wl, device, ops, grad_kind):
+    a, b, t = _to_device(wl, device)
+    n = a.shape[0] if a.dim() == 2 else a.shape[0] * a.shape[1]
+    rows = _sample_rows(wl, n)
+    ha_all, hb_all, ht_all = wl.views()
+    V = ha_all.shape[-1]
+    ha = f64(ha_all.reshape(-1, V)[rows]) if not wl.shifted else f64(ha_all.reshape(n, V)[rows])
+    hb = f64(hb_all.reshape(-1, V)[rows]) if not wl.shifted else f64(hb_all.reshape(n, V)[rows])
+    ht = ht_all.reshape(-1)[rows].numpy()
+    idx = torch.from_numpy(rows).to(device)
+    for op in ops:
+        print(wl.name, op, flush=True)
+        g = wl.g[op]
+        full = run_device_sampled(op, a, b, t, g.to(device), idx)
+        ora = run_oracle(op, ha, hb, ht, g.double().numpy()[rows])
+        check_parity(full, ora, grad_kind, "%s %s" % (wl.name, op))
+        torch.cuda.empty_cache()
+
+
+def run_device_sampled(op, a, b, t, g, idx):
+    """Run the full launch, keep only the sampled rows (gathered on the device)."""
+    res = {}
+    if op == "logprobs":
+        out, stats = B.logprobs_fwd(a, t, -100)
+        grads = (B.logprobs_bwd(a, t, stats, g, -100),)
+    elif op == "entropy":
+        out, stats = B.entropy_fwd(a)
+        grads = (B.entropy_bwd(a, stats, out, g),)
+    else:
+        x, y = (a, b) if op == "kl_ab" else (b, a)
+        out, stats = B.kl_fwd(x, y)
+        grads = B.kl_bwd(x, y, stats, out, g)
+    V = a.shape[-1]
+    res["out"] = f64(out.reshape(-1)[idx])
+    res["stats"] = f64(stats[idx])
+    res["grads"] = [f64(d.reshape(-1, V)[idx]) for d in grads]
+    del grads, out, stats
+    return res
+
+
+@pytest.mark.slow
+def test_pair8192_sampled_rows(device):
+    wl = W.workload("pair8192")
+    _sampled_parity(wl, device, OPS, "bf16")
+
+
+@pytest.mark.slow
+def test_shifted_fp32_sampled_rows(device):
+    wl = W.workload("shifted")
+    a, _, _ = wl.views()
+    assert not a.is_contiguous()
+    _sampled_parity(wl, device, ("entropy", "kl_ab", "logprobs"), "f32")

@@ -1,0 +1,241 @@
+"""ctypes binding of libvws (include/vws.h): argument marshalling only.
+
+Every step of the computation runs in the HIP kernels of libvws.so; this
+module turns torch tensors into the C descriptors, allocates outputs (torch
+owns device memory), passes torch's current HIP stream, and raises
+``VwsError`` on a non-zero status. There is no fallback: if libvws.so is
+missing or fails to load, the first call raises.
+
+Layouts: logits are [N, V] or [B, S, V] tensors whose last dimension is
+contiguous; the leading dimensions are passed as (at most) two row strides,
+so a view like ``logits[:, :-1, :]`` is read in place. Targets and upstream
+gradients have the shape of the logits without the last dimension.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvws.so")
+
+VWS_F32, VWS_BF16 = 0, 1
+OP_LOGPROBS, OP_ENTROPY, OP_KL = 0, 1, 2
+_DTYPES = {torch.float32: VWS_F32, torch.bfloat16: VWS_BF16}
+
+
+class VwsError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__("%s failed with status %d: %s" % (fn, status, msg))
+        self.status = status
+
+
+class vws_rows(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("n_outer", ctypes.c_int64),
+        ("n_inner", ctypes.c_int64),
+        ("s_outer", ctypes.c_int64),
+        ("s_inner", ctypes.c_int64),
+        ("V", ctypes.c_int64),
+        ("col_stride", ctypes.c_int64),
+    ]
+
+
+class vws_ids(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("s_outer", ctypes.c_int64), ("s_inner", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libvws.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError("libvws.so not built at %s (run python -m vocab_wide_softmax_amd.build)" % _LIB_PATH)
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I64, I32, SZ, VP, FP = (ctypes.POINTER, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p,
+                                   ctypes.c_void_p)
+        R, T = P(vws_rows), P(vws_ids)
+        sig = {
+            "vws_workspace_bytes": (SZ, [I32, I64, I64, I32]),
+            "vws_split_parts": (I32, [I32, I64, I64, I32]),
+            "vws_logprobs_fwd": (I32, [R, T, I64, FP, FP, VP, SZ, I32, VP]),
+            "vws_logprobs_bwd": (I32, [R, T, I64, FP, FP, I64, VP, VP]),
+            "vws_entropy_fwd": (I32, [R, FP, FP, VP, SZ, I32, VP]),
+            "vws_entropy_bwd": (I32, [R, FP, FP, FP, I64, VP, VP]),
+            "vws_kl_fwd": (I32, [R, R, FP, FP, VP, SZ, I32, VP]),
+            "vws_kl_bwd": (I32, [R, R, FP, FP, FP, I64, VP, VP, VP]),
+            "vws_strerror": (ctypes.c_char_p, [I32]),
+            "vws_version": (I32, []),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def strerror(status):
+    return lib().vws_strerror(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise VwsError(fn, status, strerror(status))
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def rows(t: torch.Tensor) -> vws_rows:
+    """Descriptor of a [N, V] or [B, S, V] logits tensor (last dim contiguous)."""
+    if t.dtype not in _DTYPES:
+        raise TypeError("logits must be float32 or bfloat16, got %s" % t.dtype)
+    if t.dim() == 2:
+        n_outer, n_inner, s_outer, s_inner = t.shape[0], 1, t.stride(0), 0
+    elif t.dim() == 3:
+        n_outer, n_inner, s_outer, s_inner = t.shape[0], t.shape[1], t.stride(0), t.stride(1)
+    else:
+        raise ValueError("logits must be 2-D [N, V] or 3-D [B, S, V]")
+    col_stride = t.stride(-1) if t.shape[-1] > 1 else 1
+    return vws_rows(t.data_ptr(), _DTYPES[t.dtype], n_outer, n_inner, s_outer, s_inner, t.shape[-1], col_stride)
+
+
+def ids(t: torch.Tensor, like: torch.Tensor) -> vws_ids:
+    """Descriptor of int64 targets shaped like ``like`` without its last dim."""
+    if t.dtype != torch.int64:
+        raise TypeError("targets must be int64")
+    if tuple(t.shape) != tuple(like.shape[:-1]):
+        raise ValueError("targets shape %s does not match logits %s" % (tuple(t.shape), tuple(like.shape)))
+    if t.dim() == 1:
+        return vws_ids(t.data_ptr(), t.stride(0), 0)
+    return vws_ids(t.data_ptr(), t.stride(0), t.stride(1))
+
+
+def _n_rows(z):
+    n = 1
+    for s in z.shape[:-1]:
+        n *= s
+    return n
+
+
+def _g_arg(g: torch.Tensor, like: torch.Tensor):
+    """(tensor, stride) for the fp32 upstream gradient: flat stride 1 or 0 (broadcast)."""
+    if g.dtype != torch.float32:
+        g = g.float()
+    if g.numel() == 1 or all(s == 0 for s in g.stride()):
+        return g, 0
+    g = g.reshape(-1)
+    if g.numel() != _n_rows(like):
+        raise ValueError("upstream gradient has %d elements, expected %d" % (g.numel(), _n_rows(like)))
+    if g.stride(0) != 1:
+        g = g.contiguous()
+    return g, 1
+
+
+def _outputs(z, k):
+    n = _n_rows(z)
+    out = torch.empty(z.shape[:-1], dtype=torch.float32, device=z.device)
+    stats = torch.empty((n, k), dtype=torch.float32, device=z.device)
+    return out, stats
+
+
+def workspace_bytes(op, n, v, split_hint=0):
+    r = lib().vws_workspace_bytes(op, n, v, split_hint)
+    if r == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid workspace query")
+    return r
+
+
+def split_parts(op, n, v, split_hint=0):
+    return lib().vws_split_parts(op, n, v, split_hint)
+
+
+def _workspace(op, z, split_hint):
+    nbytes = workspace_bytes(op, _n_rows(z), z.shape[-1], split_hint)
+    if nbytes == 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device=z.device), nbytes
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+# ------------------------------------------------------------------- entry points
+
+def logprobs_fwd(z, t, ignore_index=-100, split_hint=0):
+    """(logp fp32 [N...], stats fp32 [N, 2]) -- vws_logprobs_fwd."""
+    L = lib()
+    logp, stats = _outputs(z, 2)
+    ws, nb = _workspace(OP_LOGPROBS, z, split_hint)
+    r, ti = rows(z), ids(t, z)
+    _check("vws_logprobs_fwd", L.vws_logprobs_fwd(ctypes.byref(r), ctypes.byref(ti), ignore_index, _ptr(logp),
+                                                  _ptr(stats), _ptr(ws), nb, split_hint, _stream(z.device)))
+    return logp, stats
+
+
+def logprobs_bwd(z, t, stats, g, ignore_index=-100):
+    """dz [shape of z, contiguous, dtype of z] -- vws_logprobs_bwd."""
+    L = lib()
+    g, gs = _g_arg(g, z)
+    dz = torch.empty(z.shape, dtype=z.dtype, device=z.device)
+    r, ti = rows(z), ids(t, z)
+    _check("vws_logprobs_bwd", L.vws_logprobs_bwd(ctypes.byref(r), ctypes.byref(ti), ignore_index, _ptr(stats),
+                                                  _ptr(g), gs, _ptr(dz), _stream(z.device)))
+    return dz
+
+
+def entropy_fwd(z, split_hint=0):
+    """(H fp32 [N...], stats fp32 [N, 2]) -- vws_entropy_fwd."""
+    L = lib()
+    H, stats = _outputs(z, 2)
+    ws, nb = _workspace(OP_ENTROPY, z, split_hint)
+    r = rows(z)
+    _check("vws_entropy_fwd", L.vws_entropy_fwd(ctypes.byref(r), _ptr(H), _ptr(stats), _ptr(ws), nb, split_hint,
+                                                _stream(z.device)))
+    return H, stats
+
+
+def entropy_bwd(z, stats, H, g):
+    """dz -- vws_entropy_bwd."""
+    L = lib()
+    g, gs = _g_arg(g, z)
+    dz = torch.empty(z.shape, dtype=z.dtype, device=z.device)
+    r = rows(z)
+    _check("vws_entropy_bwd", L.vws_entropy_bwd(ctypes.byref(r), _ptr(stats), _ptr(H), _ptr(g), gs, _ptr(dz),
+                                                _stream(z.device)))
+    return dz
+
+
+def kl_fwd(a, b, split_hint=0):
+    """(KL(A||B) fp32 [N...], stats fp32 [N, 4]) -- vws_kl_fwd."""
+    L = lib()
+    kl, stats = _outputs(a, 4)
+    ws, nb = _workspace(OP_KL, a, split_hint)
+    ra, rb = rows(a), rows(b)
+    _check("vws_kl_fwd", L.vws_kl_fwd(ctypes.byref(ra), ctypes.byref(rb), _ptr(kl), _ptr(stats), _ptr(ws), nb,
+                                      split_hint, _stream(a.device)))
+    return kl, stats
+
+
+def kl_bwd(a, b, stats, kl, g, need_a=True, need_b=True):
+    """(da or None, db or None) -- vws_kl_bwd."""
+    L = lib()
+    g, gs = _g_arg(g, a)
+    da = torch.empty(a.shape, dtype=a.dtype, device=a.device) if need_a else None
+    db = torch.empty(b.shape, dtype=b.dtype, device=b.device) if need_b else None
+    ra, rb = rows(a), rows(b)
+    _check("vws_kl_bwd", L.vws_kl_bwd(ctypes.byref(ra), ctypes.byref(rb), _ptr(stats), _ptr(kl), _ptr(g), gs,
+                                      _ptr(da), _ptr(db), _stream(a.device)))
+    return da, db

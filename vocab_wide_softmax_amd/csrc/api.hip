@@ -1,0 +1,251 @@
+// api.hip -- the C ABI of libvws (declared in include/vws.h): argument and
+// layout validation on the host, then asynchronous launches on the caller's
+// stream. Nothing here allocates, synchronises or keeps state.
+#include <limits.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "vws.h"
+
+namespace {
+
+using vws::BwdArgs;
+using vws::FwdArgs;
+
+int elem_size(int dtype) { return dtype == VWS_BF16 ? 2 : 4; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Validates one logits descriptor; on success *N is its row count.
+int check_rows(const vws_rows* r, int64_t* N) {
+  if (!r) return VWS_EINVAL;
+  if (r->dtype != VWS_F32 && r->dtype != VWS_BF16) return VWS_EDTYPE;
+  if (r->n_outer < 0 || r->n_inner < 0 || r->V < 1) return VWS_EINVAL;
+  if (r->V > (int64_t)INT32_MAX - 4096) return VWS_EINVAL;  // column and group indexes are 32-bit
+  if (r->col_stride != 1) return VWS_ELAYOUT;
+  if (r->s_outer < 0 || r->s_inner < 0) return VWS_ELAYOUT;
+  int64_t n;
+  if (!mul_ok(r->n_outer, r->n_inner, &n)) return VWS_EINVAL;
+  if (n > ((int64_t)1 << 40)) return VWS_EINVAL;
+  *N = n;
+  if (n == 0) return VWS_OK;
+  if (!r->data) return VWS_EINVAL;
+  const int es = elem_size(r->dtype);
+  if (!aligned(r->data, (uintptr_t)es)) return VWS_ELAYOUT;
+  // last element touched: (n_outer-1) s_outer + (n_inner-1) s_inner + V - 1, in bytes
+  int64_t o1, o2, last;
+  if (!mul_ok(r->n_outer - 1, r->s_outer, &o1) || !mul_ok(r->n_inner - 1, r->s_inner, &o2)) return VWS_ELAYOUT;
+  if (o1 > INT64_MAX - o2) return VWS_ELAYOUT;
+  last = o1 + o2;
+  if (last > INT64_MAX - r->V) return VWS_ELAYOUT;
+  last += r->V;
+  if (last > INT64_MAX / es) return VWS_ELAYOUT;
+  return VWS_OK;
+}
+
+int check_ids(const vws_ids* t) {
+  if (!t || !t->data) return VWS_EINVAL;
+  if (t->s_outer < 0 || t->s_inner < 0) return VWS_ELAYOUT;
+  if (!aligned(t->data, 8)) return VWS_ELAYOUT;
+  return VWS_OK;
+}
+
+// 16-byte vector loads are legal for every row of r.
+bool rows_vec_ok(const vws_rows* r) {
+  const int es = elem_size(r->dtype);
+  if (!aligned(r->data, 16)) return false;
+  if (r->n_outer > 1 && (r->s_outer * es) % 16 != 0) return false;
+  if (r->n_inner > 1 && (r->s_inner * es) % 16 != 0) return false;
+  return true;
+}
+
+bool out_vec_ok(const void* out, int64_t N, int64_t V, int es) {
+  if (!out) return true;
+  if (!aligned(out, 16)) return false;
+  return N <= 1 || (V * es) % 16 == 0;
+}
+
+vws::RowsDev rows_dev(const vws_rows* r) {
+  return vws::RowsDev{static_cast<const char*>(r->data), r->n_inner > 0 ? r->n_inner : 1, r->s_outer, r->s_inner};
+}
+
+vws::IdsDev ids_dev(const vws_ids* t) { return vws::IdsDev{t ? t->data : nullptr, t ? t->s_outer : 0, t ? t->s_inner : 0}; }
+
+int state_floats(int op) { return op == VWS_OP_KL ? 6 : 3; }
+
+// Vocabulary parts per row for the forward (see vws_split_parts in vws.h).
+int parts_for(int op, int64_t N, int64_t V, int hint) {
+  const int64_t G = (V + 7) / 8;
+  int64_t P;
+  if (hint == 1) {
+    P = 1;
+  } else if (hint > 1) {
+    P = hint < G ? hint : G;
+  } else {
+    // Aim for >= 8192 workgroups (the chip holds about 2048 of 256 lanes at
+    // once), keeping every part at least 512 groups (4096 columns) long.
+    const int64_t want = N >= 8192 ? 1 : (8192 + N - 1) / (N > 0 ? N : 1);
+    const int64_t cap = G / 512 > 1 ? G / 512 : 1;
+    P = want < cap ? want : cap;
+  }
+  if (P > 1024) P = 1024;
+  if (P < 1) P = 1;
+  // no empty parts
+  const int64_t gpp = (G + P - 1) / P;
+  P = (G + gpp - 1) / gpp;
+  (void)op;
+  return (int)P;
+}
+
+int fwd_common(int op, const vws_rows* a, const vws_rows* b, const vws_ids* t, int64_t ignore_index, float* out,
+               float* stats, void* ws, size_t ws_bytes, int split_hint, void* stream) {
+  int64_t N, Nb;
+  int rc = check_rows(a, &N);
+  if (rc) return rc;
+  if (op == VWS_OP_KL) {
+    if ((rc = check_rows(b, &Nb))) return rc;
+    if (b->dtype != a->dtype) return VWS_EDTYPE;
+    if (Nb != N || b->V != a->V || b->n_inner != a->n_inner) return VWS_EINVAL;
+  }
+  if (split_hint < 0) return VWS_EINVAL;
+  if (N == 0) return VWS_OK;
+  if (op == VWS_OP_LOGPROBS && (rc = check_ids(t))) return rc;
+  if (!out || !stats) return VWS_EINVAL;
+  if (!aligned(out, 4) || !aligned(stats, 4)) return VWS_ELAYOUT;
+  const int P = parts_for(op, N, a->V, split_hint);
+  if (N * (int64_t)P > (int64_t)INT32_MAX) return VWS_EINVAL;
+  const size_t need = P > 1 ? (size_t)N * (size_t)P * (size_t)state_floats(op) * sizeof(float) : 0;
+  if (need > 0 && (!ws || ws_bytes < need)) return VWS_EWORKSPACE;
+  if (need > 0 && !aligned(ws, 4)) return VWS_ELAYOUT;
+
+  FwdArgs p{};
+  p.a = rows_dev(a);
+  if (op == VWS_OP_KL) p.b = rows_dev(b);
+  p.ids = ids_dev(op == VWS_OP_LOGPROBS ? t : nullptr);
+  p.N = N;
+  p.V = a->V;
+  p.ignore_index = ignore_index;
+  p.parts = P;
+  const int64_t G = (a->V + 7) / 8;
+  p.groups_per_part = (int32_t)((G + P - 1) / P);
+  p.out = out;
+  p.stats = stats;
+  p.ws = static_cast<float*>(ws);
+  const bool vec = rows_vec_ok(a) && (op != VWS_OP_KL || rows_vec_ok(b));
+  hipError_t e = vws::launch_fwd(op, p, a->dtype, vec, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VWS_OK : VWS_EHIP;
+}
+
+int bwd_common(int op, const vws_rows* a, const vws_rows* b, const vws_ids* t, int64_t ignore_index,
+               const float* stats, const float* res, const float* g, int64_t g_stride, void* da, void* db,
+               void* stream) {
+  int64_t N, Nb;
+  int rc = check_rows(a, &N);
+  if (rc) return rc;
+  if (op == VWS_OP_KL) {
+    if ((rc = check_rows(b, &Nb))) return rc;
+    if (b->dtype != a->dtype) return VWS_EDTYPE;
+    if (Nb != N || b->V != a->V || b->n_inner != a->n_inner) return VWS_EINVAL;
+  }
+  if (g_stride < 0) return VWS_EINVAL;
+  if (N == 0) return VWS_OK;
+  if (op == VWS_OP_LOGPROBS && (rc = check_ids(t))) return rc;
+  if (!stats || !g || (op != VWS_OP_LOGPROBS && !res)) return VWS_EINVAL;
+  if (op != VWS_OP_KL && !da) return VWS_EINVAL;
+  if (op == VWS_OP_KL && !da && !db) return VWS_OK;
+  if (!aligned(stats, 4) || !aligned(g, 4) || (res && !aligned(res, 4))) return VWS_ELAYOUT;
+  const int es = elem_size(a->dtype);
+  if (!aligned(da, es) || !aligned(db, es)) return VWS_ELAYOUT;
+  int64_t nv, bytes;
+  if (!mul_ok(N, a->V, &nv) || !mul_ok(nv, es, &bytes)) return VWS_EINVAL;
+  const int32_t tpr = vws::bwd_tiles_per_row(a->V);
+  if (N * (int64_t)tpr > (int64_t)INT32_MAX) return VWS_EINVAL;
+
+  BwdArgs p{};
+  p.a = rows_dev(a);
+  if (op == VWS_OP_KL) p.b = rows_dev(b);
+  p.ids = ids_dev(op == VWS_OP_LOGPROBS ? t : nullptr);
+  p.N = N;
+  p.V = a->V;
+  p.ignore_index = ignore_index;
+  p.tiles_per_row = tpr;
+  p.stats = stats;
+  p.res = res;
+  p.g = g;
+  p.g_stride = g_stride;
+  p.da = static_cast<char*>(da);
+  p.db = static_cast<char*>(db);
+  const bool vec = rows_vec_ok(a) && (op != VWS_OP_KL || rows_vec_ok(b)) && out_vec_ok(da, N, a->V, es) &&
+                   out_vec_ok(db, N, a->V, es);
+  hipError_t e = vws::launch_bwd(op, p, a->dtype, vec, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VWS_OK : VWS_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+VWS_API size_t vws_workspace_bytes(int op, int64_t N, int64_t V, int split_hint) {
+  if (op < VWS_OP_LOGPROBS || op > VWS_OP_KL || N < 0 || V < 1 || split_hint < 0) return (size_t)-1;
+  if (N == 0) return 0;
+  const int P = parts_for(op, N, V, split_hint);
+  return P > 1 ? (size_t)N * (size_t)P * (size_t)state_floats(op) * sizeof(float) : 0;
+}
+
+VWS_API int vws_split_parts(int op, int64_t N, int64_t V, int split_hint) {
+  if (op < VWS_OP_LOGPROBS || op > VWS_OP_KL || N < 0 || V < 1 || split_hint < 0) return VWS_EINVAL;
+  return parts_for(op, N, V, split_hint);
+}
+
+VWS_API int vws_logprobs_fwd(const vws_rows* z, const vws_ids* t, int64_t ignore_index, float* logp, float* stats,
+                             void* ws, size_t ws_bytes, int split_hint, void* stream) {
+  return fwd_common(VWS_OP_LOGPROBS, z, nullptr, t, ignore_index, logp, stats, ws, ws_bytes, split_hint, stream);
+}
+
+VWS_API int vws_logprobs_bwd(const vws_rows* z, const vws_ids* t, int64_t ignore_index, const float* stats,
+                             const float* g, int64_t g_stride, void* dz, void* stream) {
+  return bwd_common(VWS_OP_LOGPROBS, z, nullptr, t, ignore_index, stats, nullptr, g, g_stride, dz, nullptr, stream);
+}
+
+VWS_API int vws_entropy_fwd(const vws_rows* z, float* H, float* stats, void* ws, size_t ws_bytes, int split_hint,
+                            void* stream) {
+  return fwd_common(VWS_OP_ENTROPY, z, nullptr, nullptr, 0, H, stats, ws, ws_bytes, split_hint, stream);
+}
+
+VWS_API int vws_entropy_bwd(const vws_rows* z, const float* stats, const float* H, const float* g, int64_t g_stride,
+                            void* dz, void* stream) {
+  return bwd_common(VWS_OP_ENTROPY, z, nullptr, nullptr, 0, stats, H, g, g_stride, dz, nullptr, stream);
+}
+
+VWS_API int vws_kl_fwd(const vws_rows* a, const vws_rows* b, float* kl, float* stats, void* ws, size_t ws_bytes,
+                       int split_hint, void* stream) {
+  return fwd_common(VWS_OP_KL, a, b, nullptr, 0, kl, stats, ws, ws_bytes, split_hint, stream);
+}
+
+VWS_API int vws_kl_bwd(const vws_rows* a, const vws_rows* b, const float* stats, const float* kl, const float* g,
+                       int64_t g_stride, void* da, void* db, void* stream) {
+  return bwd_common(VWS_OP_KL, a, b, nullptr, 0, stats, kl, g, g_stride, da, db, stream);
+}
+
+VWS_API const char* vws_strerror(int status) {
+  switch (status) {
+    case VWS_OK: return "ok";
+    case VWS_EINVAL: return "invalid argument (null pointer, negative or inconsistent size)";
+    case VWS_EDTYPE: return "unsupported or mismatched dtype";
+    case VWS_ELAYOUT: return "unsupported layout (col_stride != 1, negative stride, misaligned pointer or address overflow)";
+    case VWS_EWORKSPACE: return "workspace too small";
+    case VWS_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+VWS_API int vws_version(void) { return 100; }
+
+}  // extern "C"

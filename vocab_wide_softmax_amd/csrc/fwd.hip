@@ -1,0 +1,293 @@
+// fwd.hip -- single-read forward of logprobs, entropy and KL(A||B).
+//
+// One workgroup streams one row (or one vocabulary part of one row). Each
+// lane keeps the running state of device.h over the groups of 8 columns it
+// owns: group g of part [g0, g1) belongs to lane (g - g0) mod BLOCK, and a
+// lane takes its groups in increasing order, U groups per batch. The element
+// to lane map and the order of operations do not depend on the dtype, so bf16
+// and fp32 inputs holding the same values give bit-identical results (review
+// comment on PR #8838: "bf16 and fp32 inputs give bitwise identical outputs").
+//
+// Per batch the lane takes the batch max first and rescales its state once
+// (second commit message of PR #8838: the weighted sums are "rescaled the same
+// way as the sum-exp" when the max grows), then accumulates e = exp(z - m),
+// S += e, W += e (z - m) with the zero-weight product. Lanes are merged by a
+// butterfly over the wave, waves through LDS in wave order ("lane
+// re-centring", fix commit of the 0 x inf thread).
+//
+// With P > 1 parts per row the workgroup writes its part's state to the
+// workspace and combine_kernel merges the parts in part order and finalizes:
+// the pages' MAX / re-centre / SUM across tensor-parallel shards, done inside
+// one GPU.
+#include "device.h"
+#include "launch.h"
+
+namespace vws {
+
+// ---- per-batch updates -------------------------------------------------------
+
+template <bool WITH_W, int U>
+__device__ __forceinline__ void update1(State1& st, const float (&x)[U][8]) {
+  float bm = -kInf;
+#pragma unroll
+  for (int k = 0; k < U; ++k)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bm = fmaxf(bm, x[k][j]);
+  if (bm > st.m) {
+    const float d = st.m - bm;  // -inf when the state is empty
+    const float s = expf_fast(d);
+    if (WITH_W) st.W = mul0(s, st.W + d * st.S);
+    st.S = s * st.S;
+    st.m = bm;
+  }
+  const float ref = ref_of(st.m);
+#pragma unroll
+  for (int k = 0; k < U; ++k)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float d = x[k][j] - ref;
+      const float e = expf_fast(d);
+      st.S += e;
+      if (WITH_W) st.W += mul0(e, d);
+    }
+}
+
+template <int U>
+__device__ __forceinline__ void update_kl(StateKL& st, const float (&xa)[U][8], const float (&xb)[U][8]) {
+  float bma = -kInf, bmb = -kInf, bminb = kInf;
+#pragma unroll
+  for (int k = 0; k < U; ++k)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      bma = fmaxf(bma, xa[k][j]);
+      bmb = fmaxf(bmb, xb[k][j]);
+      bminb = fminf(bminb, xb[k][j]);
+    }
+  if (bma > st.ma) {
+    const float d = st.ma - bma;
+    const float s = expf_fast(d);
+    st.W = mul0(s, st.W + d * st.Sa);
+    st.Sa = s * st.Sa;
+    st.ma = bma;
+  }
+  if (bmb > st.mb) {
+    // W holds e_a ((a - ref_a) - (b - ref_b)); moving ref_b up by delta adds delta * S_A.
+    const float delta = bmb - ref_of(st.mb);
+    st.W += mul0(st.Sa, delta);
+    st.Sb = expf_fast(st.mb - bmb) * st.Sb;
+    st.mb = bmb;
+  }
+  if (bminb == -kInf) {  // some B entry is masked: decide the support flag on the logits
+    uint32_t f = 0;
+#pragma unroll
+    for (int k = 0; k < U; ++k)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f |= (xa[k][j] > -kInf) & (xb[k][j] == -kInf);
+    st.F |= f;
+  }
+  const float ra = ref_of(st.ma), rb = ref_of(st.mb);
+#pragma unroll
+  for (int k = 0; k < U; ++k)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float da = xa[k][j] - ra;
+      const float db = xb[k][j] - rb;
+      const float ea = expf_fast(da);
+      const float eb = expf_fast(db);
+      st.Sa += ea;
+      st.Sb += eb;
+      st.W += mul0(ea, da - db);
+    }
+}
+
+// ---- finalization of a row from its merged state ----------------------------------
+
+__device__ __forceinline__ double log_d(float S) { return log((double)S); }
+
+template <int DT>
+__device__ void finalize1_logprobs(const FwdArgs& p, int64_t row, const State1& st) {
+  const double logS = log_d(st.S);
+  p.stats[2 * row + 0] = st.m;
+  p.stats[2 * row + 1] = (float)logS;
+  const int64_t t = load_id(p.ids, row, p.a.n_inner);
+  float out;
+  if (t == p.ignore_index) {
+    out = 0.0f;
+  } else if (t < 0 || t >= p.V) {
+    out = __builtin_nanf("");
+  } else {
+    const float zt = load_elem<DT>(row_ptr<DT>(p.a, row), t);
+    out = (float)(((double)zt - (double)st.m) - logS);
+  }
+  p.out[row] = out;
+}
+
+__device__ __forceinline__ void finalize1_entropy(const FwdArgs& p, int64_t row, const State1& st) {
+  const double logS = log_d(st.S);
+  p.stats[2 * row + 0] = st.m;
+  p.stats[2 * row + 1] = (float)logS;
+  p.out[row] = (float)(logS - (double)st.W / (double)st.S);
+}
+
+__device__ __forceinline__ void finalize_kl(const FwdArgs& p, int64_t row, const StateKL& st) {
+  const double lsa = log_d(st.Sa), lsb = log_d(st.Sb);
+  p.stats[4 * row + 0] = st.ma;
+  p.stats[4 * row + 1] = (float)lsa;
+  p.stats[4 * row + 2] = st.mb;
+  p.stats[4 * row + 3] = (float)lsb;
+  float out;
+  if (!(st.Sa > 0.0f) || st.Sb != st.Sb) {  // A has no live entry, or a NaN / +inf reached S
+    out = __builtin_nanf("");
+  } else if (st.F) {
+    out = kInf;
+  } else {
+    out = (float)((double)st.W / (double)st.Sa - lsa + lsb);
+  }
+  p.out[row] = out;
+}
+
+// ---- the streaming kernel -----------------------------------------------------------
+
+template <int OP, int DT, bool VEC, int BLOCK, int U>
+__global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs p) {
+  constexpr int NW = BLOCK / 64;
+  const int32_t parts = p.parts;
+  const int64_t total = p.N * parts;
+  for (int64_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
+  const int64_t row = vb / parts;
+  const int32_t part = (int32_t)(vb - row * parts);
+  const int32_t G = (int32_t)((p.V + 7) / 8);
+  const int32_t g_full = (int32_t)(p.V / 8);
+  const int32_t V = (int32_t)p.V;
+  const int32_t g0 = part * p.groups_per_part;
+  const int32_t g1 = min(G, g0 + p.groups_per_part);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  const char* ra = row_ptr<DT>(p.a, row);
+
+  if constexpr (OP == kKL) {
+    const char* rb = row_ptr<DT>(p.b, row);
+    StateKL st = statekl_init();
+    for (int32_t gb = g0 + tid; gb < g1; gb += BLOCK * U) {
+      float xa[U][8], xb[U][8];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int32_t g = gb + k * BLOCK;
+        if (g < g1) {
+          load_group<DT, VEC>(ra, g, V, g_full, xa[k]);
+          load_group<DT, VEC>(rb, g, V, g_full, xb[k]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xa[k][j] = xb[k][j] = -kInf;
+        }
+      }
+      update_kl<U>(st, xa, xb);
+    }
+    st = wave_reduce_kl(st);
+    __shared__ StateKL red[NW];
+    if (lane == 0) red[wave] = st;
+    __syncthreads();
+    if (tid == 0) {
+      StateKL s = red[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) s = merge_kl(s, red[w]);
+      if (parts == 1) {
+        finalize_kl(p, row, s);
+      } else {
+        float* o = p.ws + vb * 6;
+        o[0] = s.ma; o[1] = s.Sa; o[2] = s.mb; o[3] = s.Sb; o[4] = s.W; o[5] = (float)s.F;
+      }
+    }
+  } else {
+    constexpr bool WW = OP == kEntropy;
+    State1 st = state1_init();
+    for (int32_t gb = g0 + tid; gb < g1; gb += BLOCK * U) {
+      float x[U][8];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int32_t g = gb + k * BLOCK;
+        if (g < g1) {
+          load_group<DT, VEC>(ra, g, V, g_full, x[k]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[k][j] = -kInf;
+        }
+      }
+      update1<WW, U>(st, x);
+    }
+    st = wave_reduce1<WW>(st);
+    __shared__ State1 red[NW];
+    if (lane == 0) red[wave] = st;
+    __syncthreads();
+    if (tid == 0) {
+      State1 s = red[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) s = merge1<WW>(s, red[w]);
+      if (parts == 1) {
+        if (OP == kEntropy) finalize1_entropy(p, row, s);
+        else finalize1_logprobs<DT>(p, row, s);
+      } else {
+        float* o = p.ws + vb * 3;
+        o[0] = s.m; o[1] = s.S; o[2] = s.W;
+      }
+    }
+  }
+  __syncthreads();  // red[] is reused by the next row
+  }
+}
+
+// One thread per row: merge the row's parts in part order, then finalize.
+template <int OP, int DT>
+__global__ __launch_bounds__(256) void combine_kernel(FwdArgs p) {
+  for (int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x; row < p.N; row += (int64_t)gridDim.x * 256) {
+  if constexpr (OP == kKL) {
+    const float* w = p.ws + row * p.parts * 6;
+    StateKL s = statekl_init();
+    for (int i = 0; i < p.parts; ++i, w += 6) {
+      StateKL o{w[0], w[1], w[2], w[3], w[4], w[5] != 0.0f ? 1u : 0u};
+      s = merge_kl(s, o);
+    }
+    finalize_kl(p, row, s);
+  } else {
+    constexpr bool WW = OP == kEntropy;
+    const float* w = p.ws + row * p.parts * 3;
+    State1 s = state1_init();
+    for (int i = 0; i < p.parts; ++i, w += 3) s = merge1<WW>(s, State1{w[0], w[1], w[2]});
+    if (OP == kEntropy) finalize1_entropy(p, row, s);
+    else finalize1_logprobs<DT>(p, row, s);
+  }
+  }
+}
+
+// ---- host-side launch -----------------------------------------------------------------
+
+namespace {
+constexpr int kFwdBlock = 256;
+constexpr int kFwdU = 4;
+
+template <int OP, int DT, bool VEC>
+hipError_t launch_fwd_t(const FwdArgs& p, hipStream_t stream) {
+  const int64_t blocks = grid_cap(p.N * p.parts);
+  hipLaunchKernelGGL((fwd_kernel<OP, DT, VEC, kFwdBlock, kFwdU>), dim3((uint32_t)blocks), dim3(kFwdBlock), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.parts == 1) return e;
+  hipLaunchKernelGGL((combine_kernel<OP, DT>), dim3((uint32_t)grid_cap((p.N + 255) / 256)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int OP>
+hipError_t launch_fwd_op(const FwdArgs& p, int dtype, bool vec, hipStream_t stream) {
+  if (dtype == kBF16) return vec ? launch_fwd_t<OP, kBF16, true>(p, stream) : launch_fwd_t<OP, kBF16, false>(p, stream);
+  return vec ? launch_fwd_t<OP, kF32, true>(p, stream) : launch_fwd_t<OP, kF32, false>(p, stream);
+}
+}  // namespace
+
+hipError_t launch_fwd(int op, const FwdArgs& p, int dtype, bool vec, hipStream_t stream) {
+  switch (op) {
+    case kLogprobs: return launch_fwd_op<kLogprobs>(p, dtype, vec, stream);
+    case kEntropy: return launch_fwd_op<kEntropy>(p, dtype, vec, stream);
+    default: return launch_fwd_op<kKL>(p, dtype, vec, stream);
+  }
+}
+
+}  // namespace vws

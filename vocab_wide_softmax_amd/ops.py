@@ -1,0 +1,73 @@
+"""torch.autograd wrappers over the libvws entry points.
+
+``logprobs(z, t)``, ``entropy(z)`` and ``kl(a, b)`` return fp32 per-token
+values (shape of the logits without the last dim) and differentiate through
+the fused HIP backward kernels. Forward KL(B||A) is ``kl(b, a)``. Temperature,
+masking and normalisation stay with the caller, as on the pages (JSD PR text:
+"Leave temperature, optional T-squared scaling, masking and normalization to
+the caller").
+"""
+
+import torch
+
+from . import binding as B
+
+
+class _Logprobs(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, z, t, ignore_index, split_hint):
+        logp, stats = B.logprobs_fwd(z, t, ignore_index, split_hint)
+        ctx.save_for_backward(z, t, stats)
+        ctx.ignore_index = ignore_index
+        return logp
+
+    @staticmethod
+    def backward(ctx, g):
+        z, t, stats = ctx.saved_tensors
+        dz = B.logprobs_bwd(z, t, stats, g, ctx.ignore_index) if ctx.needs_input_grad[0] else None
+        return dz, None, None, None
+
+
+class _Entropy(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, z, split_hint):
+        H, stats = B.entropy_fwd(z, split_hint)
+        ctx.save_for_backward(z, stats, H)
+        return H
+
+    @staticmethod
+    def backward(ctx, g):
+        z, stats, H = ctx.saved_tensors
+        return (B.entropy_bwd(z, stats, H, g) if ctx.needs_input_grad[0] else None), None
+
+
+class _KL(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, a, b, split_hint):
+        kl, stats = B.kl_fwd(a, b, split_hint)
+        ctx.save_for_backward(a, b, stats, kl)
+        return kl
+
+    @staticmethod
+    def backward(ctx, g):
+        a, b, stats, kl = ctx.saved_tensors
+        na, nb = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        if not (na or nb):
+            return None, None, None
+        da, db = B.kl_bwd(a, b, stats, kl, g, need_a=na, need_b=nb)
+        return da, db, None
+
+
+def logprobs(z, t, ignore_index=-100, split_hint=0):
+    """Per-token log p_t; ``t == ignore_index`` gives 0 and no gradient."""
+    return _Logprobs.apply(z, t, ignore_index, split_hint)
+
+
+def entropy(z, split_hint=0):
+    """Per-token entropy -sum p log p."""
+    return _Entropy.apply(z, split_hint)
+
+
+def kl(a, b, split_hint=0):
+    """Per-token KL(A||B) = sum p_A (log p_A - log p_B); +inf where B masks A's support."""
+    return _KL.apply(a, b, split_hint)
