@@ -1,0 +1,341 @@
+#!/usr/bin/env python3
+"""Benchmark of the vocab-wide softmax hot path on one MI355X.
+
+One step = forward + backward of the four per-token ops the pages measure
+(DeepSpeed PR #8838, first and second commit messages) on the 8192 x 75968
+bf16 logit pair:
+    logprobs(A), entropy(A), KL(A||B) (grads to A and B), KL(B||A) (grads to B and A).
+Inputs are generated on the host (seeded, vocab_wide_softmax_amd.workloads),
+copied to HBM before timing, and every step reruns all eight kernels launches
+(plus nothing else) through the C ABI.
+
+Printed: one JSON line with the step throughput in algorithmic GB/s (bytes the
+single-read method must move: 18 x 1.2447 GB per step), ms per step, the
+per-op split, a roofline object for the dominant kernel (the KL backward,
+timed with HIP events on its stream), and the fp64 oracle's throughput on a
+bounded sample of the same workload on the host cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --calibrate          # plain copies of known size, for counter scaling
+    python bench.py --summarize DIR stats|counters   # condense rocprofv3 output for profiles/
+"""
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd ms + achieved HBM GB/s (% of peak), 8192×75968 bf16 KL/entropy/logp"
+PEAK_GBS = 8000.0
+N_ROWS, V = 8192, 75968
+T_BYTES = N_ROWS * V * 2  # one bf16 [8192, 75968] tensor
+# algorithmic bytes per op (fwd + bwd): logprobs/entropy 1 read + (1 read + 1 write);
+# KL with both gradients 2 reads + (2 reads + 2 writes)
+OP_BYTES = {"logprobs": 3 * T_BYTES, "entropy": 3 * T_BYTES, "kl_ab": 6 * T_BYTES, "kl_ba": 6 * T_BYTES}
+STEP_BYTES = sum(OP_BYTES.values())
+DOMINANT = "kl_bwd"  # KL backward: reads A and B, writes dA and dB
+DOMINANT_BYTES = 4 * T_BYTES
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["vocab_wide_softmax_amd/csrc/bwd.hip", "vocab_wide_softmax_amd/csrc/device.h"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles():
+    """HBM bytes per launch of the dominant kernel from the committed counter summary,
+    or None when it is missing or was taken on different kernel sources."""
+    path = os.path.join(PROFILE_DIR, "kl_bwd_pair8192_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- GPU step
+
+def make_inputs(wl, device):
+    import torch
+
+    from vocab_wide_softmax_amd import workloads as W
+
+    a, b, t = wl.a.to(device), wl.b.to(device), wl.t.to(device)
+    g = {op: wl.g[op].to(device) for op in W.OPS}
+    torch.cuda.synchronize()
+    return wl, a, b, t, g
+
+
+def run_step(B, a, b, t, g, ev=None):
+    """One pass of the hot path. ev: optional dict of (start, end) event lists per op phase."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+
+    def rec(key, i):
+        if ev is not None:
+            ev[key][i].record(stream)
+
+    rec("logprobs_fwd", 0)
+    lp, st = B.logprobs_fwd(a, t, -100)
+    rec("logprobs_fwd", 1)
+    rec("logprobs_bwd", 0)
+    B.logprobs_bwd(a, t, st, g["logprobs"], -100)
+    rec("logprobs_bwd", 1)
+    rec("entropy_fwd", 0)
+    H, st = B.entropy_fwd(a)
+    rec("entropy_fwd", 1)
+    rec("entropy_bwd", 0)
+    B.entropy_bwd(a, st, H, g["entropy"])
+    rec("entropy_bwd", 1)
+    for name, x, y in (("kl_ab", a, b), ("kl_ba", b, a)):
+        rec(name + "_fwd", 0)
+        kl, st = B.kl_fwd(x, y)
+        rec(name + "_fwd", 1)
+        rec(name + "_bwd", 0)
+        B.kl_bwd(x, y, st, kl, g[name])
+        rec(name + "_bwd", 1)
+
+
+PHASES = ["logprobs_fwd", "logprobs_bwd", "entropy_fwd", "entropy_bwd", "kl_ab_fwd", "kl_ab_bwd", "kl_ba_fwd",
+          "kl_ba_bwd"]
+
+
+def gpu_bench(wl, steps, warmup, device):
+    """Warm up, then time exactly `steps` steps (synchronised on both sides). HIP events
+    recorded on the kernels' stream inside the timed steps give the per-phase durations."""
+    import torch
+
+    from vocab_wide_softmax_amd import binding as B
+
+    B.lib()
+    wl, a, b, t, g = make_inputs(wl, device)
+    log("inputs resident in HBM; %d warmup steps" % warmup)
+    for _ in range(warmup):
+        run_step(B, a, b, t, g)
+    evs = [{k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in PHASES}
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run_step(B, a, b, t, g, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / steps
+    per = {k: [ev[k][0].elapsed_time(ev[k][1]) for ev in evs] for k in PHASES}
+    med = {k: sorted(v)[len(v) // 2] for k, v in per.items()}
+    mean = {k: sum(v) / len(v) for k, v in per.items()}
+    return ms_per_step, med, mean
+
+
+# --------------------------------------------------------------------------- CPU oracle
+
+def _oracle_rows(args):
+    import numpy as np
+
+    from oracle import reductions as R
+
+    a, b, t, gs = args
+    R.logprobs_fwd(a, t)
+    R.logprobs_bwd(a, t, gs[0])
+    R.entropy_fwd(a)
+    R.entropy_bwd(a, gs[1])
+    R.kl_fwd(a, b)
+    R.kl_bwd(a, b, gs[2])
+    R.kl_fwd(b, a)
+    R.kl_bwd(b, a, gs[3])
+    return int(np.asarray(a).shape[0])
+
+
+def cpu_baseline(wl, rows=256):
+    """The fp64 oracle on `rows` rows of the same workload, row chunks spread over host
+    threads (numpy releases the GIL inside its array kernels)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    from vocab_wide_softmax_amd import workloads as W
+
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    idx = np.linspace(0, N_ROWS - 1, rows).astype(np.int64)
+    a = wl.a[idx].double().numpy()
+    b = wl.b[idx].double().numpy()
+    t = wl.t[idx].numpy()
+    gs = [wl.g[op][idx].double().numpy() for op in W.OPS]
+    chunks = [c for c in np.array_split(np.arange(rows), rows // 4 if rows >= 4 else 1) if len(c)]
+    work = [(a[c], b[c], t[c], [x[c] for x in gs]) for c in chunks]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        done = sum(ex.map(_oracle_rows, work))
+    el = time.perf_counter() - t0
+    assert done == rows
+    bytes_sample = STEP_BYTES * rows / N_ROWS
+    return {
+        "value": round(bytes_sample / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "%d of 8192 rows (evenly spaced) of the 8192x75968 bf16 pair, all four ops fwd+bwd in float64 "
+                  "on %d host threads; %.1f s wall; GB/s = algorithmic bytes of those rows / wall time"
+                  % (rows, cores, el),
+    }
+
+
+# ------------------------------------------------------------------------- calibration
+
+def calibrate(device):
+    """Plain device copies of a known size (1.2447 GB each way), for scaling HBM counters."""
+    import torch
+
+    src = torch.empty(T_BYTES, dtype=torch.uint8, device=device)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes_each_way": T_BYTES, "launches": 5}))
+
+
+# -------------------------------------------------------------------- profile summaries
+
+def _rocpd(outdir):
+    import sqlite3
+
+    paths = sorted(glob.glob(os.path.join(outdir, "**", "*_results.db"), recursive=True))
+    if not paths:
+        raise FileNotFoundError("no rocprofv3 *_results.db under " + outdir)
+    return sqlite3.connect(paths[0])
+
+
+def summarize(outdir, mode):
+    """Condense rocprofv3 output (its SQLite database) in `outdir` into a text table.
+
+    mode "stats": calls and average / total duration per kernel;
+    mode "counters": mean value per dispatch of every collected counter, per kernel.
+    """
+    con = _rocpd(outdir)
+    if mode == "stats":
+        rows = con.execute("select name, count(*), avg(end - start), min(end - start), max(end - start), "
+                           "sum(end - start) from kernels group by name order by sum(end - start) desc").fetchall()
+        total = sum(r[5] for r in rows)
+        print("| kernel | calls | average us | min us | max us | total us | % |")
+        print("|---|---|---|---|---|---|---|")
+        for name, calls, avg, mn, mx, tot in rows:
+            print("| %s | %d | %.1f | %.1f | %.1f | %.1f | %.2f |" % (name, calls, avg / 1e3, mn / 1e3, mx / 1e3,
+                                                                      tot / 1e3, 100.0 * tot / total))
+        return
+    rows = con.execute("select * from counters_collection").fetchall()
+    cols = [d[0] for d in con.execute("select * from counters_collection limit 1").description]
+    ci = {c: i for i, c in enumerate(cols)}
+    name_col = "kernel_name" if "kernel_name" in ci else "name"
+    acc = {}
+    for r in rows:
+        key = (r[ci[name_col]], r[ci["counter_name"]])
+        acc.setdefault(key, {}).setdefault(r[ci["dispatch_id"]], 0.0)
+        acc[key][r[ci["dispatch_id"]]] += float(r[ci["value"]])
+    print("| kernel | counter | dispatches | mean per dispatch |")
+    print("|---|---|---|---|")
+    for (name, ctr), per in sorted(acc.items()):
+        vals = list(per.values())
+        print("| %s | %s | %d | %.1f |" % (name, ctr, len(vals), sum(vals) / len(vals)))
+
+
+# --------------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--calibrate", action="store_true")
+    ap.add_argument("--summarize", nargs=2, metavar=("DIR", "MODE"))
+    args = ap.parse_args()
+
+    if args.summarize:
+        summarize(*args.summarize)
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU: --gpus %d is not supported by this build (rows would shard across "
+              "GPUs with no communication; the one-GPU figure is each GPU's share). Use --gpus 1." % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from vocab_wide_softmax_amd import workloads as W
+
+    device = torch.device("cuda:0")
+    if args.calibrate:
+        calibrate(device)
+        return
+
+    log("generating the 8192x75968 bf16 pair on the host")
+    wl = W.workload("pair8192")
+    log("inputs ready")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_rows)
+        log("cpu baseline: %s GB/s on %d threads" % (cpu["value"], cpu["cores"]))
+    ms_per_step, med, mean = gpu_bench(wl, args.steps, args.warmup, device)
+    log("timed %d steps: %.3f ms/step" % (args.steps, ms_per_step))
+    value = STEP_BYTES / (ms_per_step * 1e-3) / 1e9
+    dom_ms = (mean["kl_ab_bwd"] + mean["kl_ba_bwd"]) / 2.0
+    achieved = DOMINANT_BYTES / (dom_ms * 1e-3) / 1e9
+    ops = {}
+    for op in ("logprobs", "entropy", "kl_ab", "kl_ba"):
+        f, bw = med[op + "_fwd"], med[op + "_bwd"]
+        ops[op] = {"fwd_ms": round(f, 4), "bwd_ms": round(bw, 4), "fwd_bwd_ms": round(f + bw, 4),
+                   "GB/s": round(OP_BYTES[op] / ((f + bw) * 1e-3) / 1e9, 1),
+                   "pct_peak": round(100 * OP_BYTES[op] / ((f + bw) * 1e-3) / 1e9 / PEAK_GBS, 1)}
+    traffic = traffic_from_profiles()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "8192x75968 bf16 logit pair (A~N(0,3^2), B=A+N(0,0.5^2), 5% rows +1e4, 1% rows "
+                               "with 64 B columns at -inf); step = logprobs, entropy, KL(A||B), KL(B||A), each fwd+bwd",
+                   "N": N_ROWS, "V": V, "step_bytes": STEP_BYTES},
+        "pct_peak": round(100 * value / PEAK_GBS, 1),
+        "ops": ops,
+        "roofline": {"bound": "hbm", "kernel": "bwd_kernel<KL,bf16> (" + DOMINANT + ")", "achieved": round(achieved, 1),
+                     "peak": PEAK_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": DOMINANT_BYTES,
+                     "avg_launch_ms": round(dom_ms, 4)},
+    }
+    out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

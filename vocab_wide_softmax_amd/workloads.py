@@ -3,20 +3,26 @@
 This module only draws random numbers and lays them out; it holds none of the
 method's arithmetic, so both the HIP path and the fp64 oracle can be fed from
 it. Everything is drawn on the CPU with ``torch.Generator().manual_seed(seed)``
-in float32, in one fixed stream order per workload:
+in float32. The large normal fields (A and B's noise, or B; h and W) are drawn
+in blocks of 256 leading rows, block i from its own generator seeded by
+(seed, field, i), so several threads can fill them and the values do not
+depend on the thread count. Everything else comes from one generator seeded
+with ``seed``, in this fixed order:
 
-    1. A          2. B (or B's noise)       3. offset-row choice
-    4. mask rows and columns                5. targets
-    6. one upstream gradient g per op, in the order of ``OPS``
+    1. offset-row choice       2. mask rows and columns
+    3. targets                 4. one upstream gradient g per op, in the order of ``OPS``
 
-and only then rounded (round-to-nearest-even) to the storage dtype. The
+Offsets and masks are applied in float32, and only then are values rounded
+(round-to-nearest-even) to the storage dtype. (The 64 x 1024 tiny pair is
+small enough to come from the one generator: A, then B, then the rest.) The
 shapes follow the pages' workloads: a 75968-column shard of a 151936-token
 vocabulary (PR #8838, B70 table caption and JSD table), 8192 tokens, large
 common offsets (+1e4 here; the pages test +1000) and -inf masks in B.
 """
 
 from dataclasses import dataclass, field
-from typing import Dict, Optional, Tuple
+from concurrent.futures import ThreadPoolExecutor
+from typing import Dict, Tuple
 
 import torch
 
@@ -70,6 +76,31 @@ def _gen(seed: int) -> torch.Generator:
     return torch.Generator().manual_seed(int(seed))
 
 
+ROW_BLOCK = 256
+
+
+def _block_gen(seed: int, stream: int, i: int) -> torch.Generator:
+    return _gen(((int(seed) * 1000003 + stream) * 1000003 + i) & 0x7FFFFFFFFFFF)
+
+
+def _for_blocks(n: int, fill) -> None:
+    """Run fill(i, r0, r1) over row blocks of ROW_BLOCK rows, on up to 16 threads."""
+    nblk = (n + ROW_BLOCK - 1) // ROW_BLOCK
+    spans = [(i, i * ROW_BLOCK, min(n, (i + 1) * ROW_BLOCK)) for i in range(nblk)]
+    if nblk <= 1:
+        for sp in spans:
+            fill(*sp)
+        return
+    with ThreadPoolExecutor(max_workers=min(16, nblk)) as ex:
+        list(ex.map(lambda sp: fill(*sp), spans))
+
+
+def _normal_block(rows: int, cols: int, seed: int, stream: int, i: int, std: float) -> torch.Tensor:
+    x = torch.empty(rows, cols, dtype=torch.float32)
+    x.normal_(0.0, 1.0, generator=_block_gen(seed, stream, i))
+    return x.mul_(std) if std != 1.0 else x
+
+
 def _pick_rows(gen: torch.Generator, n: int, k: int) -> torch.Tensor:
     """k distinct rows, row 0 always included (so one row is both offset and masked)."""
     k = max(1, min(n, k))
@@ -101,19 +132,32 @@ def logit_pair(n: int, v: int = VOCAB_SHARD, seed: int = 1, dtype=torch.bfloat16
     by +1e4 in both; a fraction of rows (row 0 included) with ``mask_cols`` distinct
     B columns at -inf; targets U[0, V); g ~ N(0, 1) per op; cast to ``dtype``."""
     gen = _gen(seed)
-    a = 3.0 * torch.randn(n, v, generator=gen)
-    b = a + 0.5 * torch.randn(n, v, generator=gen)
     offset_rows = _pick_rows(gen, n, int(round(offset_frac * n)))
-    a[offset_rows] += OFFSET
-    b[offset_rows] += OFFSET
     mask_rows = _pick_rows(gen, n, int(round(mask_frac * n)))
-    for r in mask_rows.tolist():
-        cols = torch.randperm(v, generator=gen)[: min(mask_cols, v)]
-        b[r, cols] = float("-inf")
+    masks = {r: torch.randperm(v, generator=gen)[: min(mask_cols, v)] for r in mask_rows.tolist()}
     t = torch.randint(0, v, (n,), generator=gen)
     g = {op: torch.randn(n, generator=gen) for op in OPS}
+    is_off = torch.zeros(n, dtype=torch.bool)
+    is_off[offset_rows] = True
+    a_out = torch.empty(n, v, dtype=dtype)
+    b_out = torch.empty(n, v, dtype=dtype)
+
+    def fill(i, r0, r1):
+        a = _normal_block(r1 - r0, v, seed, 1, i, 3.0)
+        b = _normal_block(r1 - r0, v, seed, 2, i, 0.5).add_(a)
+        off = is_off[r0:r1]
+        if bool(off.any()):
+            a[off] += OFFSET
+            b[off] += OFFSET
+        for r, cols in masks.items():
+            if r0 <= r < r1:
+                b[r - r0, cols] = float("-inf")
+        a_out[r0:r1] = a.to(dtype)
+        b_out[r0:r1] = b.to(dtype)
+
+    _for_blocks(n, fill)
     name = "%s logit pair %dx%d" % (str(dtype).replace("torch.", ""), n, v)
-    return Workload(name, a.to(dtype), b.to(dtype), t, False, g, offset_rows, mask_rows)
+    return Workload(name, a_out, b_out, t, False, g, offset_rows, mask_rows)
 
 
 def shifted_pair(batch: int = 4, seq: int = 2049, v: int = VOCAB_SHARD, seed: int = 3,
@@ -122,13 +166,20 @@ def shifted_pair(batch: int = 4, seq: int = 2049, v: int = VOCAB_SHARD, seed: in
     base[:, :-1, :] (batch*(seq-1) rows, two row strides, no copy). Token ids
     [batch, seq] U[0, V); targets are the next-token slice ids[:, 1:]."""
     gen = _gen(seed)
-    a = 3.0 * torch.randn(batch, seq, v, generator=gen)
-    b = 3.0 * torch.randn(batch, seq, v, generator=gen)
     ids = torch.randint(0, v, (batch, seq), generator=gen)
     n = batch * (seq - 1)
     g = {op: torch.randn(n, generator=gen) for op in OPS}
+    a_out = torch.empty(batch, seq, v, dtype=dtype)
+    b_out = torch.empty(batch, seq, v, dtype=dtype)
+    a_flat, b_flat = a_out.view(batch * seq, v), b_out.view(batch * seq, v)
+
+    def fill(i, r0, r1):
+        a_flat[r0:r1] = _normal_block(r1 - r0, v, seed, 1, i, 3.0).to(dtype)
+        b_flat[r0:r1] = _normal_block(r1 - r0, v, seed, 2, i, 3.0).to(dtype)
+
+    _for_blocks(batch * seq, fill)
     name = "%s causal-shift pair [%d,%d,%d][:, :-1]" % (str(dtype).replace("torch.", ""), batch, seq, v)
-    return Workload(name, a.to(dtype), b.to(dtype), ids, True, g)
+    return Workload(name, a_out, b_out, ids, True, g)
 
 
 @dataclass
@@ -145,10 +196,19 @@ def linear_logp(n: int = 8192, hidden: int = 4096, v: int = 151936, seed: int = 
     """h ~ N(0, 1) [n, hidden]; W ~ N(0, w_std^2) [v, hidden]; targets U[0, v);
     g ~ N(0, 1) [n]; h and W cast to ``dtype``."""
     gen = _gen(seed)
-    h = torch.randn(n, hidden, generator=gen).to(dtype)
-    W = (w_std * torch.randn(v, hidden, generator=gen)).to(dtype)
     t = torch.randint(0, v, (n,), generator=gen)
     g = torch.randn(n, generator=gen)
+    h = torch.empty(n, hidden, dtype=dtype)
+    W = torch.empty(v, hidden, dtype=dtype)
+
+    def fill_h(i, r0, r1):
+        h[r0:r1] = _normal_block(r1 - r0, hidden, seed, 1, i, 1.0).to(dtype)
+
+    def fill_w(i, r0, r1):
+        W[r0:r1] = _normal_block(r1 - r0, hidden, seed, 2, i, w_std).to(dtype)
+
+    _for_blocks(n, fill_h)
+    _for_blocks(v, fill_w)
     return LinearWorkload("linear-logp h[%d,%d] W[%d,%d] %s" % (n, hidden, v, hidden, str(dtype).replace("torch.", "")),
                           h, W, t, g)
 
