@@ -20,96 +20,133 @@
 
 namespace vws {
 
+// Per-row constants of the backward.
+struct RowBwd {
+  float m, ls, mb, lsb;  // (m, log S) of A, and of B for KL
+  float res;             // H or KL
+  float gv;
+  bool nan_a, nan_b, zero;
+  int32_t tg;  // group holding the logprobs target, -1 if none
+  int tj;
+};
+
+template <int OP, int DT, bool FULL>
+__device__ __forceinline__ void bwd_groups(const RowBwd& r, const char* ra, const char* rb, char* oa, char* ob,
+                                           int32_t g, int32_t stride, int n, int32_t G, int32_t V, int32_t g_full) {
+  const float qnan = __builtin_nanf("");
+  for (int k = 0; k < n; ++k, g += stride) {
+    if (!FULL && g >= G) break;
+    if constexpr (OP == kKL) {
+      float xa[8], xb[8], ya[8], yb[8];
+      if (FULL) {
+        load_group_vec<DT>(ra, g, xa);
+        load_group_vec<DT>(rb, g, xb);
+      } else {
+        load_group<DT, true>(ra, g, V, g_full, xa);
+        load_group<DT, true>(rb, g, V, g_full, xb);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float ua = (xa[j] - r.m) - r.ls;
+        const float ub = (xb[j] - r.mb) - r.lsb;
+        const float pa = expf_fast(ua);
+        const float pb = expf_fast(ub);
+        ya[j] = r.nan_a ? qnan : mul0(pa, (ua - ub) - r.res) * r.gv;
+        yb[j] = r.nan_b ? qnan : (pb - pa) * r.gv;
+      }
+      if (FULL) {
+        if (oa) store_group_vec<DT>(oa, g, ya);
+        if (ob) store_group_vec<DT>(ob, g, yb);
+      } else {
+        if (oa) store_group<DT, true>(oa, g, V, g_full, ya);
+        if (ob) store_group<DT, true>(ob, g, V, g_full, yb);
+      }
+    } else {
+      float x[8], y[8];
+      if (FULL) load_group_vec<DT>(ra, g, x);
+      else load_group<DT, true>(ra, g, V, g_full, x);
+      if constexpr (OP == kEntropy) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float u = (x[j] - r.m) - r.ls;  // log p_j
+          const float pj = expf_fast(u);
+          y[j] = r.nan_a ? qnan : mul0(pj, u + r.res) * (-r.gv);
+        }
+      } else {
+        float pr[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pr[j] = expf_fast((x[j] - r.m) - r.ls);
+          y[j] = r.zero ? 0.0f : (r.nan_a ? qnan : -r.gv * pr[j]);
+        }
+        if (g == r.tg) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (j == r.tj) y[j] = r.gv * (1.0f - pr[j]);
+        }
+      }
+      if (FULL) store_group_vec<DT>(oa, g, y);
+      else store_group<DT, true>(oa, g, V, g_full, y);
+    }
+  }
+}
+
 template <int OP, int DT, bool VEC, int BLOCK, int UB>
 __global__ __launch_bounds__(BLOCK) void bwd_kernel(BwdArgs p) {
   constexpr int ES = ElemSize<DT>::value;
   const int32_t tpr = p.tiles_per_row;
   const int64_t total = p.N * tpr;
-  for (int64_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
-  const int64_t row = vb / tpr;
-  const int32_t tile = (int32_t)(vb - row * tpr);
   const int32_t V = (int32_t)p.V;
   const int32_t G = (V + 7) / 8;
-  const int32_t g_full = V / 8;
-  const int32_t gt0 = tile * (BLOCK * UB) + threadIdx.x;
-  const float gv = p.g[row * p.g_stride];
-  const float qnan = __builtin_nanf("");
-  const char* ra = row_ptr<DT>(p.a, row);
-
-  if constexpr (OP == kKL) {
-    const char* rb = row_ptr<DT>(p.b, row);
+  const int32_t g_full = VEC ? V / 8 : 0;  // groups below this use 16-byte loads and stores
+  for (int64_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
+    const int64_t row = vb / tpr;
+    const int32_t tile = (int32_t)(vb - row * tpr);
+    const int32_t g0 = tile * (BLOCK * UB);
+    RowBwd r;
+    r.gv = p.g[row * p.g_stride];
+    r.zero = false;
+    r.tg = -1;
+    r.tj = 0;
+    const char* ra = row_ptr<DT>(p.a, row);
+    const char* rb = nullptr;
     char* oa = p.da ? p.da + row * (int64_t)V * ES : nullptr;
-    char* ob = p.db ? p.db + row * (int64_t)V * ES : nullptr;
-    const float ma = p.stats[4 * row + 0], lsa = p.stats[4 * row + 1];
-    const float mb = p.stats[4 * row + 2], lsb = p.stats[4 * row + 3];
-    const float kl = p.res[row];
-    const bool da_nan = !(kl < kInf);  // +inf (support mismatch) or NaN
-    const bool db_nan = kl != kl;
-#pragma unroll
-    for (int k = 0; k < UB; ++k) {
-      const int32_t g = gt0 + k * BLOCK;
-      if (g >= G) break;
-      float xa[8], xb[8], ya[8], yb[8];
-      load_group<DT, VEC>(ra, g, V, g_full, xa);
-      load_group<DT, VEC>(rb, g, V, g_full, xb);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float ua = (xa[j] - ma) - lsa;
-        const float ub = (xb[j] - mb) - lsb;
-        const float pa = expf_fast(ua);
-        const float pb = expf_fast(ub);
-        ya[j] = da_nan ? qnan : mul0(pa, (ua - ub) - kl) * gv;
-        yb[j] = db_nan ? qnan : (pb - pa) * gv;
-      }
-      if (oa) store_group<DT, VEC>(oa, g, V, g_full, ya);
-      if (ob) store_group<DT, VEC>(ob, g, V, g_full, yb);
-    }
-  } else {
-    char* oa = p.da + row * (int64_t)V * ES;
-    const float m = p.stats[2 * row + 0], ls = p.stats[2 * row + 1];
-    if constexpr (OP == kEntropy) {
-      const float H = p.res[row];
-      const bool nan_row = H != H;
-#pragma unroll
-      for (int k = 0; k < UB; ++k) {
-        const int32_t g = gt0 + k * BLOCK;
-        if (g >= G) break;
-        float x[8], y[8];
-        load_group<DT, VEC>(ra, g, V, g_full, x);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float u = (x[j] - m) - ls;  // log p_j
-          const float pj = expf_fast(u);
-          y[j] = nan_row ? qnan : mul0(pj, u + H) * (-gv);
-        }
-        store_group<DT, VEC>(oa, g, V, g_full, y);
-      }
+    char* ob = nullptr;
+    if constexpr (OP == kKL) {
+      rb = row_ptr<DT>(p.b, row);
+      ob = p.db ? p.db + row * (int64_t)V * ES : nullptr;
+      r.m = p.stats[4 * row + 0];
+      r.ls = p.stats[4 * row + 1];
+      r.mb = p.stats[4 * row + 2];
+      r.lsb = p.stats[4 * row + 3];
+      r.res = p.res[row];
+      r.nan_a = !(r.res < kInf);  // +inf (support mismatch) or NaN
+      r.nan_b = r.res != r.res;
     } else {
-      const int64_t t = load_id(p.ids, row, p.a.n_inner);
-      const bool ignored = t == p.ignore_index;
-      const bool bad = !ignored && (t < 0 || t >= V);
-      const int32_t tg = (ignored || bad) ? -1 : (int32_t)(t >> 3);
-      const int tj = (int)(t & 7);
-#pragma unroll
-      for (int k = 0; k < UB; ++k) {
-        const int32_t g = gt0 + k * BLOCK;
-        if (g >= G) break;
-        float x[8], y[8], pr[8];
-        load_group<DT, VEC>(ra, g, V, g_full, x);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pr[j] = expf_fast((x[j] - m) - ls);
-          y[j] = ignored ? 0.0f : (bad ? qnan : -gv * pr[j]);
+      r.m = p.stats[2 * row + 0];
+      r.ls = p.stats[2 * row + 1];
+      r.mb = r.lsb = 0.0f;
+      r.nan_b = false;
+      if constexpr (OP == kEntropy) {
+        r.res = p.res[row];
+        r.nan_a = r.res != r.res;
+      } else {
+        r.res = 0.0f;
+        const int64_t t = load_id(p.ids, row, p.a.n_inner);
+        r.zero = t == p.ignore_index;
+        r.nan_a = !r.zero && (t < 0 || t >= V);
+        if (!r.zero && !r.nan_a) {
+          r.tg = (int32_t)(t >> 3);
+          r.tj = (int)(t & 7);
         }
-        if (g == tg) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (j == tj) y[j] = gv * (1.0f - pr[j]);
-        }
-        store_group<DT, VEC>(oa, g, V, g_full, y);
       }
     }
-  }
+    const int32_t g = g0 + threadIdx.x;
+    if (VEC && g0 + BLOCK * UB <= g_full) {
+      bwd_groups<OP, DT, true>(r, ra, rb, oa, ob, g, BLOCK, UB, G, V, g_full);
+    } else {
+      bwd_groups<OP, DT, false>(r, ra, rb, oa, ob, g, BLOCK, UB, G, V, g_full);
+    }
   }
 }
 

@@ -36,6 +36,34 @@ constexpr float kInf = __builtin_inff();
 enum Dtype : int { kF32 = 0, kBF16 = 1 };
 enum Op : int { kLogprobs = 0, kEntropy = 1, kKL = 2 };
 
+// Cache policy of the streaming accesses: the logits are read once and the
+// gradients written once, so both default to non-temporal. (Compile-time
+// switches, so launch-shape and policy sweeps can rebuild the same kernels.)
+#ifndef VWS_NT_LOAD
+#define VWS_NT_LOAD 1
+#endif
+#ifndef VWS_NT_STORE
+#define VWS_NT_STORE 1
+#endif
+
+template <typename T>
+__device__ __forceinline__ T stream_load(const T* p) {
+#if VWS_NT_LOAD
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+template <typename T>
+__device__ __forceinline__ void stream_store(T v, T* p) {
+#if VWS_NT_STORE
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -63,7 +91,7 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t hi16) { return __ui
 template <int DT>
 __device__ __forceinline__ void load_group_vec(const char* __restrict__ row, int32_t g, float (&x)[8]) {
   if constexpr (DT == kBF16) {
-    u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + g);
+    u32x4 w = stream_load(reinterpret_cast<const u32x4*>(row) + g);
     x[0] = __uint_as_float(w.x << 16);
     x[1] = __uint_as_float(w.x & 0xffff0000u);
     x[2] = __uint_as_float(w.y << 16);
@@ -74,8 +102,8 @@ __device__ __forceinline__ void load_group_vec(const char* __restrict__ row, int
     x[7] = __uint_as_float(w.w & 0xffff0000u);
   } else {
     const f32x4* p = reinterpret_cast<const f32x4*>(row) + 2 * g;
-    f32x4 a = __builtin_nontemporal_load(p);
-    f32x4 b = __builtin_nontemporal_load(p + 1);
+    f32x4 a = stream_load(p);
+    f32x4 b = stream_load(p + 1);
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
   }
@@ -120,11 +148,11 @@ __device__ __forceinline__ void store_group_vec(char* __restrict__ row, int32_t 
     w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){y[2], y[3]}, bf16x2));
     w.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){y[4], y[5]}, bf16x2));
     w.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){y[6], y[7]}, bf16x2));
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(row) + g);
+    stream_store(w, reinterpret_cast<u32x4*>(row) + g);
   } else {
     f32x4* p = reinterpret_cast<f32x4*>(row) + 2 * g;
-    __builtin_nontemporal_store((f32x4){y[0], y[1], y[2], y[3]}, p);
-    __builtin_nontemporal_store((f32x4){y[4], y[5], y[6], y[7]}, p + 1);
+    stream_store((f32x4){y[0], y[1], y[2], y[3]}, p);
+    stream_store((f32x4){y[4], y[5], y[6], y[7]}, p + 1);
   }
 }
 

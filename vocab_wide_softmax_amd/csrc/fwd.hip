@@ -168,7 +168,20 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs p) {
   if constexpr (OP == kKL) {
     const char* rb = row_ptr<DT>(p.b, row);
     StateKL st = statekl_init();
-    for (int32_t gb = g0 + tid; gb < g1; gb += BLOCK * U) {
+    int32_t gb = g0 + tid;
+    // batches in which every group of every lane is a full vector group: no predicates
+    const int32_t nfull = VEC ? (min(g1, g_full) - g0) / (BLOCK * U) : 0;
+    for (int32_t it = 0; it < nfull; ++it, gb += BLOCK * U) {
+      float xa[U][8], xb[U][8];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        load_group_vec<DT>(ra, gb + k * BLOCK, xa[k]);
+        load_group_vec<DT>(rb, gb + k * BLOCK, xb[k]);
+      }
+      update_kl<U>(st, xa, xb);
+    }
+    // the rest of the part (same batch boundaries), groups predicated
+    for (; gb < g1; gb += BLOCK * U) {
       float xa[U][8], xb[U][8];
 #pragma unroll
       for (int k = 0; k < U; ++k) {
@@ -201,7 +214,15 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs p) {
   } else {
     constexpr bool WW = OP == kEntropy;
     State1 st = state1_init();
-    for (int32_t gb = g0 + tid; gb < g1; gb += BLOCK * U) {
+    int32_t gb = g0 + tid;
+    const int32_t nfull = VEC ? (min(g1, g_full) - g0) / (BLOCK * U) : 0;
+    for (int32_t it = 0; it < nfull; ++it, gb += BLOCK * U) {
+      float x[U][8];
+#pragma unroll
+      for (int k = 0; k < U; ++k) load_group_vec<DT>(ra, gb + k * BLOCK, x[k]);
+      update1<WW, U>(st, x);
+    }
+    for (; gb < g1; gb += BLOCK * U) {
       float x[U][8];
 #pragma unroll
       for (int k = 0; k < U; ++k) {
