@@ -18,6 +18,7 @@ bounded sample of the same workload on the host cores.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --calibrate          # plain copies of known size, for counter scaling
     python bench.py --summarize DIR stats|counters   # condense rocprofv3 output for profiles/
+    python bench.py --counters FETCH WRITE CALFETCH CALWRITE   # calibrated HBM bytes per kernel
 """
 
 import argparse
@@ -260,6 +261,48 @@ def summarize(outdir, mode):
         print("| %s | %s | %d | %.1f |" % (name, ctr, len(vals), sum(vals) / len(vals)))
 
 
+def _counter_means(path):
+    """{kernel: mean KiB per dispatch} from a rocprofv3 counter_collection.csv (one counter)."""
+    acc = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+            acc[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: (len(v), sum(v.values()) / len(v)) for k, v in acc.items()}
+
+
+def counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the same counters read for a
+    plain device copy of T bytes each way, print a table, and write the dominant kernel's
+    HBM bytes per launch to profiles/kl_bwd_pair8192_counters.json."""
+    def one(d):
+        return _counter_means(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0])
+
+    fetch, write, cf, cw = one(fetch_dir), one(write_dir), one(cal_fetch_dir), one(cal_write_dir)
+    copy_f = [v for k, v in cf.items() if "copyBuffer" in k][0][1]
+    copy_w = [v for k, v in cw.items() if "copyBuffer" in k][0][1]
+    kf, kw = T_BYTES / (copy_f * 1024.0), T_BYTES / (copy_w * 1024.0)
+    print("Calibration: a device copy of %d bytes each way reads FETCH_SIZE %.1f KiB and WRITE_SIZE %.1f KiB "
+          "per dispatch; scale factors %.5f (fetch) and %.5f (write)." % (T_BYTES, copy_f, copy_w, kf, kw))
+    print()
+    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | in units of T |")
+    print("|---|---|---|---|---|---|")
+    dom = None
+    for k in sorted(fetch):
+        n, f = fetch[k]
+        w = write.get(k, (0, 0.0))[1]
+        bytes_ = f * 1024.0 * kf + w * 1024.0 * kw
+        print("| %s | %d | %.1f | %.1f | %.0f | %.4f |" % (k, n, f, w, bytes_, bytes_ / T_BYTES))
+        if k.startswith("void vws::bwd_kernel<2, 1, true"):
+            dom = bytes_
+    out = {"kernel": "bwd_kernel<KL,bf16,vec> on the 8192x75968 bf16 pair", "hbm_bytes_per_launch": round(dom),
+           "fetch_factor": kf, "write_factor": kw, "kernel_source_hash": kernel_source_hash(),
+           "sources": KERNEL_SOURCES}
+    with open(os.path.join(PROFILE_DIR, "kl_bwd_pair8192_counters.json"), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+
+
 # --------------------------------------------------------------------------------- main
 
 def main():
@@ -271,10 +314,14 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--summarize", nargs=2, metavar=("DIR", "MODE"))
+    ap.add_argument("--counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"))
     args = ap.parse_args()
 
     if args.summarize:
         summarize(*args.summarize)
+        return
+    if args.counters:
+        counters(*args.counters)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: --gpus %d is not supported by this build (rows would shard across "
