@@ -176,6 +176,38 @@ VWS_API int vws_kl_fwd(const vws_rows* a, const vws_rows* b, float* kl, float* s
 VWS_API int vws_kl_bwd(const vws_rows* a, const vws_rows* b, const float* stats, const float* kl, const float* g,
                        int64_t g_stride, void* da, void* db, void* stream);
 
+/*
+ * Fused linear-logp (RL-Kernel PR #208, PR body "Implementation"): the per-row
+ * log-probability of the target under logits z = h W^T, computed on MFMA in
+ * vocabulary tiles whose (m, S) feed the online log-sum-exp, so the [N, V]
+ * logits are never written. The forward returns logp = z_t - lse and the
+ * per-row (m, log S); the backward recomputes the logits tile by tile, forms
+ * dz = g (onehot(t) - p) (the chunked backward of the pages' review nitpick),
+ * rounds it to bf16 into the workspace, and contracts it into dh = dz W and
+ * dW = dz^T h (fp32 accumulation, bf16 round-to-nearest-even outputs).
+ *
+ *   h       bf16 [N, H], row stride ldh (elements, >= H, multiple of 8)
+ *   W       bf16 [V, H], row stride ldw (>= H, multiple of 8)
+ *   t       int64 [N] contiguous target ids; ignore_index gives logp 0 and zero
+ *           gradient rows; any other id outside [0, V) gives NaN
+ *   logp    out fp32 [N];  stats out fp32 [N, 2] = (m, log S) of each row's logits
+ *   dh      out bf16 [N, H] contiguous, may be NULL
+ *   dW      out bf16 [V, H] contiguous, may be NULL
+ *   ws      workspace of vws_linear_workspace_bytes(pass, N, H, V) bytes
+ *           (pass 0: forward, 1: backward), 16-byte aligned
+ * h, W, dh, dW must be 16-byte aligned. dtype must be VWS_BF16.
+ */
+VWS_API size_t vws_linear_workspace_bytes(int pass, int64_t N, int64_t H, int64_t V);
+
+VWS_API int vws_linear_logp_fwd(const void* h, int64_t ldh, const void* W, int64_t ldw, int dtype, int64_t N,
+                                int64_t H, int64_t V, const int64_t* t, int64_t ignore_index, float* logp,
+                                float* stats, void* ws, size_t ws_bytes, void* stream);
+
+VWS_API int vws_linear_logp_bwd(const void* h, int64_t ldh, const void* W, int64_t ldw, int dtype, int64_t N,
+                                int64_t H, int64_t V, const int64_t* t, int64_t ignore_index, const float* stats,
+                                const float* g, int64_t g_stride, void* dh, void* dW, void* ws, size_t ws_bytes,
+                                void* stream);
+
 /* Static description of a status code. */
 VWS_API const char* vws_strerror(int status);
 

@@ -70,13 +70,18 @@ def f64_to_bf16_bits(x):
     return bits
 
 
-def check(x, y, c, kind):
+def check(x, y, c, kind, factor=None):
     """Compare device values x with oracle values y under the rule above.
 
-    kind is "f32" or "bf16". Returns a dict with the element count, the number
-    of elements missing the strict bound, the number failing both bounds, the
-    NaN / inf placement mismatches, and the worst ratio of error to allowance.
+    kind is "f32" or "bf16". ``factor`` replaces 64 eps32 in the conditioned
+    bound where the computation rounds an operand more coarsely (the fused
+    linear-logp backward feeds dz to its contractions in bf16: each term then
+    carries up to 2^-9 relative error, so its rule uses factor 2^-8).
+    Returns a dict with the element count, the number of elements missing the
+    strict bound, the number failing both bounds, the NaN / inf placement
+    mismatches, and the worst ratio of error to allowance.
     """
+    cfac = COND if factor is None else float(factor)
     x = np.asarray(x, dtype=np.float64).ravel()
     y = np.asarray(y, dtype=np.float64).ravel()
     c = np.asarray(c, dtype=np.float64).ravel()
@@ -91,7 +96,7 @@ def check(x, y, c, kind):
     if kind == "f32":
         err = np.abs(xf - yf)
         strict = REL32 * np.abs(yf) + 2.0 ** -126
-        cond = REL32 * np.abs(yf) + COND * cf
+        cond = REL32 * np.abs(yf) + cfac * cf
         strict_ok = err <= strict
         ok = strict_ok | (err <= cond)
         allow = np.maximum(strict, cond)
@@ -99,7 +104,7 @@ def check(x, y, c, kind):
         r = bf16_rne(yf)
         u = ulp_bf16(r)
         strict_ok = np.abs(xf - r) <= u
-        cond = u + COND * cf
+        cond = u + cfac * cf
         ok = strict_ok | (np.abs(xf - yf) <= cond)
         err = np.minimum(np.abs(xf - r), np.abs(xf - yf))
         allow = cond

@@ -18,7 +18,8 @@ import numpy as np
 
 from . import reductions
 
-__all__ = ["logits", "linear_logp_fwd", "linear_logp_bwd_dh", "linear_logp_bwd_dw", "cond_logits"]
+__all__ = ["logits", "linear_logp_fwd", "linear_logp_bwd_dh", "linear_logp_bwd_dw", "cond_logits",
+           "cond_linear_fwd", "cond_linear_dh", "cond_linear_dw", "linear_logp_bwd_dw_cond"]
 
 
 def _f64(x):
@@ -84,3 +85,67 @@ def linear_logp_bwd_dw(h, W, t, g, ignore_index=-100, vocab_rows=None, row_chunk
         dz = reductions.logprobs_bwd(z, t[r0:r1], g[r0:r1], ignore_index)
         dW += dz[:, cols].T @ h[r0:r1]
     return dW
+
+
+# Conditioning scales (sums of magnitudes of the terms each result combines),
+# used by the parity rule. The logits themselves are sums over the hidden dim,
+# so their magnitude sums |h| |W|^T enter every result built from them.
+
+def cond_linear_fwd(h, W, t, ignore_index=-100, rows=None):
+    """|z_t - m| + |log S| + cz_t + sum_v p_v cz_v, with cz = |h| |W|^T."""
+    t = np.asarray(t, dtype=np.int64)
+    if rows is not None:
+        t = t[np.asarray(rows)]
+    z = logits(h, W, rows)
+    cz = cond_logits(h, W, rows)
+    n, V = z.shape
+    lp, m, logS = reductions.log_softmax_rows(z)
+    p = np.exp(lp)
+    c = np.abs(logS) + np.sum(p * cz, axis=1)
+    ok = (t >= 0) & (t < V) & (t != ignore_index)
+    r = np.nonzero(ok)[0]
+    c[r] += np.abs(z[r, t[r]] - m[r]) + cz[r, t[r]]
+    return c
+
+
+def cond_linear_dh(h, W, t, g, ignore_index=-100, rows=None):
+    """sum_v |dz_nv| |W_vk|."""
+    t = np.asarray(t, dtype=np.int64)
+    g = _f64(g).reshape(-1)
+    if rows is not None:
+        t = t[np.asarray(rows)]
+        g = g[np.asarray(rows)]
+    dz = reductions.logprobs_bwd(logits(h, W, rows), t, g, ignore_index)
+    return np.abs(dz) @ np.abs(_f64(W))
+
+
+def cond_linear_dw(h, W, t, g, ignore_index=-100, vocab_rows=None, row_chunk=512):
+    """sum_n |dz_nv| |h_nk| for the selected vocabulary rows."""
+    h = _f64(h)
+    W = _f64(W)
+    t = np.asarray(t, dtype=np.int64)
+    g = _f64(g).reshape(-1)
+    cols = np.arange(W.shape[0]) if vocab_rows is None else np.asarray(vocab_rows)
+    c = np.zeros((len(cols), h.shape[1]))
+    for r0 in range(0, h.shape[0], row_chunk):
+        r1 = min(h.shape[0], r0 + row_chunk)
+        dz = reductions.logprobs_bwd(h[r0:r1] @ W.T, t[r0:r1], g[r0:r1], ignore_index)
+        c += np.abs(dz[:, cols]).T @ np.abs(h[r0:r1])
+    return c
+
+
+def linear_logp_bwd_dw_cond(h, W, t, g, ignore_index=-100, vocab_rows=None, row_chunk=512):
+    """(dW, its conditioning scale) for the selected vocabulary rows in one pass over the token rows."""
+    h = _f64(h)
+    W = _f64(W)
+    t = np.asarray(t, dtype=np.int64)
+    g = _f64(g).reshape(-1)
+    cols = np.arange(W.shape[0]) if vocab_rows is None else np.asarray(vocab_rows)
+    dW = np.zeros((len(cols), h.shape[1]))
+    c = np.zeros_like(dW)
+    for r0 in range(0, h.shape[0], row_chunk):
+        r1 = min(h.shape[0], r0 + row_chunk)
+        dz = reductions.logprobs_bwd(h[r0:r1] @ W.T, t[r0:r1], g[r0:r1], ignore_index)[:, cols]
+        dW += dz.T @ h[r0:r1]
+        c += np.abs(dz).T @ np.abs(h[r0:r1])
+    return dW, c

@@ -106,3 +106,32 @@ def test_kl_and_logprobs_validation(L):
     assert L.vws_logprobs_bwd(ctypes.byref(a), None, -100, 0x3000, 0x5000, 1, 0x6000, None) == EINVAL
     assert L.vws_entropy_bwd(ctypes.byref(a), 0x3000, 0, 0x5000, 1, 0x6000, None) == EINVAL  # H missing
     assert L.vws_entropy_bwd(ctypes.byref(a), 0x3000, 0x2000, 0x5000, 1, 0x6001, None) == ELAYOUT
+
+
+def test_linear_validation(L):
+    c_i64 = ctypes.c_int64
+
+    def fwd(h=0x1000, ldh=64, W=0x2000, ldw=64, dtype=B.VWS_BF16, N=4, H=64, V=100, t=0x3000, logp=0x4000,
+            stats=0x5000, ws=0x6000, nb=1 << 20):
+        return L.vws_linear_logp_fwd(h, ldh, W, ldw, dtype, N, H, V, t, -100, logp, stats, ws, nb, None)
+
+    assert fwd(dtype=B.VWS_F32) == EDTYPE
+    assert fwd(H=0) == EINVAL
+    assert fwd(ldh=60) == ELAYOUT  # row stride must be a multiple of 8 and >= H
+    assert fwd(ldw=72, H=80) == ELAYOUT
+    assert fwd(h=0x1008) == ELAYOUT  # 16-byte alignment
+    assert fwd(t=0) == EINVAL
+    assert fwd(logp=0) == EINVAL
+    assert fwd(nb=16) == EWORKSPACE
+    assert fwd(N=0, h=0, W=0, t=0) == 0
+    assert B.linear_workspace_bytes(1, 8, 64, 100) == 8 * 104 * 2
+    assert B.linear_workspace_bytes(0, 8, 64, 100) > 8 * 4
+    with pytest.raises(ValueError):
+        B.linear_workspace_bytes(2, 8, 64, 100)
+    bwd = L.vws_linear_logp_bwd
+    assert bwd(0x1000, 64, 0x2000, 64, B.VWS_BF16, 4, 64, 100, 0x3000, -100, 0x5000, 0x7000, -1, 0x8000, None, 0x6000,
+               1 << 20, None) == EINVAL
+    assert bwd(0x1000, 64, 0x2000, 64, B.VWS_BF16, 4, 64, 100, 0x3000, -100, 0x5000, 0x7000, 1, None, None, 0x6000,
+               1 << 20, None) == 0  # no gradient requested
+    assert bwd(0x1000, 64, 0x2000, 64, B.VWS_BF16, 4, 64, 100, 0x3000, -100, 0x5000, 0x7000, 1, 0x8000, None, 0x6000,
+               16, None) == EWORKSPACE

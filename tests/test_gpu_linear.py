@@ -1,0 +1,123 @@
+"""GPU parity of the fused linear-logp (MFMA) against the fp64 oracle, through the C ABI.
+
+* small ragged shape (300 tokens, hidden 200, vocabulary 3000: partial tiles in
+  every dimension, ignored targets): every element of logp, lse, dh and dW;
+* an out-of-range target: NaN logp and dh row, NaN dW (the row's dz is NaN);
+* the full hidden and vocabulary widths (4096 x 151936) at 512 tokens: every
+  logp and dh element, sampled dW rows;
+* the full 8192 x 4096 x 151936 launch (slow): sampled rows of logp and dh,
+  sampled vocabulary rows of dW.
+
+dh and dW are compared with the conditioned factor 2^-8: the backward feeds dz to
+its two contractions rounded to bf16 (2^-9 relative per term), as the pages'
+chunked PyTorch backward feeds bf16 operands to its matmuls.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import compare, linear_logp as OL
+from vocab_wide_softmax_amd import binding as B
+from vocab_wide_softmax_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+GEMM_FACTOR = 2.0 ** -8
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def _assert_ok(rep, label):
+    assert rep["fail"] == 0 and rep["nan_mismatch"] == 0 and rep["inf_mismatch"] == 0, (label, rep)
+    print(label, {k: (rep[k] if not isinstance(rep[k], float) else round(rep[k], 4)) for k in rep}, flush=True)
+
+
+def _small(n=300, hidden=200, v=3000, seed=11):
+    gen = torch.Generator().manual_seed(seed)
+    h = torch.randn(n, hidden, generator=gen).to(torch.bfloat16)
+    Wm = (0.05 * torch.randn(v, hidden, generator=gen)).to(torch.bfloat16)
+    t = torch.randint(0, v, (n,), generator=gen)
+    t[::37] = -100
+    g = torch.randn(n, generator=gen)
+    return h, Wm, t, g
+
+
+def _run(h, Wm, t, g, device, need_h=True, need_w=True):
+    dh_, Wd, td, gd = h.to(device), Wm.to(device), t.to(device), g.to(device)
+    logp, stats = B.linear_logp_fwd(dh_, Wd, td, -100)
+    dh, dW = B.linear_logp_bwd(dh_, Wd, td, stats, gd, -100, need_h=need_h, need_w=need_w)
+    torch.cuda.synchronize()
+    return logp, stats, dh, dW
+
+
+def test_linear_small_all_elements(device):
+    h, Wm, t, g = _small()
+    logp, stats, dh, dW = _run(h, Wm, t, g, device)
+    hh, hw, ht, hg = f64(h), f64(Wm), t.numpy(), g.double().numpy()
+    lp, m, ls = OL.linear_logp_fwd(hh, hw, ht)
+    c = OL.cond_linear_fwd(hh, hw, ht)
+    _assert_ok(compare.check(f64(logp), lp, c, "f32"), "small logp")
+    lse_dev = f64(stats[:, 0]) + f64(stats[:, 1])
+    _assert_ok(compare.check(lse_dev, m + ls, c, "f32"), "small lse")
+    _assert_ok(compare.check(f64(dh), OL.linear_logp_bwd_dh(hh, hw, ht, hg), OL.cond_linear_dh(hh, hw, ht, hg),
+                             "bf16", GEMM_FACTOR), "small dh")
+    _assert_ok(compare.check(f64(dW), OL.linear_logp_bwd_dw(hh, hw, ht, hg), OL.cond_linear_dw(hh, hw, ht, hg),
+                             "bf16", GEMM_FACTOR), "small dW")
+
+
+def test_linear_out_of_range_target(device):
+    h, Wm, t, g = _small(n=40, hidden=64, v=500, seed=3)
+    t[5] = 500
+    logp, stats, dh, dW = _run(h, Wm, t, g, device)
+    lp = logp.cpu()
+    assert torch.isnan(lp[5]) and not torch.isnan(lp[torch.arange(40) != 5]).any()
+    assert torch.isnan(dh[5].float()).all() and not torch.isnan(dh[6].float()).any()
+    assert torch.isnan(dW.float()).all()
+    assert (lp[t == -100] == 0).all()
+
+
+def test_linear_gradient_subsets(device):
+    h, Wm, t, g = _small(n=64, hidden=96, v=700, seed=5)
+    _, _, dh_both, dW_both = _run(h, Wm, t, g, device)
+    _, _, dh_only, none_w = _run(h, Wm, t, g, device, need_w=False)
+    _, _, none_h, dW_only = _run(h, Wm, t, g, device, need_h=False)
+    assert none_w is None and none_h is None
+    assert torch.equal(dh_both, dh_only) and torch.equal(dW_both, dW_only)
+
+
+def test_linear_full_width_512_tokens(device):
+    wl = W.linear_logp(n=512, seed=4)
+    logp, stats, dh, dW = _run(wl.h, wl.W, wl.t, wl.g, device)
+    hh, hw, ht, hg = f64(wl.h), f64(wl.W), wl.t.numpy(), wl.g.double().numpy()
+    lp, m, ls = OL.linear_logp_fwd(hh, hw, ht)
+    c = OL.cond_linear_fwd(hh, hw, ht)
+    _assert_ok(compare.check(f64(logp), lp, c, "f32"), "512 logp")
+    _assert_ok(compare.check(f64(dh), OL.linear_logp_bwd_dh(hh, hw, ht, hg), OL.cond_linear_dh(hh, hw, ht, hg),
+                             "bf16", GEMM_FACTOR), "512 dh")
+    rng = np.random.default_rng(0)
+    cols = np.unique(np.concatenate([ht[:8], rng.integers(0, hw.shape[0], 40), [0, hw.shape[0] - 1]]))
+    dw_ref, dw_c = OL.linear_logp_bwd_dw(hh, hw, ht, hg, vocab_rows=cols), OL.cond_linear_dw(hh, hw, ht, hg,
+                                                                                              vocab_rows=cols)
+    _assert_ok(compare.check(f64(dW[torch.from_numpy(cols).to(dW.device)]), dw_ref, dw_c, "bf16", GEMM_FACTOR),
+               "512 dW rows")
+
+
+@pytest.mark.slow
+def test_linear_full_size_sampled(device):
+    wl = W.linear_logp()
+    logp, stats, dh, dW = _run(wl.h, wl.W, wl.t, wl.g, device)
+    hh, hw, ht, hg = f64(wl.h), f64(wl.W), wl.t.numpy(), wl.g.double().numpy()
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, hh.shape[0] - 1], rng.integers(0, hh.shape[0], 14)]))
+    lp, m, ls = OL.linear_logp_fwd(hh, hw, ht, rows=rows)
+    c = OL.cond_linear_fwd(hh, hw, ht, rows=rows)
+    idx = torch.from_numpy(rows).to(device)
+    _assert_ok(compare.check(f64(logp[idx]), lp, c, "f32"), "full logp rows")
+    _assert_ok(compare.check(f64(dh[idx]), OL.linear_logp_bwd_dh(hh, hw, ht, hg, rows=rows),
+                             OL.cond_linear_dh(hh, hw, ht, hg, rows=rows), "bf16", GEMM_FACTOR), "full dh rows")
+    cols = np.unique(np.concatenate([ht[:4], rng.integers(0, hw.shape[0], 12), [hw.shape[0] - 1]]))
+    dw_ref, dw_c = OL.linear_logp_bwd_dw_cond(hh, hw, ht, hg, vocab_rows=cols)
+    _assert_ok(compare.check(f64(dW[torch.from_numpy(cols).to(device)]), dw_ref, dw_c, "bf16", GEMM_FACTOR),
+               "full dW rows")

@@ -291,6 +291,10 @@ def test_linear_logp_gradients_match_differences():
     # sampled rows / vocab rows agree with the full evaluation
     np.testing.assert_allclose(linear_logp.linear_logp_bwd_dh(h, W, t, g, rows=[2, 0]), dh[[2, 0]])
     np.testing.assert_allclose(linear_logp.linear_logp_bwd_dw(h, W, t, g, vocab_rows=[6, 1]), dW[[6, 1]])
+    dw2, c2 = linear_logp.linear_logp_bwd_dw_cond(h, W, t, g, vocab_rows=[6, 1], row_chunk=2)
+    np.testing.assert_allclose(dw2, dW[[6, 1]])
+    np.testing.assert_allclose(c2, linear_logp.cond_linear_dw(h, W, t, g, vocab_rows=[6, 1]))
+    assert np.all(c2 >= np.abs(dw2) - 1e-12)
 
 
 def test_linear_logp_forward_matches_brute_force():

@@ -69,6 +69,10 @@ def lib():
             "vws_entropy_bwd": (I32, [R, FP, FP, FP, I64, VP, VP]),
             "vws_kl_fwd": (I32, [R, R, FP, FP, VP, SZ, I32, VP]),
             "vws_kl_bwd": (I32, [R, R, FP, FP, FP, I64, VP, VP, VP]),
+            "vws_linear_workspace_bytes": (SZ, [I32, I64, I64, I64]),
+            "vws_linear_logp_fwd": (I32, [VP, I64, VP, I64, I32, I64, I64, I64, VP, I64, FP, FP, VP, SZ, VP]),
+            "vws_linear_logp_bwd": (I32, [VP, I64, VP, I64, I32, I64, I64, I64, VP, I64, FP, FP, I64, VP, VP, VP,
+                                          SZ, VP]),
             "vws_strerror": (ctypes.c_char_p, [I32]),
             "vws_version": (I32, []),
         }
@@ -239,3 +243,57 @@ def kl_bwd(a, b, stats, kl, g, need_a=True, need_b=True):
     _check("vws_kl_bwd", L.vws_kl_bwd(ctypes.byref(ra), ctypes.byref(rb), _ptr(stats), _ptr(kl), _ptr(g), gs,
                                       _ptr(da), _ptr(db), _stream(a.device)))
     return da, db
+
+
+# ------------------------------------------------------------- fused linear-logp
+
+def _lin_check(h, W, t):
+    if h.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+        raise TypeError("h and W must be bfloat16")
+    if h.dim() != 2 or W.dim() != 2 or h.shape[1] != W.shape[1]:
+        raise ValueError("h must be [N, H] and W [V, H]")
+    if h.stride(1) != 1 or W.stride(1) != 1:
+        raise ValueError("h and W need a contiguous last dimension")
+    if t.dtype != torch.int64 or t.dim() != 1 or t.shape[0] != h.shape[0] or t.stride(0) != 1:
+        raise ValueError("targets must be a contiguous int64 [N] tensor")
+
+
+def linear_workspace_bytes(pass_, n, hidden, v):
+    r = lib().vws_linear_workspace_bytes(pass_, n, hidden, v)
+    if r == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid workspace query")
+    return r
+
+
+def linear_logp_fwd(h, W, t, ignore_index=-100):
+    """(logp fp32 [N], stats fp32 [N, 2]) of the target under logits h W^T -- vws_linear_logp_fwd."""
+    L = lib()
+    _lin_check(h, W, t)
+    n, hidden = h.shape
+    v = W.shape[0]
+    logp = torch.empty(n, dtype=torch.float32, device=h.device)
+    stats = torch.empty((n, 2), dtype=torch.float32, device=h.device)
+    nb = linear_workspace_bytes(0, n, hidden, v)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=h.device)
+    _check("vws_linear_logp_fwd", L.vws_linear_logp_fwd(h.data_ptr(), h.stride(0), W.data_ptr(), W.stride(0),
+                                                        VWS_BF16, n, hidden, v, t.data_ptr(), ignore_index,
+                                                        _ptr(logp), _ptr(stats), _ptr(ws), nb, _stream(h.device)))
+    return logp, stats
+
+
+def linear_logp_bwd(h, W, t, stats, g, ignore_index=-100, need_h=True, need_w=True):
+    """(dh bf16 [N, H] or None, dW bf16 [V, H] or None) -- vws_linear_logp_bwd."""
+    L = lib()
+    _lin_check(h, W, t)
+    n, hidden = h.shape
+    v = W.shape[0]
+    g, gs = _g_arg(g, h)
+    dh = torch.empty((n, hidden), dtype=torch.bfloat16, device=h.device) if need_h else None
+    dW = torch.empty((v, hidden), dtype=torch.bfloat16, device=h.device) if need_w else None
+    nb = linear_workspace_bytes(1, n, hidden, v)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=h.device)
+    _check("vws_linear_logp_bwd", L.vws_linear_logp_bwd(h.data_ptr(), h.stride(0), W.data_ptr(), W.stride(0),
+                                                        VWS_BF16, n, hidden, v, t.data_ptr(), ignore_index,
+                                                        _ptr(stats), _ptr(g), gs, _ptr(dh), _ptr(dW), _ptr(ws), nb,
+                                                        _stream(h.device)))
+    return dh, dW

@@ -188,9 +188,107 @@ int bwd_common(int op, const vws_rows* a, const vws_rows* b, const vws_ids* t, i
   return e == hipSuccess ? VWS_OK : VWS_EHIP;
 }
 
+int64_t round_up8(int64_t x) { return (x + 7) / 8 * 8; }
+
+// Workspace layout of the fused linear-logp.
+//   forward:  part [N, chunks, 2] fp32, then zt [N] fp32
+//   backward: dz [N, round_up8(V)] bf16
+size_t lin_ws_bytes(int pass, int64_t N, int64_t V) {
+  if (pass == 0) {
+    const size_t part = (size_t)N * (size_t)vws::lin_chunks(N, V) * 2 * sizeof(float);
+    return (part + 255) / 256 * 256 + (size_t)N * sizeof(float);
+  }
+  return (size_t)N * (size_t)round_up8(V) * 2;
+}
+
+int lin_check(const void* h, int64_t ldh, const void* W, int64_t ldw, int dtype, int64_t N, int64_t H, int64_t V,
+              const int64_t* t) {
+  if (dtype != VWS_BF16) return VWS_EDTYPE;
+  if (N < 0 || H < 1 || V < 1) return VWS_EINVAL;
+  if (V > (int64_t)INT32_MAX || H > (int64_t)INT32_MAX || N > ((int64_t)1 << 31)) return VWS_EINVAL;
+  if (ldh < H || ldw < H || ldh % 8 || ldw % 8) return VWS_ELAYOUT;
+  if (N == 0) return VWS_OK;
+  if (!h || !W || !t) return VWS_EINVAL;
+  if (!aligned(h, 16) || !aligned(W, 16) || !aligned(t, 8)) return VWS_ELAYOUT;
+  int64_t x;
+  if (!mul_ok(N, ldh, &x) || !mul_ok(V, ldw, &x) || !mul_ok(N, round_up8(V), &x)) return VWS_EINVAL;
+  return VWS_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+VWS_API size_t vws_linear_workspace_bytes(int pass, int64_t N, int64_t H, int64_t V) {
+  if ((pass != 0 && pass != 1) || N < 0 || H < 1 || V < 1) return (size_t)-1;
+  if (N == 0) return 0;
+  return lin_ws_bytes(pass, N, V);
+}
+
+VWS_API int vws_linear_logp_fwd(const void* h, int64_t ldh, const void* W, int64_t ldw, int dtype, int64_t N,
+                                int64_t H, int64_t V, const int64_t* t, int64_t ignore_index, float* logp,
+                                float* stats, void* ws, size_t ws_bytes, void* stream) {
+  int rc = lin_check(h, ldh, W, ldw, dtype, N, H, V, t);
+  if (rc) return rc;
+  if (N == 0) return VWS_OK;
+  if (!logp || !stats) return VWS_EINVAL;
+  if (!aligned(logp, 4) || !aligned(stats, 4)) return VWS_ELAYOUT;
+  const size_t need = lin_ws_bytes(0, N, V);
+  if (!ws || ws_bytes < need) return VWS_EWORKSPACE;
+  if (!aligned(ws, 16)) return VWS_ELAYOUT;
+  vws::LinArgs p{};
+  p.h = static_cast<const uint16_t*>(h);
+  p.W = static_cast<const uint16_t*>(W);
+  p.ldh = ldh;
+  p.ldw = ldw;
+  p.N = N;
+  p.H = H;
+  p.V = V;
+  p.t = t;
+  p.ignore_index = ignore_index;
+  p.logp = logp;
+  p.stats = stats;
+  const size_t part = (size_t)N * (size_t)vws::lin_chunks(N, V) * 2 * sizeof(float);
+  p.part = static_cast<float*>(ws);
+  p.zt = reinterpret_cast<float*>(static_cast<char*>(ws) + (part + 255) / 256 * 256);
+  hipError_t e = vws::launch_lin_fwd(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VWS_OK : VWS_EHIP;
+}
+
+VWS_API int vws_linear_logp_bwd(const void* h, int64_t ldh, const void* W, int64_t ldw, int dtype, int64_t N,
+                                int64_t H, int64_t V, const int64_t* t, int64_t ignore_index, const float* stats,
+                                const float* g, int64_t g_stride, void* dh, void* dW, void* ws, size_t ws_bytes,
+                                void* stream) {
+  int rc = lin_check(h, ldh, W, ldw, dtype, N, H, V, t);
+  if (rc) return rc;
+  if (g_stride < 0) return VWS_EINVAL;
+  if (N == 0 || (!dh && !dW)) return VWS_OK;
+  if (!stats || !g) return VWS_EINVAL;
+  if (!aligned(stats, 4) || !aligned(g, 4) || !aligned(dh, 16) || !aligned(dW, 16)) return VWS_ELAYOUT;
+  const size_t need = lin_ws_bytes(1, N, V);
+  if (!ws || ws_bytes < need) return VWS_EWORKSPACE;
+  if (!aligned(ws, 16)) return VWS_ELAYOUT;
+  vws::LinArgs p{};
+  p.h = static_cast<const uint16_t*>(h);
+  p.W = static_cast<const uint16_t*>(W);
+  p.ldh = ldh;
+  p.ldw = ldw;
+  p.N = N;
+  p.H = H;
+  p.V = V;
+  p.t = t;
+  p.ignore_index = ignore_index;
+  p.stats = const_cast<float*>(stats);
+  p.g = g;
+  p.g_stride = g_stride;
+  p.dz = static_cast<uint16_t*>(ws);
+  p.ldz = round_up8(V);
+  p.ldw_out = H;
+  hipError_t e = vws::launch_lin_bwd(p, static_cast<uint16_t*>(dh), static_cast<uint16_t*>(dW),
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VWS_OK : VWS_EHIP;
+}
+
 
 VWS_API size_t vws_workspace_bytes(int op, int64_t N, int64_t V, int split_hint) {
   if (op < VWS_OP_LOGPROBS || op > VWS_OP_KL || N < 0 || V < 1 || split_hint < 0) return (size_t)-1;

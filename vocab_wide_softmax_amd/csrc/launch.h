@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "device.h"
+#include "gemm.h"
 
 namespace vws {
 
@@ -30,6 +31,37 @@ struct BwdArgs {
   char* da;  // dz for logprobs / entropy
   char* db;
 };
+
+// Fused linear-logp: h [N, H] and W [V, H] bf16 (row strides ldh, ldw), targets t [N].
+struct LinArgs {
+  const uint16_t* h;
+  const uint16_t* W;
+  int64_t ldh, ldw, N, H, V;
+  const int64_t* t;
+  int64_t ignore_index;
+  // forward
+  float* logp;   // [N]
+  float* stats;  // [N, 2] (m, log S); read by the backward
+  float* part;   // workspace [N, chunks, 2]
+  float* zt;     // workspace [N]
+  int32_t chunks, tiles_per_chunk;
+  // backward
+  const float* g;
+  int64_t g_stride;
+  uint16_t* dz;  // workspace [N, ldz] bf16
+  int64_t ldz;
+  int64_t ldw_out;  // row stride of dW
+};
+
+struct GemmArgs {
+  gemm::Operand A, B;
+  uint16_t* C;
+  int64_t ldc, M, Nc, K;
+};
+
+int lin_chunks(int64_t N, int64_t V);
+hipError_t launch_lin_fwd(LinArgs p, hipStream_t stream);
+hipError_t launch_lin_bwd(LinArgs p, uint16_t* dh, uint16_t* dW, hipStream_t stream);
 
 // Workgroups per launch: kernels loop over virtual blocks beyond this, which
 // keeps grid size x workgroup size below the 2^32 work-item limit.

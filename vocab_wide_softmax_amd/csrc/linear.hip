@@ -1,0 +1,314 @@
+// linear.hip -- fused linear-logp on MFMA (RL-Kernel PR #208, PR body "Implementation";
+// review nitpick on the chunked backward).
+//
+// Forward: logits z = h W^T (h [N, H] bf16 tokens, W [V, H] bf16 vocabulary rows)
+// are computed tile by tile and never stored. lin_fwd_kernel computes a 256-row
+// vocabulary tile x 256 tokens with MFMA (A = W rows, B = h rows, fp32
+// accumulation); in the accumulator layout each lane holds one token column and
+// 16 vocabulary rows per block, so the online (m, S) update of that token is
+// mostly in-lane. A workgroup walks one vocabulary chunk for one token tile and
+// writes the chunk's (m, S) per token; lin_combine_kernel merges the chunks in
+// order (the pages' MAX / rescale / SUM of running max and sum across vocab
+// shards, inside one GPU) and forms logp = z_t - lse, with z_t from
+// lin_target_kernel (one wave per token, fp32 dot product).
+//
+// Backward: dz = g (onehot(t) - p) with p = exp((z - m) - log S) recomputed
+// from a second MFMA pass (lin_dz_kernel, A = h rows, B = W rows, so a lane's
+// 32 consecutive vocabulary columns make coalesced bf16 stores of dz [N, V]);
+// then dh = dz W and dW = dz^T h by gemm_store_kernel, reading the transposed
+// operands through gfx950's transposing LDS reads (gemm.h).
+#include "device.h"
+#include "gemm.h"
+#include "launch.h"
+
+namespace vws {
+
+using gemm::Acc;
+using gemm::Cfg;
+using gemm::KROW;
+using gemm::Operand;
+using gemm::ROWK;
+
+typedef Cfg<256, 256, 32, 2, 4, ROWK, ROWK> CfgNT;  // A, B both reduction-contiguous
+typedef Cfg<256, 256, 32, 2, 4, ROWK, KROW> CfgNN;  // dh = dz W
+typedef Cfg<256, 256, 32, 2, 4, KROW, KROW> CfgTN;  // dW = dz^T h
+
+constexpr int kLinThreads = 512;
+static_assert(CfgNT::NT == kLinThreads && CfgNN::NT == kLinThreads && CfgTN::NT == kLinThreads, "threads");
+
+// ---- forward -----------------------------------------------------------------------
+
+__global__ __launch_bounds__(kLinThreads) void lin_fwd_kernel(LinArgs p) {
+  typedef CfgNT C;
+  extern __shared__ __align__(16) char lds[];
+  const int nchunks = p.chunks;
+  const int64_t tt = blockIdx.x / nchunks;   // token tile
+  const int c = blockIdx.x - tt * nchunks;  // vocabulary chunk (consecutive ids -> distinct XCDs)
+  const int64_t n0 = tt * C::BN;
+  const int64_t vt0 = (int64_t)c * p.tiles_per_chunk;
+  const int64_t vt1 = min(vt0 + p.tiles_per_chunk, (p.V + C::BM - 1) / C::BM);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+
+  const Operand A{p.W, p.ldw, p.V, p.H};
+  const Operand B{p.h, p.ldh, p.N, p.H};
+  State1 st[C::FN];
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) st[j] = state1_init();
+
+  Acc<C> acc;
+  for (int64_t vt = vt0; vt < vt1; ++vt) {
+    const int64_t m0 = vt * C::BM;
+    gemm::mainloop<C>(A, B, m0, n0, p.H, lds, acc);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      float bm = -kInf;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t row = m0 + wm * C::TM + gemm::acc_row(i, v, lane);
+          const float z = row < p.V ? acc.c[i][j][v] : -kInf;
+          acc.c[i][j][v] = z;
+          bm = fmaxf(bm, z);
+        }
+      if (bm > st[j].m) {
+        const float s = expf_fast(st[j].m - bm);
+        st[j].S *= s;
+        st[j].m = bm;
+      }
+      const float ref = ref_of(st[j].m);
+      float sum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sum += expf_fast(acc.c[i][j][v] - ref);
+      st[j].S += sum;
+    }
+  }
+  // lanes l and l ^ 32 hold the same token column
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) {
+    State1 o{__shfl_xor(st[j].m, 32, 64), __shfl_xor(st[j].S, 32, 64), 0.0f};
+    st[j] = merge1<false>(st[j], o);
+  }
+  // waves with the same token columns (different wm) merge through LDS, in wm order
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(lds);  // [WM][BN][2]
+  if (lane < 32) {
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int col = wn * C::TN + j * 32 + lane;
+      red[(wm * C::BN + col) * 2 + 0] = st[j].m;
+      red[(wm * C::BN + col) * 2 + 1] = st[j].S;
+    }
+  }
+  __syncthreads();
+  for (int col = threadIdx.x; col < C::BN; col += C::NT) {
+    State1 s = state1_init();
+#pragma unroll
+    for (int w = 0; w < C::WM; ++w) s = merge1<false>(s, State1{red[(w * C::BN + col) * 2], red[(w * C::BN + col) * 2 + 1], 0.0f});
+    const int64_t n = n0 + col;
+    if (n < p.N) {
+      p.part[(n * nchunks + c) * 2 + 0] = s.m;
+      p.part[(n * nchunks + c) * 2 + 1] = s.S;
+    }
+  }
+}
+
+// One wave per token: z_t = sum_k h[n, k] W[t, k] in fp32 (bf16 products are exact).
+__global__ __launch_bounds__(256) void lin_target_kernel(LinArgs p) {
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (n >= p.N) return;
+  const int64_t t = p.t[n];
+  if (t < 0 || t >= p.V) {
+    if (lane == 0) p.zt[n] = 0.0f;
+    return;
+  }
+  const uint16_t* hr = p.h + n * p.ldh;
+  const uint16_t* wr = p.W + t * p.ldw;
+  float s = 0.0f;
+  for (int64_t k = lane; k < p.H; k += 64)
+    s = fmaf(bf16_bits_to_float(hr[k]), bf16_bits_to_float(wr[k]), s);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (lane == 0) p.zt[n] = s;
+}
+
+// One thread per token: merge the chunk states in chunk order, then logp = z_t - (m + log S).
+__global__ __launch_bounds__(256) void lin_combine_kernel(LinArgs p) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= p.N) return;
+  State1 s = state1_init();
+  for (int c = 0; c < p.chunks; ++c)
+    s = merge1<false>(s, State1{p.part[(n * p.chunks + c) * 2], p.part[(n * p.chunks + c) * 2 + 1], 0.0f});
+  const double logS = log((double)s.S);
+  p.stats[2 * n + 0] = s.m;
+  p.stats[2 * n + 1] = (float)logS;
+  const int64_t t = p.t[n];
+  float out;
+  if (t == p.ignore_index) out = 0.0f;
+  else if (t < 0 || t >= p.V) out = __builtin_nanf("");
+  else out = (float)(((double)p.zt[n] - (double)s.m) - logS);
+  p.logp[n] = out;
+}
+
+// ---- backward ------------------------------------------------------------------------
+
+// Tile (token tile, vocabulary tile) -> block id, so that the token tiles of one
+// vocabulary tile are consecutive on one XCD (block b runs on XCD b % 8): W tiles are
+// fetched into that XCD's L2 once and shared.
+__device__ __forceinline__ void xcd_tile(int64_t b, int64_t ntt, int64_t nvt, int64_t& tt, int64_t& vt) {
+  const int64_t x = b % 8, q = b / 8;
+  tt = q % ntt;
+  vt = (q / ntt) * 8 + x;
+  if (vt >= nvt) {  // the last, partial group of 8 vocabulary tiles: plain order
+    tt = b % ntt;
+    vt = b / ntt;
+  }
+}
+
+__global__ __launch_bounds__(kLinThreads) void lin_dz_kernel(LinArgs p) {
+  typedef CfgNT C;
+  extern __shared__ __align__(16) char lds[];
+  const int64_t ntt = (p.N + C::BM - 1) / C::BM, nvt = (p.V + C::BN - 1) / C::BN;
+  int64_t tt, vt;
+  const int64_t full = (nvt / 8) * 8 * ntt;  // blocks covered by whole groups of 8 vocabulary tiles
+  if ((int64_t)blockIdx.x < full) {
+    xcd_tile(blockIdx.x, ntt, nvt, tt, vt);
+  } else {
+    const int64_t r = blockIdx.x - full;
+    tt = r % ntt;
+    vt = (nvt / 8) * 8 + r / ntt;
+  }
+  const int64_t m0 = tt * C::BM, n0 = vt * C::BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const Operand A{p.h, p.ldh, p.N, p.H};
+  const Operand B{p.W, p.ldw, p.V, p.H};
+  Acc<C> acc;
+  gemm::mainloop<C>(A, B, m0, n0, p.H, lds, acc);
+  // per-token constants of this tile into LDS: m, log S, g, target
+  float* cst = reinterpret_cast<float*>(lds);
+  int64_t* tgt = reinterpret_cast<int64_t*>(lds + C::BM * 3 * sizeof(float));
+  for (int r = threadIdx.x; r < C::BM; r += C::NT) {
+    const int64_t n = m0 + r < p.N ? m0 + r : p.N - 1;
+    cst[3 * r + 0] = p.stats[2 * n];
+    cst[3 * r + 1] = p.stats[2 * n + 1];
+    cst[3 * r + 2] = p.g[n * p.g_stride];
+    tgt[r] = p.t[n];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = wm * C::TM + gemm::acc_row(i, v, lane);
+      const int64_t n = m0 + r;
+      const float m = cst[3 * r], ls = cst[3 * r + 1], gv = cst[3 * r + 2];
+      const int64_t t = tgt[r];
+      const bool ignored = t == p.ignore_index, bad = !ignored && (t < 0 || t >= p.V);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        const int64_t col = n0 + wn * C::TN + gemm::acc_col(j, lane);
+        const float pz = expf_fast((acc.c[i][j][v] - m) - ls);
+        float d = (col == t) ? gv * (1.0f - pz) : -gv * pz;
+        d = ignored ? 0.0f : (bad ? __builtin_nanf("") : d);
+        if (n < p.N && col < p.V) {
+          const bf16x2 hb = __builtin_convertvector((f32x2){d, 0.0f}, bf16x2);
+          p.dz[n * p.ldz + col] = (uint16_t)(__builtin_bit_cast(uint32_t, hb) & 0xffffu);
+        }
+      }
+    }
+}
+
+// C = A B^T over K with bf16 (RNE) stores; used for dh (A = dz rows, B = W^T via KROW) and
+// dW (A = dz^T via KROW, B = h^T via KROW).
+template <class C>
+__global__ __launch_bounds__(kLinThreads) void gemm_store_kernel(GemmArgs g) {
+  extern __shared__ __align__(16) char lds[];
+  const int64_t ntm = (g.M + C::BM - 1) / C::BM, ntn = (g.Nc + C::BN - 1) / C::BN;
+  // consecutive blocks share the A tile (on different XCDs they still share it in the MALL)
+  const int64_t tm = blockIdx.x / ntn, tn = blockIdx.x - (blockIdx.x / ntn) * ntn;
+  (void)ntm;
+  const int64_t m0 = tm * C::BM, n0 = tn * C::BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  Acc<C> acc;
+  gemm::mainloop<C>(g.A, g.B, m0, n0, g.K, lds, acc);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t r = m0 + wm * C::TM + gemm::acc_row(i, v, lane);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        const int64_t col = n0 + wn * C::TN + gemm::acc_col(j, lane);
+        if (r < g.M && col < g.Nc) {
+          const bf16x2 hb = __builtin_convertvector((f32x2){acc.c[i][j][v], 0.0f}, bf16x2);
+          g.C[r * g.ldc + col] = (uint16_t)(__builtin_bit_cast(uint32_t, hb) & 0xffffu);
+        }
+      }
+    }
+}
+
+// ---- host-side launch ---------------------------------------------------------------------
+
+namespace {
+template <class C>
+size_t lds_bytes() {
+  return (size_t)2 * C::STAGE_BYTES;
+}
+}  // namespace
+
+int lin_chunks(int64_t N, int64_t V) {
+  // one workgroup per (256-token tile, vocabulary chunk); aim for ~2 workgroups per CU
+  const int64_t ntt = (N + CfgNT::BN - 1) / CfgNT::BN;
+  const int64_t nvt = (V + CfgNT::BM - 1) / CfgNT::BM;
+  int64_t c = (512 + ntt - 1) / ntt;
+  if (c > nvt) c = nvt;
+  if (c < 1) c = 1;
+  return (int)c;
+}
+
+hipError_t launch_lin_fwd(LinArgs p, hipStream_t stream) {
+  const int64_t ntt = (p.N + CfgNT::BN - 1) / CfgNT::BN;
+  const int64_t nvt = (p.V + CfgNT::BM - 1) / CfgNT::BM;
+  p.chunks = lin_chunks(p.N, p.V);
+  p.tiles_per_chunk = (int32_t)((nvt + p.chunks - 1) / p.chunks);
+  p.chunks = (int)((nvt + p.tiles_per_chunk - 1) / p.tiles_per_chunk);
+  hipLaunchKernelGGL(lin_target_kernel, dim3((uint32_t)((p.N + 3) / 4)), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(lin_fwd_kernel, dim3((uint32_t)(ntt * p.chunks)), dim3(kLinThreads), lds_bytes<CfgNT>(), stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(lin_combine_kernel, dim3((uint32_t)((p.N + 255) / 256)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_lin_bwd(LinArgs p, uint16_t* dh, uint16_t* dW, hipStream_t stream) {
+  const int64_t ntt = (p.N + CfgNT::BM - 1) / CfgNT::BM, nvt = (p.V + CfgNT::BN - 1) / CfgNT::BN;
+  hipLaunchKernelGGL(lin_dz_kernel, dim3((uint32_t)(ntt * nvt)), dim3(kLinThreads), lds_bytes<CfgNT>(), stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (dh) {
+    // dh[n, k] = sum_v dz[n, v] W[v, k]: A = dz (ROWK, reduction v), B(k, v) = W[v, k] (KROW)
+    GemmArgs g{Operand{p.dz, p.ldz, p.N, p.V}, Operand{p.W, p.ldw, p.H, p.V}, dh, p.H, p.N, p.H, p.V};
+    const int64_t blocks = ((p.N + 255) / 256) * ((p.H + 255) / 256);
+    hipLaunchKernelGGL((gemm_store_kernel<CfgNN>), dim3((uint32_t)blocks), dim3(kLinThreads), lds_bytes<CfgNN>(), stream, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (dW) {
+    // dW[v, k] = sum_n dz[n, v] h[n, k]: A(v, n) = dz[n, v] (KROW), B(k, n) = h[n, k] (KROW)
+    GemmArgs g{Operand{p.dz, p.ldz, p.V, p.N}, Operand{p.h, p.ldh, p.H, p.N}, dW, p.ldw_out, p.V, p.H, p.N};
+    const int64_t blocks = ((p.V + 255) / 256) * ((p.H + 255) / 256);
+    hipLaunchKernelGGL((gemm_store_kernel<CfgTN>), dim3((uint32_t)blocks), dim3(kLinThreads), lds_bytes<CfgTN>(), stream, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+size_t lin_fwd_lds_bytes() { return lds_bytes<CfgNT>(); }
+
+}  // namespace vws

@@ -58,6 +58,29 @@ class _KL(torch.autograd.Function):
         return da, db, None
 
 
+class _LinearLogp(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, h, W, t, ignore_index):
+        logp, stats = B.linear_logp_fwd(h, W, t, ignore_index)
+        ctx.save_for_backward(h, W, t, stats)
+        ctx.ignore_index = ignore_index
+        return logp
+
+    @staticmethod
+    def backward(ctx, g):
+        h, W, t, stats = ctx.saved_tensors
+        nh, nw = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        if not (nh or nw):
+            return None, None, None, None
+        dh, dW = B.linear_logp_bwd(h, W, t, stats, g, ctx.ignore_index, need_h=nh, need_w=nw)
+        return dh, dW, None, None
+
+
+def linear_logp(h, W, t, ignore_index=-100):
+    """Per-token log p_t under logits h W^T, without materialising the logits (bf16 h, W)."""
+    return _LinearLogp.apply(h, W, t, ignore_index)
+
+
 def logprobs(z, t, ignore_index=-100, split_hint=0):
     """Per-token log p_t; ``t == ignore_index`` gives 0 and no gradient."""
     return _Logprobs.apply(z, t, ignore_index, split_hint)
