@@ -148,6 +148,53 @@ def gpu_bench(wl, steps, warmup, device):
     return ms_per_step, med, mean
 
 
+# ------------------------------------------------------------------- fused linear-logp
+
+LIN_N, LIN_H, LIN_V = 8192, 4096, 151936
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def linear_bench(steps, warmup, device):
+    """Forward + backward of the fused linear-logp on h [8192, 4096], W [151936, 4096] bf16.
+    FLOPs counted: forward 2 N H V; backward 3 x 2 N H V (logits recomputed, dh, dW)."""
+    import torch
+
+    from vocab_wide_softmax_amd import binding as B
+    from vocab_wide_softmax_amd import workloads as W
+
+    wl = W.linear_logp(LIN_N, LIN_H, LIN_V)
+    h, Wm, t, g = wl.h.to(device), wl.W.to(device), wl.t.to(device), wl.g.to(device)
+    torch.cuda.synchronize()
+    log("linear-logp inputs resident; %d warmup steps" % warmup)
+    for _ in range(warmup):
+        lp, st = B.linear_logp_fwd(h, Wm, t)
+        B.linear_logp_bwd(h, Wm, t, st, g)
+    stream = torch.cuda.current_stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        lp, st = B.linear_logp_fwd(h, Wm, t)
+        evs[i][1].record(stream)
+        B.linear_logp_bwd(h, Wm, t, st, g)
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    fwd = sorted(e[0].elapsed_time(e[1]) for e in evs)[steps // 2]
+    bwd = sorted(e[1].elapsed_time(e[2]) for e in evs)[steps // 2]
+    flop = 2.0 * LIN_N * LIN_H * LIN_V
+    tf = lambda f, ms: f / (ms * 1e-3) / 1e12
+    return {
+        "workload": "h [8192, 4096] ~ N(0,1), W [151936, 4096] ~ N(0, 0.02^2), bf16; targets U[0, 151936)",
+        "ms_per_step": round(wall, 3), "fwd_ms": round(fwd, 3), "bwd_ms": round(bwd, 3),
+        "fwd_tflops": round(tf(flop, fwd), 1), "bwd_tflops": round(tf(3 * flop, bwd), 1),
+        "step_tflops": round(tf(4 * flop, fwd + bwd), 1),
+        "roofline": {"bound": "mfma", "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf(4 * flop, fwd + bwd) / MFMA_BF16_PEAK_TFLOPS, 4)},
+    }
+
+
 # --------------------------------------------------------------------------- CPU oracle
 
 def _oracle_rows(args):
@@ -311,6 +358,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-linear", action="store_true", help="skip the fused linear-logp workload")
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--summarize", nargs=2, metavar=("DIR", "MODE"))
@@ -381,6 +429,9 @@ def main():
                      "avg_launch_ms": round(dom_ms, 4)},
     }
     out["cpu_baseline"] = cpu
+    if not args.no_linear:
+        out["linear_logp"] = linear_bench(max(3, args.steps // 4), 2, device)
+        log("linear-logp: %.2f ms fwd, %.2f ms bwd" % (out["linear_logp"]["fwd_ms"], out["linear_logp"]["bwd_ms"]))
     print(json.dumps(out), flush=True)
 
 

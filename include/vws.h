@@ -195,7 +195,7 @@ VWS_API int vws_kl_bwd(const vws_rows* a, const vws_rows* b, const float* stats,
  *   dW      out bf16 [V, H] contiguous, may be NULL
  *   ws      workspace of vws_linear_workspace_bytes(pass, N, H, V) bytes
  *           (pass 0: forward, 1: backward), 16-byte aligned
- * h, W, dh, dW must be 16-byte aligned. dtype must be VWS_BF16.
+ * H must be a multiple of 8. h, W, dh, dW must be 16-byte aligned. dtype must be VWS_BF16.
  */
 VWS_API size_t vws_linear_workspace_bytes(int pass, int64_t N, int64_t H, int64_t V);
 

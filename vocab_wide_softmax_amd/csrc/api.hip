@@ -206,7 +206,7 @@ int lin_check(const void* h, int64_t ldh, const void* W, int64_t ldw, int dtype,
   if (dtype != VWS_BF16) return VWS_EDTYPE;
   if (N < 0 || H < 1 || V < 1) return VWS_EINVAL;
   if (V > (int64_t)INT32_MAX || H > (int64_t)INT32_MAX || N > ((int64_t)1 << 31)) return VWS_EINVAL;
-  if (ldh < H || ldw < H || ldh % 8 || ldw % 8) return VWS_ELAYOUT;
+  if (ldh < H || ldw < H || ldh % 8 || ldw % 8 || H % 8) return VWS_ELAYOUT;
   if (N == 0) return VWS_OK;
   if (!h || !W || !t) return VWS_EINVAL;
   if (!aligned(h, 16) || !aligned(W, 16) || !aligned(t, 8)) return VWS_ELAYOUT;

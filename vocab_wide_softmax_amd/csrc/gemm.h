@@ -5,10 +5,17 @@
 // from global memory in one of two layouts:
 //   ROWK : element (r, k) at base[r * ld + k]   (reduction dim contiguous)
 //   KROW : element (r, k) at base[k * ld + r]   (row dim contiguous)
-// and staged in LDS in that same orientation (padded rows). MFMA fragments are
-// read with ds_read_b128 from ROWK tiles and with two ds_read_b64_tr_b16 (the
-// gfx950 transposing LDS read) from KROW tiles, so no operand is ever
-// transposed in global memory.
+// and staged in LDS in that same orientation. MFMA fragments are read with
+// ds_read_b128 from ROWK tiles and with two ds_read_b64_tr_b16 (the gfx950
+// transposing LDS read) from KROW tiles, so no operand is ever transposed in
+// global memory.
+//
+// Staging: a ring of NSTAGE LDS stages filled by global_load_lds_dwordx4 (the
+// load writes LDS directly, 16 bytes per lane, a wave's 64 lanes contiguous),
+// NSTAGE - 1 stages in flight ahead of the one being multiplied; one workgroup
+// barrier per stage. Because a wave's DMA writes 1 KB contiguously, LDS rows
+// are not padded; 16-byte chunks are XOR-swizzled by row instead, which keeps
+// the fragment reads free of bank conflicts.
 //
 // MFMA 32x32x16 bf16 lane layout (checked on the device): lane l supplies
 // A[l % 32][8 (l / 32) + e] and B[8 (l / 32) + e][l % 32], e = 0..7, and holds
@@ -25,122 +32,138 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 enum Layout : int { ROWK = 0, KROW = 1 };
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Tile geometry. WM x WN waves; each wave owns a (BM/WM) x (BN/WN) sub-tile made
-// of FM x FN MFMA blocks of 32 x 32.
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int LA_, int LB_>
+// Source of the 16-byte chunks that lie past the reduction length: they must add nothing.
+extern __device__ const uint32_t kZeroChunk[4];
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int LA_, int LB_, int NSTAGE_>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, LA = LA_, LB = LB_;
-  static constexpr int NT = WM * WN * 64;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, LA = LA_, LB = LB_, NSTAGE = NSTAGE_;
+  static constexpr int NW = WM * WN, NT = NW * 64;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
-  // LDS row strides in bytes: ROWK tiles are [rows][BK] (+16 B keeps 8 lanes of a
-  // b128 read on distinct banks), KROW tiles are [BK][rows] (+32 B keeps the four
-  // rows of a transposing read on distinct banks).
-  static constexpr int SA = LA == ROWK ? BK * 2 + 16 : BM * 2 + 32;
-  static constexpr int SB = LB == ROWK ? BK * 2 + 16 : BN * 2 + 32;
-  static constexpr int A_BYTES = LA == ROWK ? BM * SA : BK * SA;
-  static constexpr int B_BYTES = LB == ROWK ? BN * SB : BK * SB;
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  // 16-byte chunks per stage, per operand, and per thread
-  static constexpr int A_CHUNKS = BM * BK / 8, B_CHUNKS = BN * BK / 8;
-  static constexpr int A_PER_T = A_CHUNKS / NT, B_PER_T = B_CHUNKS / NT;
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
+  static constexpr int A_INSTR = A_BYTES / 1024 / NW, B_INSTR = B_BYTES / 1024 / NW;  // DMA loads per wave
+  static constexpr int LOADS_PER_STAGE = A_INSTR + B_INSTR;
+  static_assert(BK == 32 || BK == 64, "ROWK swizzles exist for 4 and 8 chunks per row");
   static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "tile");
-  static_assert(BK % 16 == 0 && A_CHUNKS % NT == 0 && B_CHUNKS % NT == 0, "chunks");
+  static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole DMA instructions per wave");
 };
 
 // Global operand view.
 struct Operand {
   const uint16_t* base;
-  int64_t ld;    // elements between consecutive rows (ROWK) or consecutive k (KROW)
-  int64_t rows;  // valid rows (M or N); rows beyond are clamped on load, masked by the caller
-  int64_t K;     // valid reduction length; k beyond reads as 0
+  int64_t ld;    // elements between consecutive rows (ROWK) or consecutive k (KROW); multiple of 8
+  int64_t rows;  // valid rows (>= 8 for KROW); rows beyond are clamped on load and masked by the caller
+  int64_t K;     // valid reduction length, multiple of 8 for ROWK; chunks past it read zeros
 };
 
-// One 16-byte chunk of a stage: 8 consecutive elements along the contiguous dim.
-// Out-of-range rows are clamped (their results are discarded by the epilogue);
-// out-of-range reduction indices read as zero so they add nothing.
+// Swizzled chunk of a ROWK row (BK / 8 chunks of 16 B per row; the pattern keeps 8 and
+// 16 consecutive rows at one chunk on distinct banks) and of a KROW k-row (R / 8 chunks,
+// swizzled in pairs so a transposing read's 32 contiguous bytes stay together).
+template <int BK>
+__device__ __forceinline__ int swz_rowk(int r) {
+  if constexpr (BK == 32) return ((r >> 1) ^ (r >> 3)) & 3;
+  else return (r ^ (r >> 3)) & 7;
+}
+__device__ __forceinline__ int swz_krow(int kr) { return 2 * (kr & 3); }
+
+// Issue this wave's DMA loads of one operand tile for reduction offset k0 into lds_tile.
+template <int L, int R, int BK, int NW, int NINSTR>
+__device__ __forceinline__ void dma_tile(const Operand& op, int64_t r0, int64_t k0, char* lds_tile, int wave,
+                                         int lane) {
+#pragma unroll
+  for (int j = 0; j < NINSTR; ++j) {
+    const int instr = wave * NINSTR + j;
+    const int o = instr * 1024 + lane * 16;  // byte offset this lane fills
+    const void* src;
+    if constexpr (L == ROWK) {
+      const int r = o / (BK * 2), pc = (o % (BK * 2)) / 16;
+      const int c = pc ^ swz_rowk<BK>(r);
+      int64_t row = r0 + r;
+      row = row < op.rows ? row : op.rows - 1;
+      const int64_t k = k0 + c * 8;
+      src = k < op.K ? (const void*)(op.base + row * op.ld + k) : (const void*)kZeroChunk;
+    } else {
+      const int kr = o / (R * 2), pc = (o % (R * 2)) / 16;
+      const int c = pc ^ swz_krow(kr);
+      int64_t row = r0 + c * 8;
+      row = row + 8 <= op.rows ? row : op.rows - 8;
+      const int64_t k = k0 + kr;
+      src = k < op.K ? (const void*)(op.base + k * op.ld + row) : (const void*)kZeroChunk;
+    }
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds_tile + instr * 1024), 16, 0, 0);
+  }
+}
+
+// LDS byte address of a generic pointer into the workgroup's LDS.
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Fragment reads are issued with inline asm: the compiler neither sees them as LDS
+// reads (so it does not drain the in-flight DMA stages with vmcnt(0) in front of
+// them) nor waits for them; settle() waits (lgkmcnt(0)) and ties the registers.
+__device__ __forceinline__ void ds_b128(u32x4& r, uint32_t a) { asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(a)); }
+__device__ __forceinline__ void ds_tr16(uint32_t (&r)[2], uint32_t a) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a));
+  r[0] = v.x;
+  r[1] = v.y;
+}
+
+// One MFMA fragment: 8 reduction values of one row, for rows r0 + lane % 32, k-slice kk.
 template <int L, int R, int BK>
-__device__ __forceinline__ u32x4 load_chunk(const Operand& op, int64_t r0, int64_t k0, int c) {
-  u32x4 v;
+__device__ __forceinline__ void read_frag(u32x4& f, const char* lds, int r0, int kk, int lane) {
   if constexpr (L == ROWK) {
-    constexpr int CPR = BK / 8;  // chunks per row
-    const int r = c / CPR, kc = (c % CPR) * 8;
-    int64_t row = r0 + r;
-    row = row < op.rows ? row : op.rows - 1;
-    const int64_t k = k0 + kc;
-    const uint16_t* p = op.base + row * op.ld + k;
-    if (k + 8 <= op.K) {
-      v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    } else {
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (k + 2 * e < op.K) ? p[2 * e] : 0u;
-        const uint32_t hi = (k + 2 * e + 1 < op.K) ? p[2 * e + 1] : 0u;
-        w[e] = lo | (hi << 16);
-      }
-      v = (u32x4){w[0], w[1], w[2], w[3]};
-    }
-  } else {
-    constexpr int CPK = R / 8;  // chunks per k-row
-    const int kk = c / CPK, rc = (c % CPK) * 8;
-    const int64_t k = k0 + kk;
-    int64_t row = r0 + rc;
-    if (k >= op.K) {
-      v = (u32x4){0u, 0u, 0u, 0u};
-    } else if (row + 8 <= op.rows) {
-      v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(op.base + k * op.ld + row));
-    } else {
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t r_lo = row + 2 * e < op.rows ? row + 2 * e : op.rows - 1;
-        const int64_t r_hi = row + 2 * e + 1 < op.rows ? row + 2 * e + 1 : op.rows - 1;
-        w[e] = (uint32_t)op.base[k * op.ld + r_lo] | ((uint32_t)op.base[k * op.ld + r_hi] << 16);
-      }
-      v = (u32x4){w[0], w[1], w[2], w[3]};
-    }
-  }
-  return v;
-}
-
-template <int L, int R, int BK, int S>
-__device__ __forceinline__ void store_chunk(char* lds, int c, u32x4 v) {
-  int off;
-  if constexpr (L == ROWK) {
-    constexpr int CPR = BK / 8;
-    off = (c / CPR) * S + (c % CPR) * 16;
-  } else {
-    constexpr int CPK = R / 8;
-    off = (c / CPK) * S + (c % CPK) * 16;
-  }
-  *reinterpret_cast<u32x4*>(lds + off) = v;
-}
-
-// MFMA fragment (8 reduction values of one row) for rows r0 + lane % 32, k-slice kk.
-template <int L, int S>
-__device__ __forceinline__ bf16x8 read_frag(const char* lds, int r0, int kk, int lane) {
-  if constexpr (L == ROWK) {
-    const int off = (r0 + (lane & 31)) * S + (kk + (lane >> 5) * 8) * 2;
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lds + off));
+    const int row = r0 + (lane & 31);
+    const int c = (kk >> 3) + (lane >> 5);
+    ds_b128(f, lds_addr(lds + row * (BK * 2) + ((c ^ swz_rowk<BK>(row)) << 4)));
   } else {
     // Transposing read: within each 16-lane group, lane 4p + q addresses k-row (k0 + p),
-    // rows [4q, 4q + 4) of the group's 16 rows; lane i then holds row i at k0..k0+3.
+    // rows [4q, 4q + 4) of the group's 16 rows; lane i then holds row i at k0..k0+3
+    // (and k0+4..k0+7 from the second read, four k-rows further).
     const int g = lane >> 4, i = lane & 15, p = i >> 2, q = i & 3;
     const int rbase = r0 + (g & 1) * 16 + 4 * q;
-    const int kbase = kk + (g >> 1) * 8 + p;
-    const char* a0 = lds + kbase * S + rbase * 2;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 4 * S));
-    typedef short i16x8 __attribute__((ext_vector_type(8)));
-    const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, v);
+    const int kr = kk + (g >> 1) * 8 + p;
+    const int c = rbase >> 3, within = (rbase * 2) & 15;
+    const uint32_t a = lds_addr(lds + kr * (R * 2) + ((c ^ swz_krow(kr)) << 4) + within);
+    uint32_t lo[2], hi[2];
+    ds_tr16(lo, a);
+    ds_tr16(hi, a + 4 * (R * 2));
+    f = (u32x4){lo[0], lo[1], hi[0], hi[1]};
   }
+}
+
+template <class C>
+struct Frags {
+  u32x4 a[C::FM], b[C::FN];
+};
+
+template <class C>
+__device__ __forceinline__ void read_frags(Frags<C>& F, const char* sa, const char* sb, int wm, int wn, int kk, int lane) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) read_frag<C::LA, C::BM, C::BK>(F.a[i], sa, wm * C::TM + i * 32, kk, lane);
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) read_frag<C::LB, C::BN, C::BK>(F.b[j], sb, wn * C::TN + j * 32, kk, lane);
+}
+
+// Wait for every outstanding LDS read and make the fragments depend on that wait.
+template <class C>
+__device__ __forceinline__ void settle(Frags<C>& F) {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) asm volatile("" : "+v"(F.a[i]));
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) asm volatile("" : "+v"(F.b[j]));
 }
 
 // Accumulators of one wave: FM x FN blocks.
@@ -155,57 +178,86 @@ struct Acc {
   }
 };
 
+template <class C>
+__device__ __forceinline__ void mfmas(Acc<C>& acc, const Frags<C>& F) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+      acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, F.a[i]),
+                                                            __builtin_bit_cast(bf16x8, F.b[j]), acc.c[i][j], 0, 0, 0);
+}
+
+// Wait until at most n of this wave's DMA loads are outstanding (loads complete in order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Stage `s` has landed in LDS for every wave once this returns (given stages up to
+// min(nk - 1, s + NSTAGE - 2) were issued).
+template <class C>
+__device__ __forceinline__ void stage_ready(int s, int nk) {
+  const int newer = min(nk - 1 - s, C::NSTAGE - 2);
+  if (newer >= 2) wait_vm<2 * C::LOADS_PER_STAGE>();
+  else if (newer == 1) wait_vm<C::LOADS_PER_STAGE>();
+  else wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");  // keep LDS reads and DMA issues on their side of the barrier
+}
+
 // C_tile(m0, n0) = A[m0 : m0 + BM, :] * B[n0 : n0 + BN, :]^T over k in [0, K), into acc.
-// lds must hold 2 * STAGE_BYTES. All threads of the workgroup must call this.
+// lds must hold LDS_BYTES. All threads of the workgroup must call this; it ends with a
+// workgroup barrier, after which lds may be reused.
+//
+// Schedule: the fragments of the next k-slice are read while the MFMAs of the current
+// one run; at the last slice of stage s the workgroup waits for stage s + 1, refills the
+// stage-s buffer with stage s + NSTAGE, and reads stage s + 1's first fragments before
+// stage s's last MFMAs.
 template <class C>
 __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int64_t m0, int64_t n0, int64_t K,
                                          char* lds, Acc<C>& acc) {
+  constexpr int KQ = C::BK / 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int nk = (int)((K + C::BK - 1) / C::BK);
-  u32x4 ra[C::A_PER_T], rb[C::B_PER_T];
   acc.zero();
 
-  auto gload = [&](int s) {
+  auto issue = [&](int s) {
+    char* st = lds + (s % C::NSTAGE) * C::STAGE_BYTES;
     const int64_t k0 = (int64_t)s * C::BK;
-#pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i) ra[i] = load_chunk<C::LA, C::BM, C::BK>(A, m0, k0, tid + i * C::NT);
-#pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i) rb[i] = load_chunk<C::LB, C::BN, C::BK>(B, n0, k0, tid + i * C::NT);
+    dma_tile<C::LA, C::BM, C::BK, C::NW, C::A_INSTR>(A, m0, k0, st, wave, lane);
+    dma_tile<C::LB, C::BN, C::BK, C::NW, C::B_INSTR>(B, n0, k0, st + C::A_BYTES, wave, lane);
   };
-  auto lstore = [&](int buf) {
-    char* sa = lds + buf * C::STAGE_BYTES;
-    char* sb = sa + C::A_BYTES;
-#pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i) store_chunk<C::LA, C::BM, C::BK, C::SA>(sa, tid + i * C::NT, ra[i]);
-#pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i) store_chunk<C::LB, C::BN, C::BK, C::SB>(sb, tid + i * C::NT, rb[i]);
-  };
+  auto stage_a = [&](int s) -> const char* { return lds + (s % C::NSTAGE) * C::STAGE_BYTES; };
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int s = 0; s < nk; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nk) gload(s + 1);
-    const char* sa = lds + buf * C::STAGE_BYTES;
-    const char* sb = sa + C::A_BYTES;
 #pragma unroll
-    for (int kk = 0; kk < C::BK; kk += 16) {
-      bf16x8 fa[C::FM], fb[C::FN];
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) fa[i] = read_frag<C::LA, C::SA>(sa, wm * C::TM + i * 32, kk, lane);
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) fb[j] = read_frag<C::LB, C::SB>(sb, wn * C::TN + j * 32, kk, lane);
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-          acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc.c[i][j], 0, 0, 0);
-    }
-    if (s + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
+  for (int s = 0; s < C::NSTAGE - 1; ++s)
+    if (s < nk) issue(s);
+  Frags<C> F[2];
+  if (nk > 0) {
+    stage_ready<C>(0, nk);
+    if (C::NSTAGE - 1 < nk) issue(C::NSTAGE - 1);
+    read_frags<C>(F[0], stage_a(0), stage_a(0) + C::A_BYTES, wm, wn, 0, lane);
   }
+  int cur = 0;
+  for (int s = 0; s < nk; ++s) {
+#pragma unroll
+    for (int q = 0; q < KQ; ++q) {
+      settle<C>(F[cur]);
+      if (q + 1 < KQ) {
+        read_frags<C>(F[cur ^ 1], stage_a(s), stage_a(s) + C::A_BYTES, wm, wn, (q + 1) * 16, lane);
+      } else if (s + 1 < nk) {
+        stage_ready<C>(s + 1, nk);
+        if (s + C::NSTAGE < nk) issue(s + C::NSTAGE);
+        read_frags<C>(F[cur ^ 1], stage_a(s + 1), stage_a(s + 1) + C::A_BYTES, wm, wn, 0, lane);
+      }
+      mfmas<C>(acc, F[cur]);
+      cur ^= 1;
+    }
+  }
+  __syncthreads();
 }
 
 // Row / column of accumulator v of block (i, j) for this lane, relative to the wave tile.

@@ -29,17 +29,19 @@ using gemm::KROW;
 using gemm::Operand;
 using gemm::ROWK;
 
-typedef Cfg<256, 256, 32, 2, 4, ROWK, ROWK> CfgNT;  // A, B both reduction-contiguous
-typedef Cfg<256, 256, 32, 2, 4, ROWK, KROW> CfgNN;  // dh = dz W
-typedef Cfg<256, 256, 32, 2, 4, KROW, KROW> CfgTN;  // dW = dz^T h
+typedef Cfg<256, 256, 64, 2, 4, ROWK, ROWK, 2> CfgNT;  // A, B both reduction-contiguous
+typedef Cfg<256, 256, 32, 2, 4, ROWK, KROW, 4> CfgNN;  // dh = dz W
+typedef Cfg<256, 256, 32, 2, 4, KROW, KROW, 4> CfgTN;  // dW = dz^T h
 
-constexpr int kLinThreads = 512;
-static_assert(CfgNT::NT == kLinThreads && CfgNN::NT == kLinThreads && CfgTN::NT == kLinThreads, "threads");
+namespace gemm {
+__device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
+}  // namespace gemm
+
 
 // ---- forward -----------------------------------------------------------------------
 
-__global__ __launch_bounds__(kLinThreads) void lin_fwd_kernel(LinArgs p) {
-  typedef CfgNT C;
+template <class C>
+__global__ __launch_bounds__(C::NT) void lin_fwd_kernel(LinArgs p) {
   extern __shared__ __align__(16) char lds[];
   const int nchunks = p.chunks;
   const int64_t tt = blockIdx.x / nchunks;   // token tile
@@ -169,8 +171,8 @@ __device__ __forceinline__ void xcd_tile(int64_t b, int64_t ntt, int64_t nvt, in
   }
 }
 
-__global__ __launch_bounds__(kLinThreads) void lin_dz_kernel(LinArgs p) {
-  typedef CfgNT C;
+template <class C>
+__global__ __launch_bounds__(C::NT) void lin_dz_kernel(LinArgs p) {
   extern __shared__ __align__(16) char lds[];
   const int64_t ntt = (p.N + C::BM - 1) / C::BM, nvt = (p.V + C::BN - 1) / C::BN;
   int64_t tt, vt;
@@ -215,7 +217,8 @@ __global__ __launch_bounds__(kLinThreads) void lin_dz_kernel(LinArgs p) {
         const float pz = expf_fast((acc.c[i][j][v] - m) - ls);
         float d = (col == t) ? gv * (1.0f - pz) : -gv * pz;
         d = ignored ? 0.0f : (bad ? __builtin_nanf("") : d);
-        if (n < p.N && col < p.V) {
+        d = col < p.V ? d : 0.0f;  // columns [V, ldz) pad the rows with zeros for the dh contraction
+        if (n < p.N && col < p.ldz) {
           const bf16x2 hb = __builtin_convertvector((f32x2){d, 0.0f}, bf16x2);
           p.dz[n * p.ldz + col] = (uint16_t)(__builtin_bit_cast(uint32_t, hb) & 0xffffu);
         }
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(kLinThreads) void lin_dz_kernel(LinArgs p) {
 // C = A B^T over K with bf16 (RNE) stores; used for dh (A = dz rows, B = W^T via KROW) and
 // dW (A = dz^T via KROW, B = h^T via KROW).
 template <class C>
-__global__ __launch_bounds__(kLinThreads) void gemm_store_kernel(GemmArgs g) {
+__global__ __launch_bounds__(C::NT) void gemm_store_kernel(GemmArgs g) {
   extern __shared__ __align__(16) char lds[];
   const int64_t ntm = (g.M + C::BM - 1) / C::BM, ntn = (g.Nc + C::BN - 1) / C::BN;
   // consecutive blocks share the A tile (on different XCDs they still share it in the MALL)
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(kLinThreads) void gemm_store_kernel(GemmArgs g) {
 namespace {
 template <class C>
 size_t lds_bytes() {
-  return (size_t)2 * C::STAGE_BYTES;
+  return (size_t)C::LDS_BYTES;
 }
 }  // namespace
 
@@ -281,7 +284,7 @@ hipError_t launch_lin_fwd(LinArgs p, hipStream_t stream) {
   hipLaunchKernelGGL(lin_target_kernel, dim3((uint32_t)((p.N + 3) / 4)), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lin_fwd_kernel, dim3((uint32_t)(ntt * p.chunks)), dim3(kLinThreads), lds_bytes<CfgNT>(), stream, p);
+  hipLaunchKernelGGL((lin_fwd_kernel<CfgNT>), dim3((uint32_t)(ntt * p.chunks)), dim3(CfgNT::NT), lds_bytes<CfgNT>(), stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(lin_combine_kernel, dim3((uint32_t)((p.N + 255) / 256)), dim3(256), 0, stream, p);
   return hipGetLastError();
@@ -289,21 +292,21 @@ hipError_t launch_lin_fwd(LinArgs p, hipStream_t stream) {
 
 hipError_t launch_lin_bwd(LinArgs p, uint16_t* dh, uint16_t* dW, hipStream_t stream) {
   const int64_t ntt = (p.N + CfgNT::BM - 1) / CfgNT::BM, nvt = (p.V + CfgNT::BN - 1) / CfgNT::BN;
-  hipLaunchKernelGGL(lin_dz_kernel, dim3((uint32_t)(ntt * nvt)), dim3(kLinThreads), lds_bytes<CfgNT>(), stream, p);
+  hipLaunchKernelGGL((lin_dz_kernel<CfgNT>), dim3((uint32_t)(ntt * nvt)), dim3(CfgNT::NT), lds_bytes<CfgNT>(), stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (dh) {
     // dh[n, k] = sum_v dz[n, v] W[v, k]: A = dz (ROWK, reduction v), B(k, v) = W[v, k] (KROW)
-    GemmArgs g{Operand{p.dz, p.ldz, p.N, p.V}, Operand{p.W, p.ldw, p.H, p.V}, dh, p.H, p.N, p.H, p.V};
-    const int64_t blocks = ((p.N + 255) / 256) * ((p.H + 255) / 256);
-    hipLaunchKernelGGL((gemm_store_kernel<CfgNN>), dim3((uint32_t)blocks), dim3(kLinThreads), lds_bytes<CfgNN>(), stream, g);
+    GemmArgs g{Operand{p.dz, p.ldz, p.N, p.ldz}, Operand{p.W, p.ldw, p.H, p.V}, dh, p.H, p.N, p.H, p.ldz};
+    const int64_t blocks = ((p.N + CfgNN::BM - 1) / CfgNN::BM) * ((p.H + CfgNN::BN - 1) / CfgNN::BN);
+    hipLaunchKernelGGL((gemm_store_kernel<CfgNN>), dim3((uint32_t)blocks), dim3(CfgNN::NT), lds_bytes<CfgNN>(), stream, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (dW) {
     // dW[v, k] = sum_n dz[n, v] h[n, k]: A(v, n) = dz[n, v] (KROW), B(k, n) = h[n, k] (KROW)
-    GemmArgs g{Operand{p.dz, p.ldz, p.V, p.N}, Operand{p.h, p.ldh, p.H, p.N}, dW, p.ldw_out, p.V, p.H, p.N};
-    const int64_t blocks = ((p.V + 255) / 256) * ((p.H + 255) / 256);
-    hipLaunchKernelGGL((gemm_store_kernel<CfgTN>), dim3((uint32_t)blocks), dim3(kLinThreads), lds_bytes<CfgTN>(), stream, g);
+    GemmArgs g{Operand{p.dz, p.ldz, p.ldz, p.N}, Operand{p.h, p.ldh, p.H, p.N}, dW, p.ldw_out, p.V, p.H, p.N};
+    const int64_t blocks = ((p.V + CfgTN::BM - 1) / CfgTN::BM) * ((p.H + CfgTN::BN - 1) / CfgTN::BN);
+    hipLaunchKernelGGL((gemm_store_kernel<CfgTN>), dim3((uint32_t)blocks), dim3(CfgTN::NT), lds_bytes<CfgTN>(), stream, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
