@@ -214,7 +214,7 @@ def _oracle_rows(args):
     return int(np.asarray(a).shape[0])
 
 
-def cpu_baseline(wl, rows=256):
+def cpu_baseline(wl, rows=8192):
     """The fp64 oracle on `rows` rows of the same workload, row chunks spread over host
     threads (numpy releases the GIL inside its array kernels)."""
     from concurrent.futures import ThreadPoolExecutor
@@ -359,7 +359,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-linear", action="store_true", help="skip the fused linear-logp workload")
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--summarize", nargs=2, metavar=("DIR", "MODE"))
     ap.add_argument("--counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"))
