@@ -16,6 +16,8 @@ linear logp Triton"):
   KL = W/S_A - log S_A + log S_B (PR #8838, second commit message and the
   review comment "read each logit once") are evaluated separately by
   ``single_read_identities`` as a self-check, never as the answer.
+* ``topk``        -- multi-id (top-k) log-probabilities: K ids per row, ignored
+  slots, duplicate ids whose upstream gradients add (the PR #8838 test list).
 * ``linear_logp`` -- the fused linear-logp variant of RL-Kernel PR #208
   (PR body, "Implementation"): logits z = h W^T in float64, then the same
   log-probability and its gradients dh, dW by the chain rule.
@@ -24,9 +26,9 @@ linear logp Triton"):
   placement) and the bf16 round-to-nearest-even helpers it needs.
 
 Every function that has no independent pin would say "parity unpinned"; all
-functions here are pinned by tests/test_oracle_pins.py (brute force at 50
-digits with mpmath, torch.log_softmax in float64, closed forms, identities,
-finite differences and the extreme-range cases the pages describe).
+functions here are pinned by tests/test_oracle_pins*.py (brute force at 50
+digits with mpmath, torch.log_softmax and autograd in float64, closed forms,
+identities, finite differences and the extreme-range cases the pages describe).
 """
 
-from . import reductions, linear_logp, compare  # noqa: F401
+from . import reductions, topk, linear_logp, compare  # noqa: F401
