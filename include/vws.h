@@ -105,6 +105,14 @@ typedef struct vws_ids {
   int64_t s_outer, s_inner;
 } vws_ids;
 
+/* K ids per row for the multi-id logprobs: slot k of row r = r_o * n_inner + r_i
+ * at data[r_o * s_outer + r_i * s_inner + k * s_k]; 1 <= K <= 2048. */
+typedef struct vws_ids_k {
+  const int64_t* data;
+  int64_t s_outer, s_inner, s_k;
+  int64_t K;
+} vws_ids_k;
+
 /*
  * Bytes of workspace the forward of `op` needs for N rows of V columns with the
  * given split_hint. The forward splits each row's vocabulary over P workgroups
@@ -139,6 +147,31 @@ VWS_API int vws_logprobs_fwd(const vws_rows* z, const vws_ids* t, int64_t ignore
  */
 VWS_API int vws_logprobs_bwd(const vws_rows* z, const vws_ids* t, int64_t ignore_index, const float* stats,
                              const float* g, int64_t g_stride, void* dz, void* stream);
+
+/*
+ * Multi-id (top-k) log-probabilities: K target ids per row (PR #8838 lists
+ * duplicate and ignored top-k ids and a fully ignored row among its logprobs
+ * test cases).
+ *   ids     K ids per row (vws_ids_k); a slot equal to ignore_index gives 0,
+ *           any other slot outside [0, V) gives NaN
+ *   logp    out fp32 [N, K] contiguous: logp[r, k] = (z_id - m) - log S
+ *   stats   out fp32 [N, 2] = (m, log S);  ws as for vws_logprobs_fwd
+ *           (vws_workspace_bytes(VWS_OP_LOGPROBS, ...))
+ */
+VWS_API int vws_logprobs_topk_fwd(const vws_rows* z, const vws_ids_k* ids, int64_t ignore_index, float* logp,
+                                  float* stats, void* ws, size_t ws_bytes, int split_hint, void* stream);
+
+/*
+ * Gradient of sum_k g[r, k] logp[r, k]:  dz_j = h_j - G p_j, where h_j sums
+ * g[r, k] over the live slots whose id is j (duplicate ids add) and G sums g
+ * over all live slots. A row whose slots are all ignored gets a zero gradient
+ * row; a row with a live slot outside [0, V) a NaN row.
+ *   g       fp32 upstream gradient, element (r, k) at g[r * g_s_row + k * g_s_k]
+ *           (zero strides broadcast)
+ *   stats   as written by vws_logprobs_topk_fwd;  dz out [N, V] contiguous, dtype of z
+ */
+VWS_API int vws_logprobs_topk_bwd(const vws_rows* z, const vws_ids_k* ids, int64_t ignore_index, const float* stats,
+                                  const float* g, int64_t g_s_row, int64_t g_s_k, void* dz, void* stream);
 
 /*
  * Entropy H = -sum p log p = log S - W_H / S in one read (second commit

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(L):
     assert len(names) >= 10
     for n in names:
         assert hasattr(L, n), n
-    assert L.vws_version() == 100
+    assert L.vws_version() == 101
 
 
 def test_strerror(L):
@@ -135,3 +135,32 @@ def test_linear_validation(L):
                1 << 20, None) == 0  # no gradient requested
     assert bwd(0x1000, 64, 0x2000, 64, B.VWS_BF16, 4, 64, 100, 0x3000, -100, 0x5000, 0x7000, 1, 0x8000, None, 0x6000,
                16, None) == EWORKSPACE
+
+
+def test_topk_validation(L):
+    a = _rows()
+
+    def fwd(ids=0x7000, s_o=8, s_i=0, s_k=1, K=8, logp=0x2000, stats=0x3000, r=None):
+        t = B.vws_ids_k(ids, s_o, s_i, s_k, K)
+        r = r or a
+        return L.vws_logprobs_topk_fwd(ctypes.byref(r), ctypes.byref(t), -100, logp, stats, None, 0, 0, None)
+
+    def bwd(ids=0x7000, K=8, s_k=1, gr=8, gk=1, dz=0x6000, stats=0x3000):
+        t = B.vws_ids_k(ids, 8, 0, s_k, K)
+        return L.vws_logprobs_topk_bwd(ctypes.byref(a), ctypes.byref(t), -100, stats, 0x5000, gr, gk, dz, None)
+
+    assert fwd(K=0) == EINVAL
+    assert fwd(K=2049) == EINVAL
+    assert fwd(ids=0) == EINVAL
+    assert fwd(ids=0x7004) == ELAYOUT
+    assert fwd(s_k=-1) == ELAYOUT
+    assert fwd(logp=0) == EINVAL
+    assert fwd(stats=0) == EINVAL
+    assert fwd(logp=0x2002) == ELAYOUT
+    assert fwd(r=_rows(n_outer=0, data=0), ids=0, logp=0, stats=0) == 0  # empty batch
+    assert bwd(K=0) == EINVAL
+    assert bwd(gr=-1) == EINVAL
+    assert bwd(gk=-1) == EINVAL
+    assert bwd(dz=0) == EINVAL
+    assert bwd(dz=0x6001) == ELAYOUT
+    assert bwd(stats=0) == EINVAL

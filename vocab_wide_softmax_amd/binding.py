@@ -47,6 +47,11 @@ class vws_ids(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("s_outer", ctypes.c_int64), ("s_inner", ctypes.c_int64)]
 
 
+class vws_ids_k(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("s_outer", ctypes.c_int64), ("s_inner", ctypes.c_int64),
+                ("s_k", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -59,12 +64,14 @@ def lib():
         L = ctypes.CDLL(_LIB_PATH)
         P, I64, I32, SZ, VP, FP = (ctypes.POINTER, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p,
                                    ctypes.c_void_p)
-        R, T = P(vws_rows), P(vws_ids)
+        R, T, TK = P(vws_rows), P(vws_ids), P(vws_ids_k)
         sig = {
             "vws_workspace_bytes": (SZ, [I32, I64, I64, I32]),
             "vws_split_parts": (I32, [I32, I64, I64, I32]),
             "vws_logprobs_fwd": (I32, [R, T, I64, FP, FP, VP, SZ, I32, VP]),
             "vws_logprobs_bwd": (I32, [R, T, I64, FP, FP, I64, VP, VP]),
+            "vws_logprobs_topk_fwd": (I32, [R, TK, I64, FP, FP, VP, SZ, I32, VP]),
+            "vws_logprobs_topk_bwd": (I32, [R, TK, I64, FP, FP, I64, I64, VP, VP]),
             "vws_entropy_fwd": (I32, [R, FP, FP, VP, SZ, I32, VP]),
             "vws_entropy_bwd": (I32, [R, FP, FP, FP, I64, VP, VP]),
             "vws_kl_fwd": (I32, [R, R, FP, FP, VP, SZ, I32, VP]),
@@ -124,6 +131,17 @@ def ids(t: torch.Tensor, like: torch.Tensor) -> vws_ids:
     if t.dim() == 1:
         return vws_ids(t.data_ptr(), t.stride(0), 0)
     return vws_ids(t.data_ptr(), t.stride(0), t.stride(1))
+
+
+def ids_k(t: torch.Tensor, like: torch.Tensor) -> vws_ids_k:
+    """Descriptor of int64 ids shaped like ``like`` with its last dim replaced by K."""
+    if t.dtype != torch.int64:
+        raise TypeError("ids must be int64")
+    if t.dim() != like.dim() or tuple(t.shape[:-1]) != tuple(like.shape[:-1]):
+        raise ValueError("ids shape %s does not match logits %s" % (tuple(t.shape), tuple(like.shape)))
+    if t.dim() == 2:
+        return vws_ids_k(t.data_ptr(), t.stride(0), 0, t.stride(1), t.shape[1])
+    return vws_ids_k(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2), t.shape[2])
 
 
 def _n_rows(z):
@@ -197,6 +215,41 @@ def logprobs_bwd(z, t, stats, g, ignore_index=-100):
     r, ti = rows(z), ids(t, z)
     _check("vws_logprobs_bwd", L.vws_logprobs_bwd(ctypes.byref(r), ctypes.byref(ti), ignore_index, _ptr(stats),
                                                   _ptr(g), gs, _ptr(dz), _stream(z.device)))
+    return dz
+
+
+def logprobs_topk_fwd(z, ids, ignore_index=-100, split_hint=0):
+    """(logp fp32 [N..., K], stats fp32 [N, 2]) for K ids per row -- vws_logprobs_topk_fwd."""
+    L = lib()
+    ti = ids_k(ids, z)
+    n = _n_rows(z)
+    logp = torch.empty(tuple(z.shape[:-1]) + (ti.K,), dtype=torch.float32, device=z.device)
+    stats = torch.empty((n, 2), dtype=torch.float32, device=z.device)
+    ws, nb = _workspace(OP_LOGPROBS, z, split_hint)
+    r = rows(z)
+    _check("vws_logprobs_topk_fwd", L.vws_logprobs_topk_fwd(ctypes.byref(r), ctypes.byref(ti), ignore_index,
+                                                            _ptr(logp), _ptr(stats), _ptr(ws), nb, split_hint,
+                                                            _stream(z.device)))
+    return logp, stats
+
+
+def logprobs_topk_bwd(z, ids, stats, g, ignore_index=-100):
+    """dz [shape of z, contiguous, dtype of z] of sum g * logp over the K slots -- vws_logprobs_topk_bwd."""
+    L = lib()
+    ti = ids_k(ids, z)
+    n = _n_rows(z)
+    if g.dtype != torch.float32:
+        g = g.float()
+    if g.numel() == 1 or all(st == 0 for st in g.stride()):
+        gs_r, gs_k = 0, 0
+    else:
+        g = g.reshape(n, ti.K)
+        gs_r, gs_k = g.stride(0), g.stride(1)
+    dz = torch.empty(z.shape, dtype=z.dtype, device=z.device)
+    r = rows(z)
+    _check("vws_logprobs_topk_bwd", L.vws_logprobs_topk_bwd(ctypes.byref(r), ctypes.byref(ti), ignore_index,
+                                                            _ptr(stats), _ptr(g), gs_r, gs_k, _ptr(dz),
+                                                            _stream(z.device)))
     return dz
 
 

@@ -104,8 +104,9 @@ int parts_for(int op, int64_t N, int64_t V, int hint) {
   return (int)P;
 }
 
+// stats_only (logprobs): write the row statistics but no per-row output, for the multi-id forward.
 int fwd_common(int op, const vws_rows* a, const vws_rows* b, const vws_ids* t, int64_t ignore_index, float* out,
-               float* stats, void* ws, size_t ws_bytes, int split_hint, void* stream) {
+               float* stats, void* ws, size_t ws_bytes, int split_hint, void* stream, bool stats_only = false) {
   int64_t N, Nb;
   int rc = check_rows(a, &N);
   if (rc) return rc;
@@ -116,8 +117,8 @@ int fwd_common(int op, const vws_rows* a, const vws_rows* b, const vws_ids* t, i
   }
   if (split_hint < 0) return VWS_EINVAL;
   if (N == 0) return VWS_OK;
-  if (op == VWS_OP_LOGPROBS && (rc = check_ids(t))) return rc;
-  if (!out || !stats) return VWS_EINVAL;
+  if (op == VWS_OP_LOGPROBS && !stats_only && (rc = check_ids(t))) return rc;
+  if ((!out && !stats_only) || !stats) return VWS_EINVAL;
   if (!aligned(out, 4) || !aligned(stats, 4)) return VWS_ELAYOUT;
   const int P = parts_for(op, N, a->V, split_hint);
   if (N * (int64_t)P > (int64_t)INT32_MAX) return VWS_EINVAL;
@@ -128,14 +129,14 @@ int fwd_common(int op, const vws_rows* a, const vws_rows* b, const vws_ids* t, i
   FwdArgs p{};
   p.a = rows_dev(a);
   if (op == VWS_OP_KL) p.b = rows_dev(b);
-  p.ids = ids_dev(op == VWS_OP_LOGPROBS ? t : nullptr);
+  p.ids = ids_dev(op == VWS_OP_LOGPROBS && !stats_only ? t : nullptr);
   p.N = N;
   p.V = a->V;
   p.ignore_index = ignore_index;
   p.parts = P;
   const int64_t G = (a->V + 7) / 8;
   p.groups_per_part = (int32_t)((G + P - 1) / P);
-  p.out = out;
+  p.out = stats_only ? nullptr : out;
   p.stats = stats;
   p.ws = static_cast<float*>(ws);
   const bool vec = rows_vec_ok(a) && (op != VWS_OP_KL || rows_vec_ok(b));
@@ -186,6 +187,28 @@ int bwd_common(int op, const vws_rows* a, const vws_rows* b, const vws_ids* t, i
                    out_vec_ok(db, N, a->V, es);
   hipError_t e = vws::launch_bwd(op, p, a->dtype, vec, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? VWS_OK : VWS_EHIP;
+}
+
+int check_ids_k(const vws_ids_k* t) {
+  if (!t || !t->data) return VWS_EINVAL;
+  if (t->K < 1 || t->K > vws::kTopkMaxK) return VWS_EINVAL;
+  if (t->s_outer < 0 || t->s_inner < 0 || t->s_k < 0) return VWS_ELAYOUT;
+  if (!aligned(t->data, 8)) return VWS_ELAYOUT;
+  return VWS_OK;
+}
+
+vws::TopkArgs topk_args(const vws_rows* z, const vws_ids_k* t, int64_t N, int64_t ignore_index) {
+  vws::TopkArgs p{};
+  p.a = rows_dev(z);
+  p.ids = t->data;
+  p.ids_so = t->s_outer;
+  p.ids_si = t->s_inner;
+  p.ids_sk = t->s_k;
+  p.K = (int32_t)t->K;
+  p.N = N;
+  p.V = z->V;
+  p.ignore_index = ignore_index;
+  return p;
 }
 
 int64_t round_up8(int64_t x) { return (x + 7) / 8 * 8; }
@@ -332,6 +355,55 @@ VWS_API int vws_kl_bwd(const vws_rows* a, const vws_rows* b, const float* stats,
   return bwd_common(VWS_OP_KL, a, b, nullptr, 0, stats, kl, g, g_stride, da, db, stream);
 }
 
+VWS_API int vws_logprobs_topk_fwd(const vws_rows* z, const vws_ids_k* ids, int64_t ignore_index, float* logp,
+                                  float* stats, void* ws, size_t ws_bytes, int split_hint, void* stream) {
+  int64_t N;
+  int rc = check_rows(z, &N);
+  if (rc) return rc;
+  if (split_hint < 0) return VWS_EINVAL;
+  if (N == 0) return VWS_OK;
+  if ((rc = check_ids_k(ids))) return rc;
+  if (!logp || !stats) return VWS_EINVAL;
+  if (!aligned(logp, 4)) return VWS_ELAYOUT;
+  int64_t nk;
+  if (!mul_ok(N, ids->K, &nk)) return VWS_EINVAL;
+  rc = fwd_common(VWS_OP_LOGPROBS, z, nullptr, nullptr, ignore_index, nullptr, stats, ws, ws_bytes, split_hint,
+                  stream, true);
+  if (rc) return rc;
+  vws::TopkArgs p = topk_args(z, ids, N, ignore_index);
+  p.stats = stats;
+  p.out = logp;
+  hipError_t e = vws::launch_topk_gather(p, z->dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VWS_OK : VWS_EHIP;
+}
+
+VWS_API int vws_logprobs_topk_bwd(const vws_rows* z, const vws_ids_k* ids, int64_t ignore_index, const float* stats,
+                                  const float* g, int64_t g_s_row, int64_t g_s_k, void* dz, void* stream) {
+  int64_t N;
+  int rc = check_rows(z, &N);
+  if (rc) return rc;
+  if (g_s_row < 0 || g_s_k < 0) return VWS_EINVAL;
+  if (N == 0) return VWS_OK;
+  if ((rc = check_ids_k(ids))) return rc;
+  if (!stats || !g || !dz) return VWS_EINVAL;
+  const int es = elem_size(z->dtype);
+  if (!aligned(stats, 4) || !aligned(g, 4) || !aligned(dz, es)) return VWS_ELAYOUT;
+  int64_t nv, bytes;
+  if (!mul_ok(N, z->V, &nv) || !mul_ok(nv, es, &bytes)) return VWS_EINVAL;
+  const int32_t tpr = vws::topk_tiles_per_row(z->V);
+  if (N * (int64_t)tpr > (int64_t)INT32_MAX) return VWS_EINVAL;
+  vws::TopkArgs p = topk_args(z, ids, N, ignore_index);
+  p.tiles_per_row = tpr;
+  p.stats = stats;
+  p.g = g;
+  p.g_sr = g_s_row;
+  p.g_sk = g_s_k;
+  p.dz = static_cast<char*>(dz);
+  const bool vec = rows_vec_ok(z) && out_vec_ok(dz, N, z->V, es);
+  hipError_t e = vws::launch_topk_bwd(p, z->dtype, vec, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VWS_OK : VWS_EHIP;
+}
+
 VWS_API const char* vws_strerror(int status) {
   switch (status) {
     case VWS_OK: return "ok";
@@ -344,6 +416,6 @@ VWS_API const char* vws_strerror(int status) {
   }
 }
 
-VWS_API int vws_version(void) { return 100; }
+VWS_API int vws_version(void) { return 101; }
 
 }  // extern "C"

@@ -109,6 +109,7 @@ __device__ void finalize1_logprobs(const FwdArgs& p, int64_t row, const State1& 
   const double logS = log_d(st.S);
   p.stats[2 * row + 0] = st.m;
   p.stats[2 * row + 1] = (float)logS;
+  if (p.out == nullptr) return;  // statistics only (the multi-id forward gathers its slots afterwards)
   const int64_t t = load_id(p.ids, row, p.a.n_inner);
   float out;
   if (t == p.ignore_index) {

@@ -32,6 +32,28 @@ struct BwdArgs {
   char* db;
 };
 
+// Multi-id (top-k) logprobs: ids[n, k] at ids[r_o * ids_so + r_i * ids_si + k * ids_sk] with the
+// logits' row decomposition; upstream g[n, k] at g[n * g_sr + k * g_sk].
+constexpr int kTopkMaxK = 2048;
+
+struct TopkArgs {
+  RowsDev a;
+  const int64_t* ids;
+  int64_t ids_so, ids_si, ids_sk;
+  int32_t K;
+  int32_t tiles_per_row;
+  int64_t N, V, ignore_index;
+  const float* stats;  // [N, 2] (m, log S)
+  float* out;          // [N, K] contiguous (forward)
+  const float* g;      // backward
+  int64_t g_sr, g_sk;
+  char* dz;  // [N, V] contiguous, dtype of the logits
+};
+
+int32_t topk_tiles_per_row(int64_t V);
+hipError_t launch_topk_gather(const TopkArgs& p, int dtype, hipStream_t stream);
+hipError_t launch_topk_bwd(const TopkArgs& p, int dtype, bool vec, hipStream_t stream);
+
 // Fused linear-logp: h [N, H] and W [V, H] bf16 (row strides ldh, ldw), targets t [N].
 struct LinArgs {
   const uint16_t* h;

@@ -1,0 +1,194 @@
+// topk.hip -- multi-id (top-k) log-probabilities: K target ids per row.
+//
+// DeepSpeed PR #8838 "Add Triton kernels for vocab-parallel logprobs, entropy
+// and KL" lists duplicate and ignored top-k ids and a fully ignored row among
+// its logprobs test cases. With ids[n, k] (k < K) and upstream g[n, k]:
+//
+//   forward    out[n, k] = (z_id - m) - log S          (0 for ignore_index,
+//                                                        NaN outside [0, V))
+//   backward   dz_j = h_j - G p_j,   h_j = sum of g[n, k] over live slots with
+//              ids[n, k] = j (duplicates add), G = sum of g over live slots;
+//              a row with every slot ignored gets a zero gradient, a row with
+//              any out-of-range live slot a NaN gradient.
+//
+// The forward reuses the single-read (m, S) pass of the logprobs forward, which
+// writes the row statistics; a gather kernel (one thread per slot) then forms
+// out[n, k]. The backward is one pass over the logits per (row, column tile),
+// like the single-id backward; each workgroup first collects, in slot order,
+// the live ids that fall in its tile into LDS, so the per-column hit sums are
+// formed in the same order in every run.
+#include "device.h"
+#include "launch.h"
+
+namespace vws {
+
+namespace {
+constexpr int kTopkBlock = 256;
+constexpr int kTopkUB = 2;
+}  // namespace
+
+__device__ __forceinline__ int64_t topk_id(const TopkArgs& p, int64_t row, int32_t k) {
+  const int64_t ro = row / p.a.n_inner, ri = row - ro * p.a.n_inner;
+  return p.ids[ro * p.ids_so + ri * p.ids_si + (int64_t)k * p.ids_sk];
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void topk_gather_kernel(TopkArgs p) {
+  const int64_t total = p.N * p.K;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t row = i / p.K;
+    const int32_t k = (int32_t)(i - row * p.K);
+    const int64_t t = topk_id(p, row, k);
+    float out;
+    if (t == p.ignore_index) {
+      out = 0.0f;
+    } else if (t < 0 || t >= p.V) {
+      out = __builtin_nanf("");
+    } else {
+      const float zt = load_elem<DT>(row_ptr<DT>(p.a, row), t);
+      out = (float)(((double)zt - (double)p.stats[2 * row]) - (double)p.stats[2 * row + 1]);
+    }
+    p.out[i] = out;
+  }
+}
+
+template <int DT, bool FULL>
+__device__ __forceinline__ void topk_groups(const char* ra, char* oa, int32_t g, int n, int32_t G, int32_t V,
+                                            int32_t g_full, int32_t c0, float m, float ls, float Gs, bool nan_row,
+                                            bool zero_row, const int32_t* s_col, const float* s_g, int cnt) {
+  const float qnan = __builtin_nanf("");
+  for (int u = 0; u < n; ++u, g += kTopkBlock) {
+    if (!FULL && g >= G) break;
+    float x[8], y[8], h[8];
+    if (FULL) load_group_vec<DT>(ra, g, x);
+    else load_group<DT, true>(ra, g, V, g_full, x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = 0.0f;
+    const int32_t lg = g - (c0 >> 3);  // group index inside the tile
+    for (int e = 0; e < cnt; ++e) {
+      const int32_t c = s_col[e];
+      if ((c >> 3) == lg) {
+        const float gk = s_g[e];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j == (c & 7)) h[j] += gk;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float pj = expf_fast((x[j] - m) - ls);
+      y[j] = zero_row ? 0.0f : (nan_row ? qnan : __builtin_fmaf(-Gs, pj, h[j]));
+    }
+    if (FULL) store_group_vec<DT>(oa, g, y);
+    else store_group<DT, true>(oa, g, V, g_full, y);
+  }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kTopkBlock) void topk_bwd_kernel(TopkArgs p) {
+  constexpr int NW = kTopkBlock / 64;
+  constexpr int ES = ElemSize<DT>::value;
+  __shared__ int32_t s_col[kTopkMaxK];
+  __shared__ float s_g[kTopkMaxK];
+  __shared__ float s_red[NW];
+  __shared__ int32_t s_cnt[NW];
+  __shared__ int32_t s_flags;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t tpr = p.tiles_per_row;
+  const int64_t total = p.N * tpr;
+  const int32_t V = (int32_t)p.V;
+  const int32_t G = (V + 7) / 8;
+  const int32_t g_full = VEC ? V / 8 : 0;
+  for (int64_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
+    const int64_t row = vb / tpr;
+    const int32_t tile = (int32_t)(vb - row * tpr);
+    const int32_t g0 = tile * (kTopkBlock * kTopkUB);
+    const int32_t c0 = g0 * 8, c1 = min(V, c0 + kTopkBlock * kTopkUB * 8);
+
+    // Slots: G (sum of live g, fixed reduction tree), flags, and the tile's live ids in slot order.
+    if (tid == 0) s_flags = 0;
+    __syncthreads();
+    float gpart = 0.0f;
+    int flags = 0;  // bit 0: some slot live, bit 1: some live slot out of range
+    int32_t cnt = 0;
+    for (int32_t kc = 0; kc < p.K; kc += kTopkBlock) {
+      const int32_t k = kc + tid;
+      bool hit = false;
+      int32_t col = 0;
+      float gk = 0.0f;
+      if (k < p.K) {
+        const int64_t t = topk_id(p, row, k);
+        if (t != p.ignore_index) {
+          flags |= 1;
+          if (t < 0 || t >= V) {
+            flags |= 2;
+          } else {
+            gk = p.g[row * p.g_sr + (int64_t)k * p.g_sk];
+            gpart += gk;
+            hit = t >= c0 && t < c1;
+            col = (int32_t)(t - c0);
+          }
+        }
+      }
+      const uint64_t bal = __ballot(hit);
+      const int32_t before = (int32_t)__popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) s_cnt[wave] = (int32_t)__popcll(bal);
+      __syncthreads();
+      int32_t base = cnt;
+      for (int w = 0; w < wave; ++w) base += s_cnt[w];
+      if (hit) {
+        s_col[base + before] = col;
+        s_g[base + before] = gk;
+      }
+      for (int w = 0; w < NW; ++w) cnt += s_cnt[w];
+      __syncthreads();  // s_cnt is rewritten by the next chunk
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) gpart += __shfl_xor(gpart, off, 64);
+    if (flags) atomicOr(&s_flags, flags);
+    if (lane == 0) s_red[wave] = gpart;
+    __syncthreads();
+    float Gs = s_red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) Gs += s_red[w];
+    const int fl = s_flags;
+
+    const char* ra = row_ptr<DT>(p.a, row);
+    char* oa = p.dz + row * (int64_t)V * ES;
+    const float m = p.stats[2 * row], ls = p.stats[2 * row + 1];
+    const bool zero_row = !(fl & 1), nan_row = (fl & 2) != 0;
+    const int32_t g = g0 + tid;
+    if (VEC && g0 + kTopkBlock * kTopkUB <= g_full)
+      topk_groups<DT, true>(ra, oa, g, kTopkUB, G, V, g_full, c0, m, ls, Gs, nan_row, zero_row, s_col, s_g, cnt);
+    else
+      topk_groups<DT, false>(ra, oa, g, kTopkUB, G, V, g_full, c0, m, ls, Gs, nan_row, zero_row, s_col, s_g, cnt);
+    __syncthreads();  // LDS is reused by the next tile
+  }
+}
+
+int32_t topk_tiles_per_row(int64_t V) {
+  const int64_t G = (V + 7) / 8;
+  return (int32_t)((G + kTopkBlock * kTopkUB - 1) / (kTopkBlock * kTopkUB));
+}
+
+hipError_t launch_topk_gather(const TopkArgs& p, int dtype, hipStream_t stream) {
+  const int64_t blocks = grid_cap((p.N * p.K + 255) / 256);
+  if (dtype == kBF16) hipLaunchKernelGGL((topk_gather_kernel<kBF16>), dim3((uint32_t)blocks), dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((topk_gather_kernel<kF32>), dim3((uint32_t)blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_bwd(const TopkArgs& p, int dtype, bool vec, hipStream_t stream) {
+  const int64_t blocks = grid_cap(p.N * p.tiles_per_row);
+  const dim3 grid((uint32_t)blocks), block(kTopkBlock);
+  if (dtype == kBF16) {
+    if (vec) hipLaunchKernelGGL((topk_bwd_kernel<kBF16, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((topk_bwd_kernel<kBF16, false>), grid, block, 0, stream, p);
+  } else {
+    if (vec) hipLaunchKernelGGL((topk_bwd_kernel<kF32, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((topk_bwd_kernel<kF32, false>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace vws

@@ -28,6 +28,21 @@ class _Logprobs(torch.autograd.Function):
         return dz, None, None, None
 
 
+class _LogprobsTopk(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, z, ids, ignore_index, split_hint):
+        logp, stats = B.logprobs_topk_fwd(z, ids, ignore_index, split_hint)
+        ctx.save_for_backward(z, ids, stats)
+        ctx.ignore_index = ignore_index
+        return logp
+
+    @staticmethod
+    def backward(ctx, g):
+        z, ids, stats = ctx.saved_tensors
+        dz = B.logprobs_topk_bwd(z, ids, stats, g, ctx.ignore_index) if ctx.needs_input_grad[0] else None
+        return dz, None, None, None
+
+
 class _Entropy(torch.autograd.Function):
     @staticmethod
     def forward(ctx, z, split_hint):
@@ -82,7 +97,14 @@ def linear_logp(h, W, t, ignore_index=-100):
 
 
 def logprobs(z, t, ignore_index=-100, split_hint=0):
-    """Per-token log p_t; ``t == ignore_index`` gives 0 and no gradient."""
+    """Per-token log p_t; ``t == ignore_index`` gives 0 and no gradient.
+
+    ``t`` shaped like the logits without the last dim gives one value per row;
+    ``t`` with an extra trailing dim K (top-k ids) gives [..., K] values, and the
+    gradient adds the upstream gradients of duplicate ids.
+    """
+    if t.dim() == z.dim():
+        return _LogprobsTopk.apply(z, t, ignore_index, split_hint)
     return _Logprobs.apply(z, t, ignore_index, split_hint)
 
 
