@@ -18,6 +18,9 @@ linear logp Triton"):
   ``single_read_identities`` as a self-check, never as the answer.
 * ``topk``        -- multi-id (top-k) log-probabilities: K ids per row, ignored
   slots, duplicate ids whose upstream gradients add (the PR #8838 test list).
+* ``jsd``         -- the generalized Jensen-Shannon divergence of the JSD pull
+  request pasted into PR #8838 (mixture weight beta on the teacher; beta = 0
+  and 1 are the forward and reverse KL branches), with gradients to both inputs.
 * ``linear_logp`` -- the fused linear-logp variant of RL-Kernel PR #208
   (PR body, "Implementation"): logits z = h W^T in float64, then the same
   log-probability and its gradients dh, dW by the chain rule.
@@ -31,4 +34,4 @@ digits with mpmath, torch.log_softmax and autograd in float64, closed forms,
 identities, finite differences and the extreme-range cases the pages describe).
 """
 
-from . import reductions, topk, linear_logp, compare  # noqa: F401
+from . import reductions, topk, jsd, linear_logp, compare  # noqa: F401
