@@ -22,7 +22,11 @@ does not print them), with K_S = KL(S || M) and K_T = KL(T || M):
     dJSD/ds_k = (1 - beta) p^S_k ((log p^S_k - log M_k) - K_S)
     dJSD/dt_k = beta       p^T_k ((log p^T_k - log M_k) - K_T)
 
-Entries equal to -inf have probability 0, add nothing and get gradient 0.
+Entries equal to -inf have probability 0, add nothing and get gradient 0; so
+does any term whose probability is exactly 0 in float64 (an underflow, as for
+a row spanning -3e38..3e38), by the zero-weight rule of the "0 x inf" review
+thread and its fix commit on PR #8838 (a weighted contribution whose weight is
+zero is masked, never 0 x inf).
 A row where either input is undefined (NaN, +inf, or no entry above -inf)
 gives NaN and NaN gradients. Disjoint supports are finite in the interior
 (the page tests "disjoint support").
@@ -48,8 +52,8 @@ def _interior(s, t, beta):
         ps, pt = np.exp(ls), np.exp(lt)
         M = (1.0 - beta) * ps + beta * pt
         lm = np.log(M)
-        Ks = np.sum(np.where(live_s, ps * (ls - lm), 0.0), axis=1)
-        Kt = np.sum(np.where(live_t, pt * (lt - lm), 0.0), axis=1)
+        Ks = np.sum(np.where(ps > 0, ps * (ls - lm), 0.0), axis=1)
+        Kt = np.sum(np.where(pt > 0, pt * (lt - lm), 0.0), axis=1)
     bad = ~row_defined(s) | ~row_defined(t)
     return ps, pt, ls, lt, lm, live_s, live_t, Ks, Kt, bad
 
@@ -82,8 +86,8 @@ def jsd_bwd(s, t, g, beta):
         return kl_bwd(s, t, g)
     ps, pt, ls, lt, lm, live_s, live_t, Ks, Kt, bad = _interior(s, t, beta)
     with np.errstate(**_ERR):
-        ds = np.where(live_s, g[:, None] * (1.0 - beta) * ps * ((ls - lm) - Ks[:, None]), 0.0)
-        dt = np.where(live_t, g[:, None] * beta * pt * ((lt - lm) - Kt[:, None]), 0.0)
+        ds = np.where(ps > 0, g[:, None] * (1.0 - beta) * ps * ((ls - lm) - Ks[:, None]), 0.0)
+        dt = np.where(pt > 0, g[:, None] * beta * pt * ((lt - lm) - Kt[:, None]), 0.0)
     ds[bad] = np.nan
     dt[bad] = np.nan
     return ds, dt
@@ -105,8 +109,8 @@ def cond_jsd_fwd(s, t, beta):
     _, ms, lss = log_softmax_rows(s)
     _, mt, lst = log_softmax_rows(t)
     with np.errstate(**_ERR):
-        ws = np.where(live_s, ps * (np.abs(ls) + np.abs(lm) + np.abs(s - ms[:, None])), 0.0)
-        wt = np.where(live_t, pt * (np.abs(lt) + np.abs(lm) + np.abs(t - mt[:, None])), 0.0)
+        ws = np.where(ps > 0, ps * (np.abs(ls) + np.abs(lm) + np.abs(s - ms[:, None])), 0.0)
+        wt = np.where(pt > 0, pt * (np.abs(lt) + np.abs(lm) + np.abs(t - mt[:, None])), 0.0)
         return np.sum(ws, axis=1) + np.sum(wt, axis=1) + np.abs(lss) + np.abs(lst)
 
 
@@ -129,13 +133,14 @@ def cond_jsd_bwd(s, t, g, beta):
     _, mt, lst = log_softmax_rows(t)
     with np.errstate(**_ERR):
         base = 1.0 + np.abs(lm)
-        cs = np.where(live_s, (1.0 - beta) * ps * (base + np.abs(s - ms[:, None]) + np.abs(lss)[:, None]
+        cs = np.where(ps > 0, (1.0 - beta) * ps * (base + np.abs(s - ms[:, None]) + np.abs(lss)[:, None]
                                                    + np.abs(Ks)[:, None]), 0.0)
-        ct = np.where(live_t, beta * pt * (base + np.abs(t - mt[:, None]) + np.abs(lst)[:, None]
+        ct = np.where(pt > 0, beta * pt * (base + np.abs(t - mt[:, None]) + np.abs(lst)[:, None]
                                            + np.abs(Kt)[:, None]), 0.0)
         # M mixes both inputs: each gradient also carries the other side's share of log M
-        both = live_s & live_t
+        both = (ps > 0) & live_t
         cs = cs + np.where(both, (1.0 - beta) * ps * (np.abs(t - mt[:, None]) + np.abs(lst)[:, None]), 0.0)
+        both = (pt > 0) & live_s
         ct = ct + np.where(both, beta * pt * (np.abs(s - ms[:, None]) + np.abs(lss)[:, None]), 0.0)
     cs = np.where(np.isnan(cs), 0.0, cs)
     ct = np.where(np.isnan(ct), 0.0, ct)

@@ -172,6 +172,25 @@ def test_small_beta_limits_fix_the_mixture_convention():
     np.testing.assert_allclose(dt / eps, pt - ps, rtol=1e-4, atol=1e-8)  # reverse KL(S||T) gradient
 
 
+def test_extreme_range_rows_have_zero_divergence():
+    """A row spanning -3e38..3e38 is one-hot in float64 too (the other entries underflow):
+    JSD(p, p) = 0 with zero gradients, and against a different one-hot row the binary
+    entropy of beta (disjoint supports), as the zero-weight rule requires."""
+    v = 12
+    s = np.full((2, v), -3e38)
+    s[:, 4] = 3e38
+    t = s.copy()
+    t[1, 4] = -3e38
+    t[1, 9] = 3e38
+    for beta in (0.2, 0.5):
+        out, _ = J.jsd_fwd(s, t, beta)
+        ds, dt = J.jsd_bwd(s, t, np.ones(2), beta)
+        assert out[0] == 0.0 and (ds[0] == 0).all() and (dt[0] == 0).all()
+        hb = -beta * math.log(beta) - (1 - beta) * math.log(1 - beta)
+        assert abs(out[1] - hb) < 1e-15
+        assert np.isfinite(ds).all() and np.isfinite(dt).all()
+
+
 def test_undefined_rows_are_nan():
     s, t = _rows(8)
     s[0, 3] = np.nan
