@@ -78,7 +78,7 @@ typedef enum vws_status {
 
 typedef enum vws_dtype { VWS_F32 = 0, VWS_BF16 = 1 } vws_dtype;
 
-typedef enum vws_op { VWS_OP_LOGPROBS = 0, VWS_OP_ENTROPY = 1, VWS_OP_KL = 2 } vws_op;
+typedef enum vws_op { VWS_OP_LOGPROBS = 0, VWS_OP_ENTROPY = 1, VWS_OP_KL = 2, VWS_OP_JSD = 3 } vws_op;
 
 /*
  * A logical [N, V] matrix of logits whose rows are addressed with up to two
@@ -208,6 +208,41 @@ VWS_API int vws_kl_fwd(const vws_rows* a, const vws_rows* b, float* kl, float* s
  */
 VWS_API int vws_kl_bwd(const vws_rows* a, const vws_rows* b, const float* stats, const float* kl, const float* g,
                        int64_t g_stride, void* da, void* db, void* stream);
+
+/*
+ * Generalized Jensen-Shannon divergence of student S and teacher T (the JSD
+ * pull request pasted into PR #8838: "Changes", "Scope and limitations"), with
+ * the GKD-style mixture M = (1 - beta) p_S + beta p_T:
+ *   JSD = beta KL(T||M) + (1 - beta) KL(S||M)      for 0 < beta < 1,
+ * and, as explicit endpoint branches, beta = 0 gives forward KL(T||S) and
+ * beta = 1 reverse KL(S||T) (the KL entry points with the arguments in that
+ * order). The interior takes two reads of both inputs: the single-read KL
+ * statistics pass for (m, log S) of S and T, then a divergence pass that forms
+ * K_S = KL(S||M) and K_T = KL(T||M). Disjoint supports are finite inside; a row
+ * where either input is undefined gives NaN.
+ *   s, t    logits [N, V] (equal N, V, dtype; strides may differ)
+ *   beta    in [0, 1]
+ *   jsd     out fp32 [N]
+ *   stats   out fp32 [N, 6]; opaque, pass it unchanged to vws_jsd_bwd with the
+ *           same beta (interior: m_S, log S_S, m_T, log S_T, K_S, K_T per row;
+ *           endpoints: the KL statistics, [N, 4] packed at its start)
+ *   ws      workspace of vws_workspace_bytes(VWS_OP_JSD, N, V, split_hint) bytes
+ */
+VWS_API int vws_jsd_fwd(const vws_rows* s, const vws_rows* t, float beta, float* jsd, float* stats, void* ws,
+                        size_t ws_bytes, int split_hint, void* stream);
+
+/*
+ * Gradients of g * JSD (interior, derived from the definition; the page does not
+ * print them):
+ *   ds_j = g (1 - beta) p_S,j ((log p_S,j - log M_j) - K_S)
+ *   dt_j = g beta p_T,j ((log p_T,j - log M_j) - K_T)
+ * 0 where the input is -inf; the endpoints are the KL gradients. ds or dt may be
+ * NULL (a detached teacher, a frozen student).
+ *   stats, jsd   as written by vws_jsd_fwd with the same beta
+ *   ds, dt       out [N, V] contiguous, dtype of the inputs
+ */
+VWS_API int vws_jsd_bwd(const vws_rows* s, const vws_rows* t, float beta, const float* stats, const float* jsd,
+                        const float* g, int64_t g_stride, void* ds, void* dt, void* stream);
 
 /*
  * Fused linear-logp (RL-Kernel PR #208, PR body "Implementation"): the per-row

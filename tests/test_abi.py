@@ -164,3 +164,32 @@ def test_topk_validation(L):
     assert bwd(dz=0) == EINVAL
     assert bwd(dz=0x6001) == ELAYOUT
     assert bwd(stats=0) == EINVAL
+
+
+def test_jsd_validation(L):
+    s, t = _rows(), _rows()
+    f = ctypes.c_float
+
+    def fwd(beta=0.5, jsd=0x2000, stats=0x3000, ws=0x4000, nb=1 << 20, a=None, b=None):
+        return L.vws_jsd_fwd(ctypes.byref(a or s), ctypes.byref(b or t), f(beta), jsd, stats, ws, nb, 0, None)
+
+    assert fwd(beta=-0.1) == EINVAL
+    assert fwd(beta=1.5) == EINVAL
+    assert fwd(beta=float("nan")) == EINVAL
+    assert fwd(b=_rows(dtype=B.VWS_F32)) == EDTYPE
+    assert fwd(b=_rows(V=32, s_outer=32)) == EINVAL
+    assert fwd(jsd=0) == EINVAL
+    assert fwd(stats=0x3002) == ELAYOUT
+    assert fwd(ws=None, nb=0) == EWORKSPACE
+    assert fwd(nb=16) == EWORKSPACE
+    assert fwd(a=_rows(n_outer=0, data=0), b=_rows(n_outer=0, data=0), jsd=0, stats=0, ws=None, nb=0) == 0
+    assert B.workspace_bytes(B.OP_JSD, 8, 100) == 8 * 4 * 4
+    assert B.workspace_bytes(B.OP_JSD, 4, 151936) == 4 * 4 * 4 + 4 * B.split_parts(B.OP_JSD, 4, 151936) * 8 * 4
+    # the endpoints are the KL calls: their argument errors are the KL ones
+    assert fwd(beta=0.0, b=_rows(dtype=B.VWS_F32)) == EDTYPE
+    assert fwd(beta=1.0, jsd=0) == EINVAL
+    bw = L.vws_jsd_bwd
+    assert bw(ctypes.byref(s), ctypes.byref(t), f(0.5), 0x3000, 0x2000, 0x5000, -1, 0x6000, None, None) == EINVAL
+    assert bw(ctypes.byref(s), ctypes.byref(t), f(0.5), 0, 0x2000, 0x5000, 1, 0x6000, None, None) == EINVAL
+    assert bw(ctypes.byref(s), ctypes.byref(t), f(0.5), 0x3000, 0x2000, 0x5000, 1, None, None, None) == 0
+    assert bw(ctypes.byref(s), ctypes.byref(t), f(0.5), 0x3000, 0x2000, 0x5000, 1, 0x6001, None, None) == ELAYOUT

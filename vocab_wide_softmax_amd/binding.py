@@ -20,7 +20,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvws.so")
 
 VWS_F32, VWS_BF16 = 0, 1
-OP_LOGPROBS, OP_ENTROPY, OP_KL = 0, 1, 2
+OP_LOGPROBS, OP_ENTROPY, OP_KL, OP_JSD = 0, 1, 2, 3
 _DTYPES = {torch.float32: VWS_F32, torch.bfloat16: VWS_BF16}
 
 
@@ -76,6 +76,8 @@ def lib():
             "vws_entropy_bwd": (I32, [R, FP, FP, FP, I64, VP, VP]),
             "vws_kl_fwd": (I32, [R, R, FP, FP, VP, SZ, I32, VP]),
             "vws_kl_bwd": (I32, [R, R, FP, FP, FP, I64, VP, VP, VP]),
+            "vws_jsd_fwd": (I32, [R, R, ctypes.c_float, FP, FP, VP, SZ, I32, VP]),
+            "vws_jsd_bwd": (I32, [R, R, ctypes.c_float, FP, FP, FP, I64, VP, VP, VP]),
             "vws_linear_workspace_bytes": (SZ, [I32, I64, I64, I64]),
             "vws_linear_logp_fwd": (I32, [VP, I64, VP, I64, I32, I64, I64, I64, VP, I64, FP, FP, VP, SZ, VP]),
             "vws_linear_logp_bwd": (I32, [VP, I64, VP, I64, I32, I64, I64, I64, VP, I64, FP, FP, I64, VP, VP, VP,
@@ -296,6 +298,29 @@ def kl_bwd(a, b, stats, kl, g, need_a=True, need_b=True):
     _check("vws_kl_bwd", L.vws_kl_bwd(ctypes.byref(ra), ctypes.byref(rb), _ptr(stats), _ptr(kl), _ptr(g), gs,
                                       _ptr(da), _ptr(db), _stream(a.device)))
     return da, db
+
+
+def jsd_fwd(s, t, beta=0.5, split_hint=0):
+    """(JSD fp32 [N...], stats fp32 [N, 6]) of student s and teacher t -- vws_jsd_fwd."""
+    L = lib()
+    out, stats = _outputs(s, 6)
+    ws, nb = _workspace(OP_JSD, s, split_hint)
+    rs, rt = rows(s), rows(t)
+    _check("vws_jsd_fwd", L.vws_jsd_fwd(ctypes.byref(rs), ctypes.byref(rt), float(beta), _ptr(out), _ptr(stats),
+                                        _ptr(ws), nb, split_hint, _stream(s.device)))
+    return out, stats
+
+
+def jsd_bwd(s, t, beta, stats, out, g, need_s=True, need_t=True):
+    """(ds or None, dt or None) -- vws_jsd_bwd."""
+    L = lib()
+    g, gs = _g_arg(g, s)
+    ds = torch.empty(s.shape, dtype=s.dtype, device=s.device) if need_s else None
+    dt = torch.empty(t.shape, dtype=t.dtype, device=t.device) if need_t else None
+    rs, rt = rows(s), rows(t)
+    _check("vws_jsd_bwd", L.vws_jsd_bwd(ctypes.byref(rs), ctypes.byref(rt), float(beta), _ptr(stats), _ptr(out),
+                                        _ptr(g), gs, _ptr(ds), _ptr(dt), _stream(s.device)))
+    return ds, dt
 
 
 # ------------------------------------------------------------- fused linear-logp

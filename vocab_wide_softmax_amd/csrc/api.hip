@@ -211,6 +211,23 @@ vws::TopkArgs topk_args(const vws_rows* z, const vws_ids_k* t, int64_t N, int64_
   return p;
 }
 
+// JSD forward workspace: statistics [N, 4], then the statistics pass's partial states
+// [N, P, 6] and the divergence pass's partial sums [N, P, 2] when P > 1.
+size_t jsd_ws_bytes(int64_t N, int P) {
+  return (size_t)N * 4 * sizeof(float) + (P > 1 ? (size_t)N * (size_t)P * 8 * sizeof(float) : 0);
+}
+
+// Shared checks of the two JSD inputs; *N is the row count.
+int jsd_check_pair(const vws_rows* s, const vws_rows* t, int64_t* N) {
+  int64_t Nt;
+  int rc = check_rows(s, N);
+  if (rc) return rc;
+  if ((rc = check_rows(t, &Nt))) return rc;
+  if (t->dtype != s->dtype) return VWS_EDTYPE;
+  if (Nt != *N || t->V != s->V || t->n_inner != s->n_inner) return VWS_EINVAL;
+  return VWS_OK;
+}
+
 int64_t round_up8(int64_t x) { return (x + 7) / 8 * 8; }
 
 // Workspace layout of the fused linear-logp.
@@ -314,14 +331,15 @@ VWS_API int vws_linear_logp_bwd(const void* h, int64_t ldh, const void* W, int64
 
 
 VWS_API size_t vws_workspace_bytes(int op, int64_t N, int64_t V, int split_hint) {
-  if (op < VWS_OP_LOGPROBS || op > VWS_OP_KL || N < 0 || V < 1 || split_hint < 0) return (size_t)-1;
+  if (op < VWS_OP_LOGPROBS || op > VWS_OP_JSD || N < 0 || V < 1 || split_hint < 0) return (size_t)-1;
   if (N == 0) return 0;
   const int P = parts_for(op, N, V, split_hint);
+  if (op == VWS_OP_JSD) return jsd_ws_bytes(N, P);
   return P > 1 ? (size_t)N * (size_t)P * (size_t)state_floats(op) * sizeof(float) : 0;
 }
 
 VWS_API int vws_split_parts(int op, int64_t N, int64_t V, int split_hint) {
-  if (op < VWS_OP_LOGPROBS || op > VWS_OP_KL || N < 0 || V < 1 || split_hint < 0) return VWS_EINVAL;
+  if (op < VWS_OP_LOGPROBS || op > VWS_OP_JSD || N < 0 || V < 1 || split_hint < 0) return VWS_EINVAL;
   return parts_for(op, N, V, split_hint);
 }
 
@@ -401,6 +419,84 @@ VWS_API int vws_logprobs_topk_bwd(const vws_rows* z, const vws_ids_k* ids, int64
   p.dz = static_cast<char*>(dz);
   const bool vec = rows_vec_ok(z) && out_vec_ok(dz, N, z->V, es);
   hipError_t e = vws::launch_topk_bwd(p, z->dtype, vec, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VWS_OK : VWS_EHIP;
+}
+
+VWS_API int vws_jsd_fwd(const vws_rows* s, const vws_rows* t, float beta, float* jsd, float* stats, void* ws,
+                        size_t ws_bytes, int split_hint, void* stream) {
+  if (!(beta >= 0.0f && beta <= 1.0f)) return VWS_EINVAL;
+  // endpoint branches: forward KL(T||S) and reverse KL(S||T)
+  if (beta == 0.0f) return fwd_common(VWS_OP_KL, t, s, nullptr, 0, jsd, stats, ws, ws_bytes, split_hint, stream);
+  if (beta == 1.0f) return fwd_common(VWS_OP_KL, s, t, nullptr, 0, jsd, stats, ws, ws_bytes, split_hint, stream);
+  int64_t N;
+  int rc = jsd_check_pair(s, t, &N);
+  if (rc) return rc;
+  if (split_hint < 0) return VWS_EINVAL;
+  if (N == 0) return VWS_OK;
+  if (!jsd || !stats) return VWS_EINVAL;
+  if (!aligned(jsd, 4) || !aligned(stats, 4)) return VWS_ELAYOUT;
+  const int P = parts_for(VWS_OP_JSD, N, s->V, split_hint);
+  if (N * (int64_t)P > (int64_t)INT32_MAX) return VWS_EINVAL;
+  if (!ws || ws_bytes < jsd_ws_bytes(N, P)) return VWS_EWORKSPACE;
+  if (!aligned(ws, 4)) return VWS_ELAYOUT;
+  float* st4 = static_cast<float*>(ws);
+  float* part1 = st4 + 4 * N;
+  float* part2 = part1 + (P > 1 ? N * (int64_t)P * 6 : 0);
+  // pass 1: (m, log S) of both inputs in one read (the KL forward, statistics only)
+  rc = fwd_common(VWS_OP_KL, s, t, nullptr, 0, nullptr, st4, part1, P > 1 ? (size_t)N * P * 6 * sizeof(float) : 0,
+                  split_hint, stream, true);
+  if (rc) return rc;
+  // pass 2: K_S and K_T, then JSD = beta K_T + (1 - beta) K_S
+  vws::JsdArgs p{};
+  p.s = rows_dev(s);
+  p.t = rows_dev(t);
+  p.N = N;
+  p.V = s->V;
+  p.beta = beta;
+  p.parts = P;
+  const int64_t G = (s->V + 7) / 8;
+  p.groups_per_part = (int32_t)((G + P - 1) / P);
+  p.st4 = st4;
+  p.ws2 = part2;
+  p.out = jsd;
+  p.stats = stats;
+  const bool vec = rows_vec_ok(s) && rows_vec_ok(t);
+  hipError_t e = vws::launch_jsd_div(p, s->dtype, vec, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VWS_OK : VWS_EHIP;
+}
+
+VWS_API int vws_jsd_bwd(const vws_rows* s, const vws_rows* t, float beta, const float* stats, const float* jsd,
+                        const float* g, int64_t g_stride, void* ds, void* dt, void* stream) {
+  if (!(beta >= 0.0f && beta <= 1.0f)) return VWS_EINVAL;
+  if (beta == 0.0f) return bwd_common(VWS_OP_KL, t, s, nullptr, 0, stats, jsd, g, g_stride, dt, ds, stream);
+  if (beta == 1.0f) return bwd_common(VWS_OP_KL, s, t, nullptr, 0, stats, jsd, g, g_stride, ds, dt, stream);
+  int64_t N;
+  int rc = jsd_check_pair(s, t, &N);
+  if (rc) return rc;
+  if (g_stride < 0) return VWS_EINVAL;
+  if (N == 0) return VWS_OK;
+  if (!stats || !jsd || !g) return VWS_EINVAL;
+  if (!ds && !dt) return VWS_OK;
+  const int es = elem_size(s->dtype);
+  if (!aligned(stats, 4) || !aligned(g, 4) || !aligned(ds, es) || !aligned(dt, es)) return VWS_ELAYOUT;
+  int64_t nv, bytes;
+  if (!mul_ok(N, s->V, &nv) || !mul_ok(nv, es, &bytes)) return VWS_EINVAL;
+  const int32_t tpr = vws::jsd_tiles_per_row(s->V);
+  if (N * (int64_t)tpr > (int64_t)INT32_MAX) return VWS_EINVAL;
+  vws::JsdArgs p{};
+  p.s = rows_dev(s);
+  p.t = rows_dev(t);
+  p.N = N;
+  p.V = s->V;
+  p.beta = beta;
+  p.tiles_per_row = tpr;
+  p.stats = const_cast<float*>(stats);
+  p.g = g;
+  p.g_stride = g_stride;
+  p.ds = static_cast<char*>(ds);
+  p.dt = static_cast<char*>(dt);
+  const bool vec = rows_vec_ok(s) && rows_vec_ok(t) && out_vec_ok(ds, N, s->V, es) && out_vec_ok(dt, N, s->V, es);
+  hipError_t e = vws::launch_jsd_bwd(p, s->dtype, vec, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? VWS_OK : VWS_EHIP;
 }
 

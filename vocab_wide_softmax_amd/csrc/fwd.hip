@@ -136,6 +136,7 @@ __device__ __forceinline__ void finalize_kl(const FwdArgs& p, int64_t row, const
   p.stats[4 * row + 1] = (float)lsa;
   p.stats[4 * row + 2] = st.mb;
   p.stats[4 * row + 3] = (float)lsb;
+  if (p.out == nullptr) return;  // statistics only (the JSD statistics pass)
   float out;
   if (!(st.Sa > 0.0f) || st.Sb != st.Sb) {  // A has no live entry, or a NaN / +inf reached S
     out = __builtin_nanf("");

@@ -1,0 +1,273 @@
+// jsd.hip -- generalized Jensen-Shannon divergence, 0 < beta < 1.
+//
+// The JSD pull request pasted into DeepSpeed PR #8838 ("Changes", "Scope and
+// limitations") adds jsd(student, teacher, beta): fp32 per token, gradients to
+// both inputs, beta = 0 and beta = 1 as explicit forward / reverse KL branches
+// (handled by the host through the KL kernels), and for the interior a
+// statistics pass followed by a divergence pass, because the nonlinear mixture
+// needs the global normalisation first. With S = student, T = teacher and the
+// mixture M = (1 - beta) p_S + beta p_T (mixture weight beta on the teacher, as
+// in GKD-style distillation):
+//
+//   K_S = sum p_S (log p_S - log M),   K_T = sum p_T (log p_T - log M)
+//   JSD = beta K_T + (1 - beta) K_S                 (the two KL-to-mixture sums)
+//   dJSD/ds_j = (1 - beta) p_S,j ((log p_S,j - log M_j) - K_S)
+//   dJSD/dt_j = beta p_T,j ((log p_T,j - log M_j) - K_T)
+//
+// Pass 1 is the KL forward's single read of both inputs, kept for its
+// statistics (m, log S) of S and T. Pass 2 (jsd_div_kernel) reads both again and
+// accumulates K_S and K_T; with P > 1 vocabulary parts per row the partial sums
+// are added in part order by jsd_combine_kernel. The backward recomputes p_S,
+// p_T and log M in registers from the saved (m, log S, K_S, K_T) and writes
+// contiguous gradients. Masked (-inf) entries have zero weight (the zero-weight
+// product); rows where either input is undefined give NaN.
+#include "device.h"
+#include "launch.h"
+
+namespace vws {
+
+namespace {
+constexpr int kJsdBlock = 256;
+constexpr int kJsdU = 2;   // forward groups per lane per batch
+constexpr int kJsdUB = 2;  // backward groups per lane per tile
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kFltMin = 1.17549435e-38f;
+}  // namespace
+
+// Per-row constants: (m, log S) of both inputs, beta and 1 - beta.
+struct JsdRow {
+  float ms, lss, mt, lst;
+  float wt, ws;
+  bool bad;
+};
+
+__device__ __forceinline__ JsdRow jsd_row(const float* st4, float beta) {
+  JsdRow r;
+  r.ms = st4[0];
+  r.lss = st4[1];
+  r.mt = st4[2];
+  r.lst = st4[3];
+  r.wt = beta;
+  r.ws = 1.0f - beta;
+  // a defined row has a finite max and a finite log S >= 0; an all -inf row has
+  // m = -inf, a NaN or +inf entry gives m = +inf or S = NaN
+  r.bad = !(__builtin_isfinite(r.ms) && __builtin_isfinite(r.lss) && __builtin_isfinite(r.mt) &&
+            __builtin_isfinite(r.lst));
+  return r;
+}
+
+// log p_S, log p_T, p_S, p_T and log M of one column.
+__device__ __forceinline__ void jsd_point(const JsdRow& r, float xs, float xt, float& ls, float& lt, float& ps,
+                                          float& pt, float& lm) {
+  ls = (xs - r.ms) - r.lss;
+  lt = (xt - r.mt) - r.lst;
+  ps = expf_fast(ls);
+  pt = expf_fast(lt);
+  const float mix = __builtin_fmaf(r.wt, pt, r.ws * ps);
+  if (mix >= kFltMin) {
+    lm = __builtin_amdgcn_logf(mix) * kLn2;
+  } else {
+    // both probabilities tiny or zero: log M = max(ls, lt) + log((1-b) e^(ls-mx) + b e^(lt-mx)),
+    // whose argument lies in [min(b, 1-b), 1]; NaN when both entries are masked (zero weight)
+    const float mx = fmaxf(ls, lt);
+    const float inner = __builtin_fmaf(r.wt, expf_fast(lt - mx), r.ws * expf_fast(ls - mx));
+    lm = mx + __builtin_amdgcn_logf(inner) * kLn2;
+  }
+}
+
+// ---- pass 2: the two KL-to-mixture sums ------------------------------------------------
+
+// Writes the row's outputs: JSD, and stats (m_s, log S_s, m_t, log S_t, K_S, K_T).
+__device__ void jsd_finalize(const JsdArgs& p, int64_t row, float Ks, float Kt) {
+  const float* st4 = p.st4 + 4 * row;
+  float* o = p.stats + 6 * row;
+  const JsdRow r = jsd_row(st4, p.beta);
+  o[0] = r.ms;
+  o[1] = r.lss;
+  o[2] = r.mt;
+  o[3] = r.lst;
+  const float qnan = __builtin_nanf("");
+  o[4] = r.bad ? qnan : Ks;
+  o[5] = r.bad ? qnan : Kt;
+  p.out[row] = r.bad ? qnan : (float)((double)p.beta * (double)Kt + (1.0 - (double)p.beta) * (double)Ks);
+}
+
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kJsdBlock) void jsd_div_kernel(JsdArgs p) {
+  constexpr int NW = kJsdBlock / 64;
+  constexpr int U = kJsdU;
+  __shared__ float red[2][NW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t parts = p.parts;
+  const int64_t total = p.N * parts;
+  const int32_t G = (int32_t)((p.V + 7) / 8);
+  const int32_t g_full = VEC ? (int32_t)(p.V / 8) : 0;
+  const int32_t V = (int32_t)p.V;
+  for (int64_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
+    const int64_t row = vb / parts;
+    const int32_t part = (int32_t)(vb - row * parts);
+    const int32_t g0 = part * p.groups_per_part;
+    const int32_t g1 = min(G, g0 + p.groups_per_part);
+    const JsdRow r = jsd_row(p.st4 + 4 * row, p.beta);
+    const char* rs = row_ptr<DT>(p.s, row);
+    const char* rt = row_ptr<DT>(p.t, row);
+    float Ks = 0.0f, Kt = 0.0f;
+    for (int32_t gb = g0 + tid; gb < g1; gb += kJsdBlock * U) {
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int32_t g = gb + k * kJsdBlock;
+        if (g < g1) {
+          float xs[8], xt[8];
+          load_group<DT, VEC>(rs, g, V, g_full, xs);
+          load_group<DT, VEC>(rt, g, V, g_full, xt);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            float ls, lt, ps, pt, lm;
+            jsd_point(r, xs[j], xt[j], ls, lt, ps, pt, lm);
+            Ks += mul0(ps, ls - lm);
+            Kt += mul0(pt, lt - lm);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      Ks += __shfl_xor(Ks, off, 64);
+      Kt += __shfl_xor(Kt, off, 64);
+    }
+    if (lane == 0) {
+      red[0][wave] = Ks;
+      red[1][wave] = Kt;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float s = red[0][0], t = red[1][0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        s += red[0][w];
+        t += red[1][w];
+      }
+      if (parts == 1) {
+        jsd_finalize(p, row, s, t);
+      } else {
+        p.ws2[2 * vb] = s;
+        p.ws2[2 * vb + 1] = t;
+      }
+    }
+    __syncthreads();  // red[] is reused by the next row
+  }
+}
+
+// One thread per row: add the parts' sums in part order, then finalize.
+__global__ __launch_bounds__(256) void jsd_combine_kernel(JsdArgs p) {
+  for (int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x; row < p.N; row += (int64_t)gridDim.x * 256) {
+    const float* w = p.ws2 + 2 * row * p.parts;
+    float Ks = 0.0f, Kt = 0.0f;
+    for (int i = 0; i < p.parts; ++i) {
+      Ks += w[2 * i];
+      Kt += w[2 * i + 1];
+    }
+    jsd_finalize(p, row, Ks, Kt);
+  }
+}
+
+// ---- backward ---------------------------------------------------------------------------
+
+template <int DT, bool FULL>
+__device__ __forceinline__ void jsd_bwd_groups(const JsdRow& r, float Ks, float Kt, float gs, float gt,
+                                               const char* rs, const char* rt, char* os, char* ot, int32_t g,
+                                               int n, int32_t G, int32_t V, int32_t g_full) {
+  const float qnan = __builtin_nanf("");
+  for (int u = 0; u < n; ++u, g += kJsdBlock) {
+    if (!FULL && g >= G) break;
+    float xs[8], xt[8], ys[8], yt[8];
+    if (FULL) {
+      load_group_vec<DT>(rs, g, xs);
+      load_group_vec<DT>(rt, g, xt);
+    } else {
+      load_group<DT, true>(rs, g, V, g_full, xs);
+      load_group<DT, true>(rt, g, V, g_full, xt);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float ls, lt, ps, pt, lm;
+      jsd_point(r, xs[j], xt[j], ls, lt, ps, pt, lm);
+      ys[j] = r.bad ? qnan : mul0(ps, (ls - lm) - Ks) * gs;
+      yt[j] = r.bad ? qnan : mul0(pt, (lt - lm) - Kt) * gt;
+    }
+    if (FULL) {
+      if (os) store_group_vec<DT>(os, g, ys);
+      if (ot) store_group_vec<DT>(ot, g, yt);
+    } else {
+      if (os) store_group<DT, true>(os, g, V, g_full, ys);
+      if (ot) store_group<DT, true>(ot, g, V, g_full, yt);
+    }
+  }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kJsdBlock) void jsd_bwd_kernel(JsdArgs p) {
+  constexpr int ES = ElemSize<DT>::value;
+  const int32_t tpr = p.tiles_per_row;
+  const int64_t total = p.N * tpr;
+  const int32_t V = (int32_t)p.V;
+  const int32_t G = (V + 7) / 8;
+  const int32_t g_full = VEC ? V / 8 : 0;
+  for (int64_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
+    const int64_t row = vb / tpr;
+    const int32_t tile = (int32_t)(vb - row * tpr);
+    const int32_t g0 = tile * (kJsdBlock * kJsdUB);
+    const float* st = p.stats + 6 * row;
+    JsdRow r = jsd_row(st, p.beta);
+    const float Ks = st[4], Kt = st[5];
+    r.bad = r.bad || !(Ks == Ks) || !(Kt == Kt);
+    const float gv = p.g[row * p.g_stride];
+    const float gs = gv * r.ws, gt = gv * r.wt;
+    const char* rs = row_ptr<DT>(p.s, row);
+    const char* rt = row_ptr<DT>(p.t, row);
+    char* os = p.ds ? p.ds + row * (int64_t)V * ES : nullptr;
+    char* ot = p.dt ? p.dt + row * (int64_t)V * ES : nullptr;
+    const int32_t g = g0 + threadIdx.x;
+    if (VEC && g0 + kJsdBlock * kJsdUB <= g_full)
+      jsd_bwd_groups<DT, true>(r, Ks, Kt, gs, gt, rs, rt, os, ot, g, kJsdUB, G, V, g_full);
+    else
+      jsd_bwd_groups<DT, false>(r, Ks, Kt, gs, gt, rs, rt, os, ot, g, kJsdUB, G, V, g_full);
+  }
+}
+
+// ---- host-side launch -------------------------------------------------------------------
+
+int32_t jsd_tiles_per_row(int64_t V) {
+  const int64_t G = (V + 7) / 8;
+  return (int32_t)((G + kJsdBlock * kJsdUB - 1) / (kJsdBlock * kJsdUB));
+}
+
+hipError_t launch_jsd_div(const JsdArgs& p, int dtype, bool vec, hipStream_t stream) {
+  const dim3 grid((uint32_t)grid_cap(p.N * p.parts)), block(kJsdBlock);
+  if (dtype == kBF16) {
+    if (vec) hipLaunchKernelGGL((jsd_div_kernel<kBF16, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((jsd_div_kernel<kBF16, false>), grid, block, 0, stream, p);
+  } else {
+    if (vec) hipLaunchKernelGGL((jsd_div_kernel<kF32, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((jsd_div_kernel<kF32, false>), grid, block, 0, stream, p);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.parts == 1) return e;
+  hipLaunchKernelGGL(jsd_combine_kernel, dim3((uint32_t)grid_cap((p.N + 255) / 256)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_jsd_bwd(const JsdArgs& p, int dtype, bool vec, hipStream_t stream) {
+  const dim3 grid((uint32_t)grid_cap(p.N * p.tiles_per_row)), block(kJsdBlock);
+  if (dtype == kBF16) {
+    if (vec) hipLaunchKernelGGL((jsd_bwd_kernel<kBF16, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((jsd_bwd_kernel<kBF16, false>), grid, block, 0, stream, p);
+  } else {
+    if (vec) hipLaunchKernelGGL((jsd_bwd_kernel<kF32, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((jsd_bwd_kernel<kF32, false>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace vws

@@ -54,6 +54,26 @@ int32_t topk_tiles_per_row(int64_t V);
 hipError_t launch_topk_gather(const TopkArgs& p, int dtype, hipStream_t stream);
 hipError_t launch_topk_bwd(const TopkArgs& p, int dtype, bool vec, hipStream_t stream);
 
+// Generalized JSD (0 < beta < 1) of student s and teacher t.
+struct JsdArgs {
+  RowsDev s, t;
+  int64_t N, V;
+  float beta;
+  int32_t parts, groups_per_part, tiles_per_row;
+  const float* st4;  // [N, 4] (m_s, log S_s, m_t, log S_t) from the statistics pass (forward)
+  float* ws2;        // [N, parts, 2] partial (K_S, K_T) when parts > 1
+  float* out;        // [N] JSD
+  float* stats;      // [N, 6] (m_s, log S_s, m_t, log S_t, K_S, K_T); read by the backward
+  const float* g;
+  int64_t g_stride;
+  char* ds;  // [N, V] contiguous, may be null
+  char* dt;  // [N, V] contiguous, may be null
+};
+
+int32_t jsd_tiles_per_row(int64_t V);
+hipError_t launch_jsd_div(const JsdArgs& p, int dtype, bool vec, hipStream_t stream);
+hipError_t launch_jsd_bwd(const JsdArgs& p, int dtype, bool vec, hipStream_t stream);
+
 // Fused linear-logp: h [N, H] and W [V, H] bf16 (row strides ldh, ldw), targets t [N].
 struct LinArgs {
   const uint16_t* h;

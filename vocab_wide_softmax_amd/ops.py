@@ -73,6 +73,24 @@ class _KL(torch.autograd.Function):
         return da, db, None
 
 
+class _JSD(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, s, t, beta, split_hint):
+        out, stats = B.jsd_fwd(s, t, beta, split_hint)
+        ctx.save_for_backward(s, t, stats, out)
+        ctx.beta = beta
+        return out
+
+    @staticmethod
+    def backward(ctx, g):
+        s, t, stats, out = ctx.saved_tensors
+        ns, nt = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        if not (ns or nt):
+            return None, None, None, None
+        ds, dt = B.jsd_bwd(s, t, ctx.beta, stats, out, g, need_s=ns, need_t=nt)
+        return ds, dt, None, None
+
+
 class _LinearLogp(torch.autograd.Function):
     @staticmethod
     def forward(ctx, h, W, t, ignore_index):
@@ -116,3 +134,9 @@ def entropy(z, split_hint=0):
 def kl(a, b, split_hint=0):
     """Per-token KL(A||B) = sum p_A (log p_A - log p_B); +inf where B masks A's support."""
     return _KL.apply(a, b, split_hint)
+
+
+def jsd(student, teacher, beta=0.5, split_hint=0):
+    """Per-token generalized JSD with mixture M = (1 - beta) p_S + beta p_T:
+    beta KL(T||M) + (1 - beta) KL(S||M); beta = 0 is KL(T||S), beta = 1 is KL(S||T)."""
+    return _JSD.apply(student, teacher, float(beta), split_hint)
