@@ -76,7 +76,9 @@ typedef enum vws_status {
   VWS_EHIP = -5        /* a HIP launch failed */
 } vws_status;
 
-typedef enum vws_dtype { VWS_F32 = 0, VWS_BF16 = 1 } vws_dtype;
+typedef enum vws_dtype { VWS_F32 = 0, VWS_BF16 = 1, VWS_F16 = 2 } vws_dtype;
+
+enum { VWS_SPLIT_INVARIANT = -1 };
 
 typedef enum vws_op { VWS_OP_LOGPROBS = 0, VWS_OP_ENTROPY = 1, VWS_OP_KL = 2, VWS_OP_JSD = 3 } vws_op;
 
@@ -118,8 +120,14 @@ typedef struct vws_ids_k {
  * given split_hint. The forward splits each row's vocabulary over P workgroups
  * when N is small (the pages' cross-shard combine -- MAX of m, re-centring of
  * S and W on it, SUM -- done inside one GPU); the partial statistics go to
- * the workspace and a second kernel merges them. split_hint: 0 = automatic,
- * 1 = never split, P > 1 = split into P parts (capped at ceil(V/8)).
+ * the workspace and a second kernel merges them. split_hint:
+ *   0 = automatic (P grows as N shrinks; a row's rounding may then depend on N),
+ *   1 = never split, P > 1 = split into P parts (capped at ceil(V/8)),
+ *   VWS_SPLIT_INVARIANT (-1) = fixed segments of 32768 columns, so P and every
+ *       row's reduction order depend on V alone: a row's outputs are bitwise
+ *       the same whatever the batch it is in (the batch-invariance remark on
+ *       PR #8838). Any fixed split_hint >= 1 is batch invariant too; the
+ *       backward passes are per element and never depend on the batch.
  * Returns 0 when no workspace is needed, (size_t)-1 for invalid arguments.
  */
 VWS_API size_t vws_workspace_bytes(int op, int64_t N, int64_t V, int split_hint);

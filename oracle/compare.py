@@ -11,6 +11,8 @@ Tolerances (stated for this path; the pages report errors, not a rule):
     |x - y| <= ulp_bf16(rne(y)) + 64 eps32 c             (conditioned),
   with rne the round-to-nearest-even of y to bf16 (the bf16 gradient is the
   RNE of the fp32 value, as the review comment of PR #8838 observes).
+* fp16 outputs pass by the bf16 rule with fp16 rounding and spacing
+    (|x - rne16(y)| <= ulp_f16(rne16(y)), or the conditioned form).
 * NaN positions must match exactly, and so must +inf / -inf positions.
 
 The conditioned branch exists because a purely relative bound cannot be met
@@ -24,7 +26,7 @@ EPS32 = 2.0 ** -23
 REL32 = 2e-5
 COND = 64.0 * EPS32
 
-__all__ = ["EPS32", "bf16_rne", "ulp_bf16", "check", "bf16_bits_to_f64", "f64_to_bf16_bits"]
+__all__ = ["EPS32", "bf16_rne", "ulp_bf16", "f16_rne", "ulp_f16", "check", "bf16_bits_to_f64", "f64_to_bf16_bits"]
 
 
 def bf16_rne(y):
@@ -55,6 +57,34 @@ def ulp_bf16(v):
     return 2.0 ** (e - 7)
 
 
+def f16_rne(y):
+    """Round float64 values to the nearest IEEE half value, ties to even; beyond the largest
+    half (65504) values that round up to 2^16 become inf."""
+    y = np.asarray(y, dtype=np.float64)
+    out = np.array(y, dtype=np.float64, copy=True)
+    fin = np.isfinite(y) & (y != 0)
+    a = np.abs(y[fin])
+    e = np.floor(np.log2(a))
+    e = np.where(2.0 ** e > a, e - 1, e)
+    e = np.where(2.0 ** (e + 1) <= a, e + 1, e)
+    e = np.maximum(e, -14.0)  # subnormal halves share the spacing 2^-24
+    ulp = 2.0 ** (e - 10)
+    r = np.rint(a / ulp) * ulp
+    r = np.where(r > 65504.0, np.inf, r)
+    out[fin] = np.sign(y[fin]) * r
+    return out
+
+
+def ulp_f16(v):
+    """Spacing of half values at |v| (v a half value or 0)."""
+    v = np.abs(np.asarray(v, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(v > 0, v, 1.0)))
+    e = np.where(v > 0, e, -14.0)
+    e = np.maximum(e, -14.0)
+    return 2.0 ** (e - 10)
+
+
 def bf16_bits_to_f64(bits):
     """uint16 bf16 bit patterns -> float64 values (exact)."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
@@ -73,7 +103,7 @@ def f64_to_bf16_bits(x):
 def check(x, y, c, kind, factor=None):
     """Compare device values x with oracle values y under the rule above.
 
-    kind is "f32" or "bf16". ``factor`` replaces 64 eps32 in the conditioned
+    kind is "f32", "bf16" or "f16". ``factor`` replaces 64 eps32 in the conditioned
     bound where the computation rounds an operand more coarsely (the fused
     linear-logp backward feeds dz to its contractions in bf16: each term then
     carries up to 2^-9 relative error, so its rule uses factor 2^-8).
@@ -100,9 +130,9 @@ def check(x, y, c, kind, factor=None):
         strict_ok = err <= strict
         ok = strict_ok | (err <= cond)
         allow = np.maximum(strict, cond)
-    elif kind == "bf16":
-        r = bf16_rne(yf)
-        u = ulp_bf16(r)
+    elif kind in ("bf16", "f16"):
+        r = bf16_rne(yf) if kind == "bf16" else f16_rne(yf)
+        u = ulp_bf16(r) if kind == "bf16" else ulp_f16(np.where(np.isfinite(r), r, 65504.0))
         strict_ok = np.abs(xf - r) <= u
         cond = u + cfac * cf
         ok = strict_ok | (np.abs(xf - yf) <= cond)

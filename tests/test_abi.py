@@ -79,7 +79,7 @@ def test_forward_validation(L):
     assert _ent(L, _rows(), out=0) == EINVAL
     assert _ent(L, _rows(), stats=0) == EINVAL
     assert _ent(L, _rows(), out=0x2002) == ELAYOUT
-    assert _ent(L, _rows(), hint=-1) == EINVAL
+    assert _ent(L, _rows(), hint=-2) == EINVAL
     assert _ent(L, _rows(s_outer=2 ** 62, n_outer=8)) == ELAYOUT  # address overflow
     # empty batch: no-op, even with null pointers
     assert _ent(L, _rows(n_outer=0, data=0), out=0, stats=0) == 0
@@ -193,3 +193,13 @@ def test_jsd_validation(L):
     assert bw(ctypes.byref(s), ctypes.byref(t), f(0.5), 0, 0x2000, 0x5000, 1, 0x6000, None, None) == EINVAL
     assert bw(ctypes.byref(s), ctypes.byref(t), f(0.5), 0x3000, 0x2000, 0x5000, 1, None, None, None) == 0
     assert bw(ctypes.byref(s), ctypes.byref(t), f(0.5), 0x3000, 0x2000, 0x5000, 1, 0x6001, None, None) == ELAYOUT
+
+
+def test_batch_invariant_split_depends_on_v_only(L):
+    for V, want in ((1024, 1), (32768, 1), (32769, 2), (75968, 3), (151936, 5)):
+        got = {B.split_parts(op, n, V, B.SPLIT_INVARIANT) for op in (0, 1, 2, 3) for n in (1, 7, 64, 1024, 8192)}
+        assert got == {want}, (V, got)
+    # the automatic choice does depend on N (that is what the invariant mode avoids)
+    assert B.split_parts(0, 64, 75968) != B.split_parts(0, 8192, 75968)
+    assert B.workspace_bytes(2, 8192, 75968, B.SPLIT_INVARIANT) == 8192 * 3 * 6 * 4
+    assert L.vws_split_parts(0, 8, 100, -2) < 0

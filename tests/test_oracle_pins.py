@@ -321,6 +321,23 @@ def test_bf16_rne_matches_torch_cast():
     assert compare.bf16_rne(np.array([1 + 3 * 2 ** -8]))[0] == 1 + 2 ** -6
 
 
+def test_f16_rne_matches_torch_and_numpy_casts():
+    rng = np.random.default_rng(32)
+    x = np.concatenate([rng.normal(0, 1, 10000), rng.normal(0, 3e4, 200), rng.normal(0, 1e-6, 200),
+                        rng.normal(0, 1e-9, 50), [1 + 2 ** -11, 1 + 3 * 2 ** -11, 65504.0, 65519.0, 65520.0,
+                                                  2 ** -25, 3 * 2 ** -26, 0.0]])
+    mine = compare.f16_rne(x)
+    ref_np = x.astype(np.float16).astype(np.float64)
+    ref_torch = torch.from_numpy(x.astype(np.float32)).to(torch.float16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(mine, ref_np)
+    exact32 = x.astype(np.float32).astype(np.float64) == x  # values a float32 holds exactly: no double rounding
+    np.testing.assert_array_equal(mine[exact32], ref_torch[exact32])
+    assert compare.f16_rne(np.array([1 + 2 ** -11]))[0] == 1.0  # tie to even
+    assert compare.f16_rne(np.array([65520.0]))[0] == np.inf
+    assert compare.ulp_f16(np.array([1.0, 2 ** -20, 0.0]))[0] == 2 ** -10
+    assert compare.ulp_f16(np.array([2 ** -20]))[0] == 2 ** -24
+
+
 def test_check_accepts_exact_and_rejects_planted_errors():
     y = np.array([1.0, -2.5, 1e-3, np.inf, np.nan])
     c = np.abs(y)

@@ -19,9 +19,10 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvws.so")
 
-VWS_F32, VWS_BF16 = 0, 1
+VWS_F32, VWS_BF16, VWS_F16 = 0, 1, 2
 OP_LOGPROBS, OP_ENTROPY, OP_KL, OP_JSD = 0, 1, 2, 3
-_DTYPES = {torch.float32: VWS_F32, torch.bfloat16: VWS_BF16}
+SPLIT_INVARIANT = -1  # fixed V-only vocabulary segments: results independent of the batch
+_DTYPES = {torch.float32: VWS_F32, torch.bfloat16: VWS_BF16, torch.float16: VWS_F16}
 
 
 class VwsError(RuntimeError):
@@ -113,7 +114,7 @@ def _stream(dev):
 def rows(t: torch.Tensor) -> vws_rows:
     """Descriptor of a [N, V] or [B, S, V] logits tensor (last dim contiguous)."""
     if t.dtype not in _DTYPES:
-        raise TypeError("logits must be float32 or bfloat16, got %s" % t.dtype)
+        raise TypeError("logits must be float32, bfloat16 or float16, got %s" % t.dtype)
     if t.dim() == 2:
         n_outer, n_inner, s_outer, s_inner = t.shape[0], 1, t.stride(0), 0
     elif t.dim() == 3:

@@ -12,7 +12,7 @@ namespace {
 using vws::BwdArgs;
 using vws::FwdArgs;
 
-int elem_size(int dtype) { return dtype == VWS_BF16 ? 2 : 4; }
+int elem_size(int dtype) { return dtype == VWS_F32 ? 4 : 2; }
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   if (a < 0 || b < 0) return false;
@@ -26,7 +26,7 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 // Validates one logits descriptor; on success *N is its row count.
 int check_rows(const vws_rows* r, int64_t* N) {
   if (!r) return VWS_EINVAL;
-  if (r->dtype != VWS_F32 && r->dtype != VWS_BF16) return VWS_EDTYPE;
+  if (r->dtype != VWS_F32 && r->dtype != VWS_BF16 && r->dtype != VWS_F16) return VWS_EDTYPE;
   if (r->n_outer < 0 || r->n_inner < 0 || r->V < 1) return VWS_EINVAL;
   if (r->V > (int64_t)INT32_MAX - 4096) return VWS_EINVAL;  // column and group indexes are 32-bit
   if (r->col_stride != 1) return VWS_ELAYOUT;
@@ -80,11 +80,18 @@ vws::IdsDev ids_dev(const vws_ids* t) { return vws::IdsDev{t ? t->data : nullptr
 
 int state_floats(int op) { return op == VWS_OP_KL ? 6 : 3; }
 
+// Segment length (in groups of 8 columns) of the batch-invariant split: 32768 columns.
+constexpr int64_t kInvariantGroups = 4096;
+
 // Vocabulary parts per row for the forward (see vws_split_parts in vws.h).
 int parts_for(int op, int64_t N, int64_t V, int hint) {
   const int64_t G = (V + 7) / 8;
   int64_t P;
-  if (hint == 1) {
+  if (hint == VWS_SPLIT_INVARIANT) {
+    // fixed vocabulary segments of kInvariantGroups groups: the part count, and so
+    // every row's reduction order, depends on V alone (batch invariant)
+    P = (G + kInvariantGroups - 1) / kInvariantGroups;
+  } else if (hint == 1) {
     P = 1;
   } else if (hint > 1) {
     P = hint < G ? hint : G;
@@ -115,7 +122,7 @@ int fwd_common(int op, const vws_rows* a, const vws_rows* b, const vws_ids* t, i
     if (b->dtype != a->dtype) return VWS_EDTYPE;
     if (Nb != N || b->V != a->V || b->n_inner != a->n_inner) return VWS_EINVAL;
   }
-  if (split_hint < 0) return VWS_EINVAL;
+  if (split_hint < VWS_SPLIT_INVARIANT) return VWS_EINVAL;
   if (N == 0) return VWS_OK;
   if (op == VWS_OP_LOGPROBS && !stats_only && (rc = check_ids(t))) return rc;
   if ((!out && !stats_only) || !stats) return VWS_EINVAL;
@@ -331,7 +338,7 @@ VWS_API int vws_linear_logp_bwd(const void* h, int64_t ldh, const void* W, int64
 
 
 VWS_API size_t vws_workspace_bytes(int op, int64_t N, int64_t V, int split_hint) {
-  if (op < VWS_OP_LOGPROBS || op > VWS_OP_JSD || N < 0 || V < 1 || split_hint < 0) return (size_t)-1;
+  if (op < VWS_OP_LOGPROBS || op > VWS_OP_JSD || N < 0 || V < 1 || split_hint < VWS_SPLIT_INVARIANT) return (size_t)-1;
   if (N == 0) return 0;
   const int P = parts_for(op, N, V, split_hint);
   if (op == VWS_OP_JSD) return jsd_ws_bytes(N, P);
@@ -339,7 +346,7 @@ VWS_API size_t vws_workspace_bytes(int op, int64_t N, int64_t V, int split_hint)
 }
 
 VWS_API int vws_split_parts(int op, int64_t N, int64_t V, int split_hint) {
-  if (op < VWS_OP_LOGPROBS || op > VWS_OP_JSD || N < 0 || V < 1 || split_hint < 0) return VWS_EINVAL;
+  if (op < VWS_OP_LOGPROBS || op > VWS_OP_JSD || N < 0 || V < 1 || split_hint < VWS_SPLIT_INVARIANT) return VWS_EINVAL;
   return parts_for(op, N, V, split_hint);
 }
 
@@ -378,7 +385,7 @@ VWS_API int vws_logprobs_topk_fwd(const vws_rows* z, const vws_ids_k* ids, int64
   int64_t N;
   int rc = check_rows(z, &N);
   if (rc) return rc;
-  if (split_hint < 0) return VWS_EINVAL;
+  if (split_hint < VWS_SPLIT_INVARIANT) return VWS_EINVAL;
   if (N == 0) return VWS_OK;
   if ((rc = check_ids_k(ids))) return rc;
   if (!logp || !stats) return VWS_EINVAL;
@@ -431,7 +438,7 @@ VWS_API int vws_jsd_fwd(const vws_rows* s, const vws_rows* t, float beta, float*
   int64_t N;
   int rc = jsd_check_pair(s, t, &N);
   if (rc) return rc;
-  if (split_hint < 0) return VWS_EINVAL;
+  if (split_hint < VWS_SPLIT_INVARIANT) return VWS_EINVAL;
   if (N == 0) return VWS_OK;
   if (!jsd || !stats) return VWS_EINVAL;
   if (!aligned(jsd, 4) || !aligned(stats, 4)) return VWS_ELAYOUT;

@@ -163,8 +163,10 @@ hipError_t launch_bwd_t(const BwdArgs& p, hipStream_t stream) {
 
 template <int OP>
 hipError_t launch_bwd_op(const BwdArgs& p, int dtype, bool vec, hipStream_t stream) {
-  if (dtype == kBF16) return vec ? launch_bwd_t<OP, kBF16, true>(p, stream) : launch_bwd_t<OP, kBF16, false>(p, stream);
-  return vec ? launch_bwd_t<OP, kF32, true>(p, stream) : launch_bwd_t<OP, kF32, false>(p, stream);
+  return dispatch_dtype(dtype, [&](auto dt) {
+    constexpr int DT = decltype(dt)::value;
+    return vec ? launch_bwd_t<OP, DT, true>(p, stream) : launch_bwd_t<OP, DT, false>(p, stream);
+  });
 }
 }  // namespace
 

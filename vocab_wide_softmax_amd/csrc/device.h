@@ -33,7 +33,7 @@ namespace vws {
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kInf = __builtin_inff();
 
-enum Dtype : int { kF32 = 0, kBF16 = 1 };
+enum Dtype : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
 enum Op : int { kLogprobs = 0, kEntropy = 1, kKL = 2 };
 
 // Cache policy of the streaming accesses: the logits are read once and the
@@ -68,6 +68,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 extern "C" __device__ float vws_llvm_fmul_legacy(float, float) __asm("llvm.amdgcn.fmul.legacy");
 
@@ -79,7 +81,7 @@ __device__ __forceinline__ float expf_fast(float x) { return __builtin_amdgcn_ex
 
 template <int DT>
 struct ElemSize {
-  static constexpr int value = DT == kBF16 ? 2 : 4;
+  static constexpr int value = DT == kF32 ? 4 : 2;
 };
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t hi16) { return __uint_as_float(hi16 << 16); }
@@ -90,7 +92,11 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t hi16) { return __ui
 
 template <int DT>
 __device__ __forceinline__ void load_group_vec(const char* __restrict__ row, int32_t g, float (&x)[8]) {
-  if constexpr (DT == kBF16) {
+  if constexpr (DT == kF16) {
+    const f16x8 h = __builtin_bit_cast(f16x8, stream_load(reinterpret_cast<const u32x4*>(row) + g));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = (float)h[k];
+  } else if constexpr (DT == kBF16) {
     u32x4 w = stream_load(reinterpret_cast<const u32x4*>(row) + g);
     x[0] = __uint_as_float(w.x << 16);
     x[1] = __uint_as_float(w.x & 0xffff0000u);
@@ -111,7 +117,9 @@ __device__ __forceinline__ void load_group_vec(const char* __restrict__ row, int
 
 template <int DT>
 __device__ __forceinline__ float load_elem(const char* __restrict__ row, int64_t col) {
-  if constexpr (DT == kBF16) {
+  if constexpr (DT == kF16) {
+    return (float)reinterpret_cast<const _Float16*>(row)[col];
+  } else if constexpr (DT == kBF16) {
     return bf16_bits_to_float(reinterpret_cast<const uint16_t*>(row)[col]);
   } else {
     return reinterpret_cast<const float*>(row)[col];
@@ -142,7 +150,14 @@ __device__ __forceinline__ void load_group(const char* __restrict__ row, int32_t
 
 template <int DT>
 __device__ __forceinline__ void store_group_vec(char* __restrict__ row, int32_t g, const float (&y)[8]) {
-  if constexpr (DT == kBF16) {
+  if constexpr (DT == kF16) {
+    u32x4 w;
+    w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){y[0], y[1]}, f16x2));
+    w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){y[2], y[3]}, f16x2));
+    w.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){y[4], y[5]}, f16x2));
+    w.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){y[6], y[7]}, f16x2));
+    stream_store(w, reinterpret_cast<u32x4*>(row) + g);
+  } else if constexpr (DT == kBF16) {
     u32x4 w;
     w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){y[0], y[1]}, bf16x2));
     w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){y[2], y[3]}, bf16x2));
@@ -158,7 +173,9 @@ __device__ __forceinline__ void store_group_vec(char* __restrict__ row, int32_t 
 
 template <int DT>
 __device__ __forceinline__ void store_elem(char* __restrict__ row, int64_t col, float y) {
-  if constexpr (DT == kBF16) {
+  if constexpr (DT == kF16) {
+    reinterpret_cast<_Float16*>(row)[col] = (_Float16)y;
+  } else if constexpr (DT == kBF16) {
     bf16x2 h = __builtin_convertvector((f32x2){y, 0.0f}, bf16x2);
     reinterpret_cast<uint16_t*>(row)[col] = (uint16_t)(__builtin_bit_cast(uint32_t, h) & 0xffffu);
   } else {

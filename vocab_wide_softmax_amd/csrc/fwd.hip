@@ -300,8 +300,10 @@ hipError_t launch_fwd_t(const FwdArgs& p, hipStream_t stream) {
 
 template <int OP>
 hipError_t launch_fwd_op(const FwdArgs& p, int dtype, bool vec, hipStream_t stream) {
-  if (dtype == kBF16) return vec ? launch_fwd_t<OP, kBF16, true>(p, stream) : launch_fwd_t<OP, kBF16, false>(p, stream);
-  return vec ? launch_fwd_t<OP, kF32, true>(p, stream) : launch_fwd_t<OP, kF32, false>(p, stream);
+  return dispatch_dtype(dtype, [&](auto dt) {
+    constexpr int DT = decltype(dt)::value;
+    return vec ? launch_fwd_t<OP, DT, true>(p, stream) : launch_fwd_t<OP, DT, false>(p, stream);
+  });
 }
 }  // namespace
 

@@ -245,14 +245,12 @@ int32_t jsd_tiles_per_row(int64_t V) {
 
 hipError_t launch_jsd_div(const JsdArgs& p, int dtype, bool vec, hipStream_t stream) {
   const dim3 grid((uint32_t)grid_cap(p.N * p.parts)), block(kJsdBlock);
-  if (dtype == kBF16) {
-    if (vec) hipLaunchKernelGGL((jsd_div_kernel<kBF16, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((jsd_div_kernel<kBF16, false>), grid, block, 0, stream, p);
-  } else {
-    if (vec) hipLaunchKernelGGL((jsd_div_kernel<kF32, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((jsd_div_kernel<kF32, false>), grid, block, 0, stream, p);
-  }
-  hipError_t e = hipGetLastError();
+  hipError_t e = dispatch_dtype(dtype, [&](auto dt) {
+    constexpr int DT = decltype(dt)::value;
+    if (vec) hipLaunchKernelGGL((jsd_div_kernel<DT, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((jsd_div_kernel<DT, false>), grid, block, 0, stream, p);
+    return hipGetLastError();
+  });
   if (e != hipSuccess || p.parts == 1) return e;
   hipLaunchKernelGGL(jsd_combine_kernel, dim3((uint32_t)grid_cap((p.N + 255) / 256)), dim3(256), 0, stream, p);
   return hipGetLastError();
@@ -260,14 +258,12 @@ hipError_t launch_jsd_div(const JsdArgs& p, int dtype, bool vec, hipStream_t str
 
 hipError_t launch_jsd_bwd(const JsdArgs& p, int dtype, bool vec, hipStream_t stream) {
   const dim3 grid((uint32_t)grid_cap(p.N * p.tiles_per_row)), block(kJsdBlock);
-  if (dtype == kBF16) {
-    if (vec) hipLaunchKernelGGL((jsd_bwd_kernel<kBF16, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((jsd_bwd_kernel<kBF16, false>), grid, block, 0, stream, p);
-  } else {
-    if (vec) hipLaunchKernelGGL((jsd_bwd_kernel<kF32, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((jsd_bwd_kernel<kF32, false>), grid, block, 0, stream, p);
-  }
-  return hipGetLastError();
+  return dispatch_dtype(dtype, [&](auto dt) {
+    constexpr int DT = decltype(dt)::value;
+    if (vec) hipLaunchKernelGGL((jsd_bwd_kernel<DT, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((jsd_bwd_kernel<DT, false>), grid, block, 0, stream, p);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace vws

@@ -9,6 +9,21 @@
 
 namespace vws {
 
+template <int DT>
+struct DtypeTag {
+  static constexpr int value = DT;
+};
+
+// Calls f(DtypeTag<DT>{}) for the logits dtype code (kF32, kBF16 or kF16).
+template <class F>
+hipError_t dispatch_dtype(int dtype, F&& f) {
+  switch (dtype) {
+    case kBF16: return f(DtypeTag<kBF16>{});
+    case kF16: return f(DtypeTag<kF16>{});
+    default: return f(DtypeTag<kF32>{});
+  }
+}
+
 struct FwdArgs {
   RowsDev a, b;  // b used by KL only
   IdsDev ids;    // logprobs only

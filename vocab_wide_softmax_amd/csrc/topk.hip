@@ -173,22 +173,21 @@ int32_t topk_tiles_per_row(int64_t V) {
 
 hipError_t launch_topk_gather(const TopkArgs& p, int dtype, hipStream_t stream) {
   const int64_t blocks = grid_cap((p.N * p.K + 255) / 256);
-  if (dtype == kBF16) hipLaunchKernelGGL((topk_gather_kernel<kBF16>), dim3((uint32_t)blocks), dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((topk_gather_kernel<kF32>), dim3((uint32_t)blocks), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  return dispatch_dtype(dtype, [&](auto dt) {
+    hipLaunchKernelGGL((topk_gather_kernel<decltype(dt)::value>), dim3((uint32_t)blocks), dim3(256), 0, stream, p);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_topk_bwd(const TopkArgs& p, int dtype, bool vec, hipStream_t stream) {
   const int64_t blocks = grid_cap(p.N * p.tiles_per_row);
   const dim3 grid((uint32_t)blocks), block(kTopkBlock);
-  if (dtype == kBF16) {
-    if (vec) hipLaunchKernelGGL((topk_bwd_kernel<kBF16, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((topk_bwd_kernel<kBF16, false>), grid, block, 0, stream, p);
-  } else {
-    if (vec) hipLaunchKernelGGL((topk_bwd_kernel<kF32, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((topk_bwd_kernel<kF32, false>), grid, block, 0, stream, p);
-  }
-  return hipGetLastError();
+  return dispatch_dtype(dtype, [&](auto dt) {
+    constexpr int DT = decltype(dt)::value;
+    if (vec) hipLaunchKernelGGL((topk_bwd_kernel<DT, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((topk_bwd_kernel<DT, false>), grid, block, 0, stream, p);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace vws
