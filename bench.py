@@ -86,7 +86,7 @@ def make_inputs(wl, device):
     return wl, a, b, t, g
 
 
-def run_step(B, a, b, t, g, ev=None):
+def run_step(B, a, b, t, g, ev=None, split=0):
     """One pass of the hot path. ev: optional dict of (start, end) event lists per op phase."""
     import torch
 
@@ -97,20 +97,20 @@ def run_step(B, a, b, t, g, ev=None):
             ev[key][i].record(stream)
 
     rec("logprobs_fwd", 0)
-    lp, st = B.logprobs_fwd(a, t, -100)
+    lp, st = B.logprobs_fwd(a, t, -100, split)
     rec("logprobs_fwd", 1)
     rec("logprobs_bwd", 0)
     B.logprobs_bwd(a, t, st, g["logprobs"], -100)
     rec("logprobs_bwd", 1)
     rec("entropy_fwd", 0)
-    H, st = B.entropy_fwd(a)
+    H, st = B.entropy_fwd(a, split)
     rec("entropy_fwd", 1)
     rec("entropy_bwd", 0)
     B.entropy_bwd(a, st, H, g["entropy"])
     rec("entropy_bwd", 1)
     for name, x, y in (("kl_ab", a, b), ("kl_ba", b, a)):
         rec(name + "_fwd", 0)
-        kl, st = B.kl_fwd(x, y)
+        kl, st = B.kl_fwd(x, y, split)
         rec(name + "_fwd", 1)
         rec(name + "_bwd", 0)
         B.kl_bwd(x, y, st, kl, g[name])
@@ -146,6 +146,74 @@ def gpu_bench(wl, steps, warmup, device):
     med = {k: sorted(v)[len(v) // 2] for k, v in per.items()}
     mean = {k: sum(v) / len(v) for k, v in per.items()}
     return ms_per_step, med, mean
+
+
+# ------------------------------------------------------------------------- other ops
+
+def _timed(fwd, bwd, steps, warmup):
+    """Median fwd and bwd milliseconds (HIP events on the current stream)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        bwd(fwd())
+    f, b = [], []
+    for _ in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        r = fwd()
+        e[1].record(stream)
+        bwd(r)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        f.append(e[0].elapsed_time(e[1]))
+        b.append(e[1].elapsed_time(e[2]))
+    return sorted(f)[steps // 2], sorted(b)[steps // 2]
+
+
+def extras_bench(wl, device, steps=7, warmup=2):
+    """The other ops on the same 8192 x 75968 pair, each fwd+bwd, with their algorithmic bytes:
+    top-k logprobs (K = 16 ids per row), the generalized JSD (beta = 0.5: two reads of both
+    inputs forward, one read of both and two writes backward), the four-op step on fp16 copies
+    of the logits, and the four-op step in the batch-invariant split mode."""
+    import torch
+
+    from vocab_wide_softmax_amd import binding as B
+    from vocab_wide_softmax_amd import workloads as W
+
+    a, b = wl.a.to(device), wl.b.to(device)
+    g = {op: wl.g[op].to(device) for op in W.OPS}
+    ids = torch.randint(0, V, (N_ROWS, 16), generator=torch.Generator().manual_seed(5)).to(device)
+    gk = torch.randn(N_ROWS, 16, generator=torch.Generator().manual_seed(6)).to(device)
+    torch.cuda.synchronize()
+    out = {}
+
+    def put(name, f_ms, b_ms, nbytes):
+        gbs = nbytes / ((f_ms + b_ms) * 1e-3) / 1e9
+        out[name] = {"fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "fwd_bwd_ms": round(f_ms + b_ms, 4),
+                     "bytes": nbytes, "GB/s": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
+
+    f_ms, b_ms = _timed(lambda: B.logprobs_topk_fwd(a, ids, -100),
+                        lambda r: B.logprobs_topk_bwd(a, ids, r[1], gk, -100), steps, warmup)
+    put("logprobs_topk16", f_ms, b_ms, 3 * T_BYTES)
+    f_ms, b_ms = _timed(lambda: B.jsd_fwd(a, b, 0.5),
+                        lambda r: B.jsd_bwd(a, b, 0.5, r[1], r[0], g["kl_ab"]), steps, warmup)
+    put("jsd_beta0.5", f_ms, b_ms, 8 * T_BYTES)
+    t = wl.t.to(device)
+    for name, x, y, split in (("step_fp16", a.half(), b.half(), 0), ("step_batch_invariant", a, b, -1)):
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            run_step(B, x, y, t, g, split=split)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            run_step(B, x, y, t, g, split=split)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        gbs = STEP_BYTES / (ms * 1e-3) / 1e9
+        out[name] = {"ms_per_step": round(ms, 4), "bytes": STEP_BYTES, "GB/s": round(gbs, 1),
+                     "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
+    return out
 
 
 # ------------------------------------------------------------------- fused linear-logp
@@ -359,6 +427,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-linear", action="store_true", help="skip the fused linear-logp workload")
+    ap.add_argument("--no-extras", action="store_true", help="skip top-k, JSD, fp16 and batch-invariant timings")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--summarize", nargs=2, metavar=("DIR", "MODE"))
@@ -429,6 +498,9 @@ def main():
                      "avg_launch_ms": round(dom_ms, 4)},
     }
     out["cpu_baseline"] = cpu
+    if not args.no_extras:
+        log("other ops: top-k logprobs, JSD, fp16 step, batch-invariant step")
+        out["other_ops"] = extras_bench(wl, device)
     if not args.no_linear:
         out["linear_logp"] = linear_bench(max(3, args.steps // 4), 2, device)
         log("linear-logp: %.2f ms fwd, %.2f ms bwd" % (out["linear_logp"]["fwd_ms"], out["linear_logp"]["bwd_ms"]))
