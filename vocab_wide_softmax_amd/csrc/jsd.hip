@@ -56,28 +56,44 @@ __device__ __forceinline__ JsdRow jsd_row(const float* st4, float beta) {
   return r;
 }
 
-// log p_S, log p_T, p_S, p_T and log M of one column.
-__device__ __forceinline__ void jsd_point(const JsdRow& r, float xs, float xt, float& ls, float& lt, float& ps,
-                                          float& pt, float& lm) {
-  ls = (xs - r.ms) - r.lss;
-  lt = (xt - r.mt) - r.lst;
-  ps = expf_fast(ls);
-  pt = expf_fast(lt);
-  const float mix = __builtin_fmaf(r.wt, pt, r.ws * ps);
-  if (mix >= kFltMin) {
-    lm = __builtin_amdgcn_logf(mix) * kLn2;
-  } else {
-    // both probabilities tiny or zero: log M = max(ls, lt) + log((1-b) e^(ls-mx) + b e^(lt-mx)),
-    // whose argument lies in [min(b, 1-b), 1]; NaN when both entries are masked (zero weight)
-    const float mx = fmaxf(ls, lt);
-    const float inner = __builtin_fmaf(r.wt, expf_fast(lt - mx), r.ws * expf_fast(ls - mx));
-    lm = mx + __builtin_amdgcn_logf(inner) * kLn2;
+// Base-2 log-probabilities u = log2 p of one group of 8 columns, the probabilities, and
+// l = log2 M of the mixture. log M is taken from the mixture itself while that is a
+// normal float; a group holding a smaller mixture (both probabilities tiny, or both
+// entries masked) recomputes it as mx + log2((1-b) 2^(us-mx) + b 2^(ut-mx)) with
+// mx = max(us, ut), whose argument lies in [min(b, 1-b), 1] (NaN when both are masked,
+// where both weights are 0).
+struct JsdGroup {
+  float us[8], ut[8], ps[8], pt[8], lm[8];
+};
+
+__device__ __forceinline__ void jsd_group(const JsdRow& r, const float (&xs)[8], const float (&xt)[8], JsdGroup& q) {
+  bool small = false;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    q.us[j] = ((xs[j] - r.ms) - r.lss) * kLog2e;
+    q.ut[j] = ((xt[j] - r.mt) - r.lst) * kLog2e;
+    q.ps[j] = __builtin_amdgcn_exp2f(q.us[j]);
+    q.pt[j] = __builtin_amdgcn_exp2f(q.ut[j]);
+    const float mix = __builtin_fmaf(r.wt, q.pt[j], r.ws * q.ps[j]);
+    q.lm[j] = __builtin_amdgcn_logf(mix);
+    small |= !(mix >= kFltMin);
+  }
+  if (small) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float mx = fmaxf(q.us[j], q.ut[j]);
+      const float inner =
+          __builtin_fmaf(r.wt, __builtin_amdgcn_exp2f(q.ut[j] - mx), r.ws * __builtin_amdgcn_exp2f(q.us[j] - mx));
+      const float mix = __builtin_fmaf(r.wt, q.pt[j], r.ws * q.ps[j]);
+      if (!(mix >= kFltMin)) q.lm[j] = mx + __builtin_amdgcn_logf(inner);
+    }
   }
 }
 
 // ---- pass 2: the two KL-to-mixture sums ------------------------------------------------
 
-// Writes the row's outputs: JSD, and stats (m_s, log S_s, m_t, log S_t, K_S, K_T).
+// Writes the row's outputs from the base-2 sums: JSD, and stats (m_s, log S_s, m_t, log S_t,
+// K_S, K_T) with K in natural units.
 __device__ void jsd_finalize(const JsdArgs& p, int64_t row, float Ks, float Kt) {
   const float* st4 = p.st4 + 4 * row;
   float* o = p.stats + 6 * row;
@@ -87,9 +103,10 @@ __device__ void jsd_finalize(const JsdArgs& p, int64_t row, float Ks, float Kt) 
   o[2] = r.mt;
   o[3] = r.lst;
   const float qnan = __builtin_nanf("");
-  o[4] = r.bad ? qnan : Ks;
-  o[5] = r.bad ? qnan : Kt;
-  p.out[row] = r.bad ? qnan : (float)((double)p.beta * (double)Kt + (1.0 - (double)p.beta) * (double)Ks);
+  const double ks = (double)Ks * 0.69314718055994530942, kt = (double)Kt * 0.69314718055994530942;
+  o[4] = r.bad ? qnan : (float)ks;
+  o[5] = r.bad ? qnan : (float)kt;
+  p.out[row] = r.bad ? qnan : (float)((double)p.beta * kt + (1.0 - (double)p.beta) * ks);
 }
 
 
@@ -112,8 +129,30 @@ __global__ __launch_bounds__(kJsdBlock) void jsd_div_kernel(JsdArgs p) {
     const JsdRow r = jsd_row(p.st4 + 4 * row, p.beta);
     const char* rs = row_ptr<DT>(p.s, row);
     const char* rt = row_ptr<DT>(p.t, row);
-    float Ks = 0.0f, Kt = 0.0f;
-    for (int32_t gb = g0 + tid; gb < g1; gb += kJsdBlock * U) {
+    float Ks = 0.0f, Kt = 0.0f;  // base-2 sums; scaled by ln 2 once per row
+    auto accumulate = [&](const float (&xs)[8], const float (&xt)[8]) {
+      JsdGroup q;
+      jsd_group(r, xs, xt, q);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        Ks += mul0(q.ps[j], q.us[j] - q.lm[j]);
+        Kt += mul0(q.pt[j], q.ut[j] - q.lm[j]);
+      }
+    };
+    int32_t gb = g0 + tid;
+    // whole vector groups of every lane: no predicates
+    const int32_t nfull = VEC ? (min(g1, g_full) - g0) / (kJsdBlock * U) : 0;
+    for (int32_t it = 0; it < nfull; ++it, gb += kJsdBlock * U) {
+      float xs[U][8], xt[U][8];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        load_group_vec<DT>(rs, gb + k * kJsdBlock, xs[k]);
+        load_group_vec<DT>(rt, gb + k * kJsdBlock, xt[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k) accumulate(xs[k], xt[k]);
+    }
+    for (; gb < g1; gb += kJsdBlock * U) {
 #pragma unroll
       for (int k = 0; k < U; ++k) {
         const int32_t g = gb + k * kJsdBlock;
@@ -121,13 +160,7 @@ __global__ __launch_bounds__(kJsdBlock) void jsd_div_kernel(JsdArgs p) {
           float xs[8], xt[8];
           load_group<DT, VEC>(rs, g, V, g_full, xs);
           load_group<DT, VEC>(rt, g, V, g_full, xt);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            float ls, lt, ps, pt, lm;
-            jsd_point(r, xs[j], xt[j], ls, lt, ps, pt, lm);
-            Ks += mul0(ps, ls - lm);
-            Kt += mul0(pt, lt - lm);
-          }
+          accumulate(xs, xt);
         }
       }
     }
@@ -189,12 +222,13 @@ __device__ __forceinline__ void jsd_bwd_groups(const JsdRow& r, float Ks, float 
       load_group<DT, true>(rs, g, V, g_full, xs);
       load_group<DT, true>(rt, g, V, g_full, xt);
     }
+    JsdGroup q;
+    jsd_group(r, xs, xt, q);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float ls, lt, ps, pt, lm;
-      jsd_point(r, xs[j], xt[j], ls, lt, ps, pt, lm);
-      ys[j] = r.bad ? qnan : mul0(ps, (ls - lm) - Ks) * gs;
-      yt[j] = r.bad ? qnan : mul0(pt, (lt - lm) - Kt) * gt;
+      // (log p - log M) - K in natural units: ln 2 (u - l) - K
+      ys[j] = r.bad ? qnan : mul0(q.ps[j], __builtin_fmaf(kLn2, q.us[j] - q.lm[j], -Ks)) * gs;
+      yt[j] = r.bad ? qnan : mul0(q.pt[j], __builtin_fmaf(kLn2, q.ut[j] - q.lm[j], -Kt)) * gt;
     }
     if (FULL) {
       if (os) store_group_vec<DT>(os, g, ys);

@@ -24,7 +24,7 @@ namespace vws {
 
 namespace {
 constexpr int kTopkBlock = 256;
-constexpr int kTopkUB = 2;
+constexpr int kTopkUB = 4;  // groups of 8 columns per lane per tile (8192-column tiles)
 }  // namespace
 
 __device__ __forceinline__ int64_t topk_id(const TopkArgs& p, int64_t row, int32_t k) {
@@ -52,16 +52,33 @@ __global__ __launch_bounds__(256) void topk_gather_kernel(TopkArgs p) {
   }
 }
 
-template <int DT, bool FULL>
-__device__ __forceinline__ void topk_groups(const char* ra, char* oa, int32_t g, int n, int32_t G, int32_t V,
+// Loads this lane's groups of the tile (issued before the slot phase so that their
+// latency overlaps it); groups past the row end read as -inf and are not stored.
+template <int DT, bool FULL, int UB>
+__device__ __forceinline__ void topk_load(const char* ra, int32_t g, int32_t G, int32_t V, int32_t g_full,
+                                          float (&x)[UB][8]) {
+#pragma unroll
+  for (int u = 0; u < UB; ++u, g += kTopkBlock) {
+    if (FULL) {
+      load_group_vec<DT>(ra, g, x[u]);
+    } else if (g < G) {
+      load_group<DT, true>(ra, g, V, g_full, x[u]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[u][j] = -kInf;
+    }
+  }
+}
+
+template <int DT, bool FULL, int UB>
+__device__ __forceinline__ void topk_groups(const float (&x)[UB][8], char* oa, int32_t g, int32_t G, int32_t V,
                                             int32_t g_full, int32_t c0, float m, float ls, float Gs, bool nan_row,
                                             bool zero_row, const int32_t* s_col, const float* s_g, int cnt) {
   const float qnan = __builtin_nanf("");
-  for (int u = 0; u < n; ++u, g += kTopkBlock) {
+#pragma unroll
+  for (int u = 0; u < UB; ++u, g += kTopkBlock) {
     if (!FULL && g >= G) break;
-    float x[8], y[8], h[8];
-    if (FULL) load_group_vec<DT>(ra, g, x);
-    else load_group<DT, true>(ra, g, V, g_full, x);
+    float y[8], h[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) h[j] = 0.0f;
     const int32_t lg = g - (c0 >> 3);  // group index inside the tile
@@ -76,7 +93,7 @@ __device__ __forceinline__ void topk_groups(const char* ra, char* oa, int32_t g,
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float pj = expf_fast((x[j] - m) - ls);
+      const float pj = expf_fast((x[u][j] - m) - ls);
       y[j] = zero_row ? 0.0f : (nan_row ? qnan : __builtin_fmaf(-Gs, pj, h[j]));
     }
     if (FULL) store_group_vec<DT>(oa, g, y);
@@ -84,7 +101,7 @@ __device__ __forceinline__ void topk_groups(const char* ra, char* oa, int32_t g,
   }
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, int UB>
 __global__ __launch_bounds__(kTopkBlock) void topk_bwd_kernel(TopkArgs p) {
   constexpr int NW = kTopkBlock / 64;
   constexpr int ES = ElemSize<DT>::value;
@@ -102,8 +119,14 @@ __global__ __launch_bounds__(kTopkBlock) void topk_bwd_kernel(TopkArgs p) {
   for (int64_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
     const int64_t row = vb / tpr;
     const int32_t tile = (int32_t)(vb - row * tpr);
-    const int32_t g0 = tile * (kTopkBlock * kTopkUB);
-    const int32_t c0 = g0 * 8, c1 = min(V, c0 + kTopkBlock * kTopkUB * 8);
+    const int32_t g0 = tile * (kTopkBlock * UB);
+    const int32_t c0 = g0 * 8, c1 = min(V, c0 + kTopkBlock * UB * 8);
+    const char* ra = row_ptr<DT>(p.a, row);
+    const int32_t g = g0 + tid;
+    const bool full = VEC && g0 + kTopkBlock * UB <= g_full;
+    float x[UB][8];
+    if (full) topk_load<DT, true, UB>(ra, g, G, V, g_full, x);
+    else topk_load<DT, false, UB>(ra, g, G, V, g_full, x);
 
     // Slots: G (sum of live g, fixed reduction tree), flags, and the tile's live ids in slot order.
     if (tid == 0) s_flags = 0;
@@ -153,15 +176,13 @@ __global__ __launch_bounds__(kTopkBlock) void topk_bwd_kernel(TopkArgs p) {
     for (int w = 1; w < NW; ++w) Gs += s_red[w];
     const int fl = s_flags;
 
-    const char* ra = row_ptr<DT>(p.a, row);
     char* oa = p.dz + row * (int64_t)V * ES;
     const float m = p.stats[2 * row], ls = p.stats[2 * row + 1];
     const bool zero_row = !(fl & 1), nan_row = (fl & 2) != 0;
-    const int32_t g = g0 + tid;
-    if (VEC && g0 + kTopkBlock * kTopkUB <= g_full)
-      topk_groups<DT, true>(ra, oa, g, kTopkUB, G, V, g_full, c0, m, ls, Gs, nan_row, zero_row, s_col, s_g, cnt);
+    if (full)
+      topk_groups<DT, true, UB>(x, oa, g, G, V, g_full, c0, m, ls, Gs, nan_row, zero_row, s_col, s_g, cnt);
     else
-      topk_groups<DT, false>(ra, oa, g, kTopkUB, G, V, g_full, c0, m, ls, Gs, nan_row, zero_row, s_col, s_g, cnt);
+      topk_groups<DT, false, UB>(x, oa, g, G, V, g_full, c0, m, ls, Gs, nan_row, zero_row, s_col, s_g, cnt);
     __syncthreads();  // LDS is reused by the next tile
   }
 }
@@ -184,8 +205,8 @@ hipError_t launch_topk_bwd(const TopkArgs& p, int dtype, bool vec, hipStream_t s
   const dim3 grid((uint32_t)blocks), block(kTopkBlock);
   return dispatch_dtype(dtype, [&](auto dt) {
     constexpr int DT = decltype(dt)::value;
-    if (vec) hipLaunchKernelGGL((topk_bwd_kernel<DT, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((topk_bwd_kernel<DT, false>), grid, block, 0, stream, p);
+    if (vec) hipLaunchKernelGGL((topk_bwd_kernel<DT, true, kTopkUB>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((topk_bwd_kernel<DT, false, kTopkUB>), grid, block, 0, stream, p);
     return hipGetLastError();
   });
 }
