@@ -49,10 +49,15 @@ KERNEL_SOURCES = ["vocab_wide_softmax_amd/csrc/bwd.hip", "vocab_wide_softmax_amd
 
 
 def kernel_source_hash():
+    """Hash of the dominant kernel's code with // comments and blank lines removed, so that
+    the stored counter figures stay valid across comment-only edits and no longer."""
+    import re
+
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            src = re.sub(r"//[^\n]*", "", f.read())
+        h.update("\n".join(line.rstrip() for line in src.split("\n") if line.strip()).encode())
     return h.hexdigest()[:16]
 
 

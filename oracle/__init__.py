@@ -14,7 +14,7 @@ linear logp Triton"):
   backward, written as the plain two-pass definitions (max, then sums) in
   float64. The single-read identities H = log S - W/S and
   KL = W/S_A - log S_A + log S_B (PR #8838, second commit message and the
-  review comment "read each logit once") are evaluated separately by
+  review comment proposing a single read) are evaluated separately by
   ``single_read_identities`` as a self-check, never as the answer.
 * ``topk``        -- multi-id (top-k) log-probabilities: K ids per row, ignored
   slots, duplicate ids whose upstream gradients add (the PR #8838 test list).

@@ -1,11 +1,10 @@
 // bwd.hip -- fused backward of logprobs, entropy and KL(A||B).
 //
 // The probabilities are recomputed in registers from the per-row statistics
-// the forward saved (JSD PR text pasted into PR #8838: "Recompute
-// probabilities in registers during backward rather than retaining full FP32
-// probability tensors"), p = exp((z - m) - log S) with m and log S kept apart,
-// and the gradient is written contiguous in the input dtype (second commit
-// message: "Gradients are returned contiguous"), bf16 by round-to-nearest-even.
+// the forward saved, never stored as an fp32 tensor (the JSD PR text pasted
+// into PR #8838, "Changes"), p = exp((z - m) - log S) with m and log S kept
+// apart, and the gradient is written contiguous in the input dtype (second
+// commit message of PR #8838), bf16 by round-to-nearest-even.
 //
 // Grid: one workgroup per (row, column tile); tiles of a row are consecutive
 // workgroups, so the workgroups in flight write one contiguous window of the

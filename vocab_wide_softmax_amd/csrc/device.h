@@ -2,7 +2,7 @@
 //
 // Running statistics of one row (or one part of a row), after DeepSpeed PR
 // #8838 "Add Triton kernels for vocab-parallel logprobs, entropy and KL"
-// (second commit message; review comment "read each logit once"):
+// (second commit message; the review comment proposing a single read):
 //   m  running max,  S = sum e^(z - m),  W = sum e^(z - m) (z - m)
 // and for KL(A||B) the pair (m_a, S_A), (m_b, S_B) with
 //   W = sum e^(a - m_a) ((a - m_a) - (b - m_b))
@@ -10,8 +10,8 @@
 //
 // When the max grows from m to M, S <- s S and W <- s (W + (m - M) S) with
 // s = e^(m - M); parts are merged the same way after taking the larger max.
-// Zero-weight rule (review thread "Guard zero rescaling before applying
-// infinite shifts" and its fix commit): a term or a part whose weight is
+// Zero-weight rule (the review thread on 0 x inf in the rescaling, and its fix
+// commit): a term or a part whose weight is
 // exactly 0 contributes nothing, never 0 x inf. It is implemented with
 // v_mul_legacy_f32, whose product is 0 whenever either factor is 0 (also
 // against inf and NaN).

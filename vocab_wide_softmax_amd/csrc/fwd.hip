@@ -5,12 +5,12 @@
 // owns: group g of part [g0, g1) belongs to lane (g - g0) mod BLOCK, and a
 // lane takes its groups in increasing order, U groups per batch. The element
 // to lane map and the order of operations do not depend on the dtype, so bf16
-// and fp32 inputs holding the same values give bit-identical results (review
-// comment on PR #8838: "bf16 and fp32 inputs give bitwise identical outputs").
+// and fp32 inputs holding the same values give bit-identical results (the
+// review comment on PR #8838 reports the same property for its patched kernels).
 //
 // Per batch the lane takes the batch max first and rescales its state once
-// (second commit message of PR #8838: the weighted sums are "rescaled the same
-// way as the sum-exp" when the max grows), then accumulates e = exp(z - m),
+// (second commit message of PR #8838: when the max grows, the weighted sum is
+// rescaled like the sum-exp), then accumulates e = exp(z - m),
 // S += e, W += e (z - m) with the zero-weight product. Lanes are merged by a
 // butterfly over the wave, waves through LDS in wave order ("lane
 // re-centring", fix commit of the 0 x inf thread).

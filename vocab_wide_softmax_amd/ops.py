@@ -3,9 +3,8 @@
 ``logprobs(z, t)``, ``entropy(z)`` and ``kl(a, b)`` return fp32 per-token
 values (shape of the logits without the last dim) and differentiate through
 the fused HIP backward kernels. Forward KL(B||A) is ``kl(b, a)``. Temperature,
-masking and normalisation stay with the caller, as on the pages (JSD PR text:
-"Leave temperature, optional T-squared scaling, masking and normalization to
-the caller").
+its squared scaling, masking and normalisation stay with the caller, as the JSD
+PR text on the pages states for all these per-token ops ("Changes").
 """
 
 import torch
