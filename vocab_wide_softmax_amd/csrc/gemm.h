@@ -54,6 +54,7 @@ struct Cfg {
   static constexpr int LOADS_PER_STAGE = A_INSTR + B_INSTR;
   static_assert(BK == 32 || BK == 64, "ROWK swizzles exist for 4 and 8 chunks per row");
   static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "tile");
+  static_assert((LA != KROW || BM % 128 == 0) && (LB != KROW || BN % 128 == 0), "KROW swizzle needs 16 chunks per k-row");
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole DMA instructions per wave");
 };
 
@@ -66,14 +67,16 @@ struct Operand {
 };
 
 // Swizzled chunk of a ROWK row (BK / 8 chunks of 16 B per row; the pattern keeps 8 and
-// 16 consecutive rows at one chunk on distinct banks) and of a KROW k-row (R / 8 chunks,
-// swizzled in pairs so a transposing read's 32 contiguous bytes stay together).
+// 16 consecutive rows at one chunk on distinct banks) and of a KROW k-row (R / 8 chunks).
+// A transposing read takes 64 contiguous bytes of each of 4 consecutive k-rows per half
+// wave; XOR-ing the chunk index with 4 (kr mod 4) puts those four 64-byte pieces in the
+// four distinct 64-byte windows of the 256-byte bank space, so they do not conflict.
 template <int BK>
 __device__ __forceinline__ int swz_rowk(int r) {
   if constexpr (BK == 32) return ((r >> 1) ^ (r >> 3)) & 3;
   else return (r ^ (r >> 3)) & 7;
 }
-__device__ __forceinline__ int swz_krow(int kr) { return 2 * (kr & 3); }
+__device__ __forceinline__ int swz_krow(int kr) { return 4 * (kr & 3); }
 
 // Issue this wave's DMA loads of one operand tile for reduction offset k0 into lds_tile.
 template <int L, int R, int BK, int NW, int NINSTR>
