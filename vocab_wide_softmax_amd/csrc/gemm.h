@@ -79,7 +79,10 @@ __device__ __forceinline__ int swz_rowk(int r) {
 __device__ __forceinline__ int swz_krow(int kr) { return 4 * (kr & 3); }
 
 // Issue this wave's DMA loads of one operand tile for reduction offset k0 into lds_tile.
-template <int L, int R, int BK, int NW, int NINSTR>
+// EDGE: the tile may extend past the operand's rows or the stage past its reduction length
+// (rows are clamped, chunks past K read zeros); an interior tile needs neither check, which
+// leaves one pointer add per load.
+template <int L, int R, int BK, int NW, int NINSTR, bool EDGE>
 __device__ __forceinline__ void dma_tile(const Operand& op, int64_t r0, int64_t k0, char* lds_tile, int wave,
                                          int lane) {
 #pragma unroll
@@ -91,16 +94,24 @@ __device__ __forceinline__ void dma_tile(const Operand& op, int64_t r0, int64_t 
       const int r = o / (BK * 2), pc = (o % (BK * 2)) / 16;
       const int c = pc ^ swz_rowk<BK>(r);
       int64_t row = r0 + r;
-      row = row < op.rows ? row : op.rows - 1;
       const int64_t k = k0 + c * 8;
-      src = k < op.K ? (const void*)(op.base + row * op.ld + k) : (const void*)kZeroChunk;
+      if constexpr (EDGE) {
+        row = row < op.rows ? row : op.rows - 1;
+        src = k < op.K ? (const void*)(op.base + row * op.ld + k) : (const void*)kZeroChunk;
+      } else {
+        src = (const void*)(op.base + row * op.ld + k);
+      }
     } else {
       const int kr = o / (R * 2), pc = (o % (R * 2)) / 16;
       const int c = pc ^ swz_krow(kr);
       int64_t row = r0 + c * 8;
-      row = row + 8 <= op.rows ? row : op.rows - 8;
       const int64_t k = k0 + kr;
-      src = k < op.K ? (const void*)(op.base + k * op.ld + row) : (const void*)kZeroChunk;
+      if constexpr (EDGE) {
+        row = row + 8 <= op.rows ? row : op.rows - 8;
+        src = k < op.K ? (const void*)(op.base + k * op.ld + row) : (const void*)kZeroChunk;
+      } else {
+        src = (const void*)(op.base + k * op.ld + row);
+      }
     }
     __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds_tile + instr * 1024), 16, 0, 0);
   }
@@ -218,11 +229,12 @@ __device__ __forceinline__ void stage_ready(int s, int nk) {
 // one run; at the last slice of stage s the workgroup waits for stage s + 1, refills the
 // stage-s buffer with stage s + NSTAGE, and reads stage s + 1's first fragments before
 // stage s's last MFMAs.
-template <class C>
-__device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int64_t m0, int64_t n0, int64_t K,
-                                         char* lds, Acc<C>& acc) {
+template <class C, bool EDGE>
+__device__ __forceinline__ void mainloop_t(const Operand& A, const Operand& B, int64_t m0, int64_t n0, int64_t K,
+                                           char* lds, Acc<C>& acc) {
   constexpr int KQ = C::BK / 16;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS targets stay scalar
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int nk = (int)((K + C::BK - 1) / C::BK);
   acc.zero();
@@ -230,8 +242,8 @@ __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int
   auto issue = [&](int s) {
     char* st = lds + (s % C::NSTAGE) * C::STAGE_BYTES;
     const int64_t k0 = (int64_t)s * C::BK;
-    dma_tile<C::LA, C::BM, C::BK, C::NW, C::A_INSTR>(A, m0, k0, st, wave, lane);
-    dma_tile<C::LB, C::BN, C::BK, C::NW, C::B_INSTR>(B, n0, k0, st + C::A_BYTES, wave, lane);
+    dma_tile<C::LA, C::BM, C::BK, C::NW, C::A_INSTR, EDGE>(A, m0, k0, st, wave, lane);
+    dma_tile<C::LB, C::BN, C::BK, C::NW, C::B_INSTR, EDGE>(B, n0, k0, st + C::A_BYTES, wave, lane);
   };
   auto stage_a = [&](int s) -> const char* { return lds + (s % C::NSTAGE) * C::STAGE_BYTES; };
 
@@ -261,6 +273,16 @@ __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int
     }
   }
   __syncthreads();
+}
+
+// Interior tiles (every row of both operand tiles exists and K is a whole number of stages)
+// take the unchecked loads.
+template <class C>
+__device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int64_t m0, int64_t n0, int64_t K,
+                                         char* lds, Acc<C>& acc) {
+  const bool interior = m0 + C::BM <= A.rows && n0 + C::BN <= B.rows && K % C::BK == 0 && A.K >= K && B.K >= K;
+  if (interior) mainloop_t<C, false>(A, B, m0, n0, K, lds, acc);
+  else mainloop_t<C, true>(A, B, m0, n0, K, lds, acc);
 }
 
 // Row / column of accumulator v of block (i, j) for this lane, relative to the wave tile.

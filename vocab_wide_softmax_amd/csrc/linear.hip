@@ -30,8 +30,8 @@ using gemm::Operand;
 using gemm::ROWK;
 
 typedef Cfg<256, 256, 64, 2, 4, ROWK, ROWK, 2> CfgNT;  // A, B both reduction-contiguous
-typedef Cfg<256, 256, 32, 2, 4, ROWK, KROW, 4> CfgNN;  // dh = dz W
-typedef Cfg<256, 256, 32, 2, 4, KROW, KROW, 4> CfgTN;  // dW = dz^T h
+typedef Cfg<256, 256, 64, 2, 4, ROWK, KROW, 2> CfgNN;  // dh = dz W
+typedef Cfg<256, 256, 64, 2, 4, KROW, KROW, 2> CfgTN;  // dW = dz^T h
 
 namespace gemm {
 __device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
