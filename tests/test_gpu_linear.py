@@ -121,3 +121,28 @@ def test_linear_full_size_sampled(device):
     dw_ref, dw_c = OL.linear_logp_bwd_dw_cond(hh, hw, ht, hg, vocab_rows=cols)
     _assert_ok(compare.check(f64(dW[torch.from_numpy(cols).to(device)]), dw_ref, dw_c, "bf16", GEMM_FACTOR),
                "full dW rows")
+
+
+def test_linear_strided_rows_broadcast_g_and_partial_stage(device):
+    """Row pitches above H (views of wider buffers), H = 72 (a partial last k-stage), ragged
+    N and V (partial tiles in both), and an upstream gradient broadcast from one value."""
+    gen = torch.Generator().manual_seed(21)
+    n, hidden, v = 257, 72, 1000
+    hb = torch.randn(n, 88, generator=gen).to(torch.bfloat16)
+    wb = (0.08 * torch.randn(v, 80, generator=gen)).to(torch.bfloat16)
+    t = torch.randint(0, v, (n,), generator=gen)
+    t[::50] = -100
+    h_dev, w_dev = hb.to(device)[:, :hidden], wb.to(device)[:, :hidden]
+    assert h_dev.stride(0) == 88 and w_dev.stride(0) == 80
+    g = torch.tensor(0.625)
+    logp, stats = B.linear_logp_fwd(h_dev, w_dev, t.to(device), -100)
+    dh, dW = B.linear_logp_bwd(h_dev, w_dev, t.to(device), stats, g.to(device).expand(n), -100)
+    torch.cuda.synchronize()
+    hh, hw, ht = f64(hb[:, :hidden]), f64(wb[:, :hidden]), t.numpy()
+    hg = np.full(n, 0.625)
+    _assert_ok(compare.check(f64(logp), OL.linear_logp_fwd(hh, hw, ht)[0], OL.cond_linear_fwd(hh, hw, ht), "f32"),
+               "strided logp")
+    _assert_ok(compare.check(f64(dh), OL.linear_logp_bwd_dh(hh, hw, ht, hg), OL.cond_linear_dh(hh, hw, ht, hg),
+                             "bf16", GEMM_FACTOR), "strided dh")
+    _assert_ok(compare.check(f64(dW), OL.linear_logp_bwd_dw(hh, hw, ht, hg), OL.cond_linear_dw(hh, hw, ht, hg),
+                             "bf16", GEMM_FACTOR), "strided dW")
