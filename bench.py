@@ -6,13 +6,14 @@ One step = forward + backward of the four per-token ops the pages measure
 bf16 logit pair:
     logprobs(A), entropy(A), KL(A||B) (grads to A and B), KL(B||A) (grads to B and A).
 Inputs are generated on the host (seeded, vocab_wide_softmax_amd.workloads),
-copied to HBM before timing, and every step reruns all eight kernels launches
+copied to HBM before timing, and every step reruns all eight kernel launches
 (plus nothing else) through the C ABI.
 
 Printed: one JSON line with the step throughput in algorithmic GB/s (bytes the
 single-read method must move: 18 x 1.2447 GB per step), ms per step, the
-per-op split, a roofline object for the dominant kernel (the KL backward,
-timed with HIP events on its stream), and the fp64 oracle's throughput on a
+per-op split (from an untimed pass with events around every launch), a roofline
+object for the dominant kernel (the KL(A||B) backward, bracketed by HIP events
+on its stream inside the timed steps), and the fp64 oracle's throughput on a
 bounded sample of the same workload on the host cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -44,6 +45,7 @@ OP_BYTES = {"logprobs": 3 * T_BYTES, "entropy": 3 * T_BYTES, "kl_ab": 6 * T_BYTE
 STEP_BYTES = sum(OP_BYTES.values())
 DOMINANT = "kl_bwd"  # KL backward: reads A and B, writes dA and dB
 DOMINANT_BYTES = 4 * T_BYTES
+DOM_PHASE = "kl_ab_bwd"  # the launch of it that the timed steps bracket with events
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["vocab_wide_softmax_amd/csrc/bwd.hip", "vocab_wide_softmax_amd/csrc/device.h"]
 
@@ -98,7 +100,7 @@ def run_step(B, a, b, t, g, ev=None, split=0):
     stream = torch.cuda.current_stream()
 
     def rec(key, i):
-        if ev is not None:
+        if ev is not None and key in ev:
             ev[key][i].record(stream)
 
     rec("logprobs_fwd", 0)
@@ -127,8 +129,10 @@ PHASES = ["logprobs_fwd", "logprobs_bwd", "entropy_fwd", "entropy_bwd", "kl_ab_f
 
 
 def gpu_bench(wl, steps, warmup, device):
-    """Warm up, then time exactly `steps` steps (synchronised on both sides). HIP events
-    recorded on the kernels' stream inside the timed steps give the per-phase durations."""
+    """Warm up, then time exactly `steps` steps (synchronised on both sides). Inside the timed
+    steps HIP events bracket only the dominant kernel (the KL(A||B) backward), on the stream it is
+    launched on; a second, untimed pass of `steps` steps with events around every phase gives the
+    per-op breakdown (each event pair costs a few microseconds, so the timed steps carry only one)."""
     import torch
 
     from vocab_wide_softmax_amd import binding as B
@@ -138,19 +142,28 @@ def gpu_bench(wl, steps, warmup, device):
     log("inputs resident in HBM; %d warmup steps" % warmup)
     for _ in range(warmup):
         run_step(B, a, b, t, g)
-    evs = [{k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in PHASES}
-           for _ in range(steps)]
+
+    def events(keys):
+        return [{k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in keys}
+                for _ in range(steps)]
+
+    dom = events([DOM_PHASE])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        run_step(B, a, b, t, g, evs[i])
+        run_step(B, a, b, t, g, dom[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / steps
+    dom_ms = [ev[DOM_PHASE][0].elapsed_time(ev[DOM_PHASE][1]) for ev in dom]
+
+    evs = events(PHASES)
+    for i in range(steps):
+        run_step(B, a, b, t, g, evs[i])
+    torch.cuda.synchronize()
     per = {k: [ev[k][0].elapsed_time(ev[k][1]) for ev in evs] for k in PHASES}
     med = {k: sorted(v)[len(v) // 2] for k, v in per.items()}
-    mean = {k: sum(v) / len(v) for k, v in per.items()}
-    return ms_per_step, med, mean
+    return ms_per_step, med, sum(dom_ms) / len(dom_ms)
 
 
 # ------------------------------------------------------------------------- other ops
@@ -467,10 +480,9 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_rows)
         log("cpu baseline: %s GB/s on %d threads" % (cpu["value"], cpu["cores"]))
-    ms_per_step, med, mean = gpu_bench(wl, args.steps, args.warmup, device)
+    ms_per_step, med, dom_ms = gpu_bench(wl, args.steps, args.warmup, device)
     log("timed %d steps: %.3f ms/step" % (args.steps, ms_per_step))
     value = STEP_BYTES / (ms_per_step * 1e-3) / 1e9
-    dom_ms = (mean["kl_ab_bwd"] + mean["kl_ba_bwd"]) / 2.0
     achieved = DOMINANT_BYTES / (dom_ms * 1e-3) / 1e9
     ops = {}
     for op in ("logprobs", "entropy", "kl_ab", "kl_ba"):
@@ -497,7 +509,7 @@ def main():
                    "N": N_ROWS, "V": V, "step_bytes": STEP_BYTES},
         "pct_peak": round(100 * value / PEAK_GBS, 1),
         "ops": ops,
-        "roofline": {"bound": "hbm", "kernel": "bwd_kernel<KL,bf16> (" + DOMINANT + ")", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": "bwd_kernel<KL,bf16> (" + DOM_PHASE + ")", "achieved": round(achieved, 1),
                      "peak": PEAK_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": DOMINANT_BYTES,
                      "avg_launch_ms": round(dom_ms, 4)},
