@@ -203,3 +203,32 @@ def test_batch_invariant_split_depends_on_v_only(L):
     assert B.split_parts(0, 64, 75968) != B.split_parts(0, 8192, 75968)
     assert B.workspace_bytes(2, 8192, 75968, B.SPLIT_INVARIANT) == 8192 * 3 * 6 * 4
     assert L.vws_split_parts(0, 8, 100, -2) < 0
+
+
+def test_binding_rejects_host_tensors():
+    """The Python binding refuses host tensors before any pointer reaches the library."""
+    import torch
+
+    z = torch.zeros(4, 16, dtype=torch.bfloat16)
+    t = torch.zeros(4, dtype=torch.int64)
+    ids = torch.zeros(4, 3, dtype=torch.int64)
+    st2, st4, st6 = torch.zeros(4, 2), torch.zeros(4, 4), torch.zeros(4, 6)
+    g, v = torch.ones(4), torch.zeros(4)
+    h, W = torch.zeros(4, 8, dtype=torch.bfloat16), torch.zeros(16, 8, dtype=torch.bfloat16)
+    calls = [
+        lambda: B.logprobs_fwd(z, t),
+        lambda: B.logprobs_bwd(z, t, st2, g),
+        lambda: B.logprobs_topk_fwd(z, ids),
+        lambda: B.logprobs_topk_bwd(z, ids, st2, torch.ones(4, 3)),
+        lambda: B.entropy_fwd(z),
+        lambda: B.entropy_bwd(z, st2, v, g),
+        lambda: B.kl_fwd(z, z),
+        lambda: B.kl_bwd(z, z, st4, v, g),
+        lambda: B.jsd_fwd(z, z, 0.5),
+        lambda: B.jsd_bwd(z, z, 0.5, st6, v, g),
+        lambda: B.linear_logp_fwd(h, W, t),
+        lambda: B.linear_logp_bwd(h, W, t, st2, g),
+    ]
+    for call in calls:
+        with pytest.raises(ValueError, match="GPU tensors"):
+            call()

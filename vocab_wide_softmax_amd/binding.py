@@ -2,8 +2,10 @@
 
 Every step of the computation runs in the HIP kernels of libvws.so; this
 module turns torch tensors into the C descriptors, allocates outputs (torch
-owns device memory), passes torch's current HIP stream, and raises
-``VwsError`` on a non-zero status. There is no fallback: if libvws.so is
+owns device memory), passes torch's current HIP stream of the tensors' GPU
+(with that GPU made current for the call), and raises ``VwsError`` on a
+non-zero status. Tensors on the host or on different GPUs raise ValueError
+before any pointer reaches the library. There is no fallback: if libvws.so is
 missing or fails to load, the first call raises.
 
 Layouts: logits are [N, V] or [B, S, V] tensors whose last dimension is
@@ -197,32 +199,53 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _device(*tensors):
+    """The one GPU every given tensor lives on. Host tensors are rejected here, before any
+    pointer reaches the library (a host pointer in a kernel would be a memory fault)."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libvws takes GPU tensors; got a tensor on %s" % t.device)
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors on different devices: %s and %s" % (dev, t.device))
+    return dev
+
+
 # ------------------------------------------------------------------- entry points
 
 def logprobs_fwd(z, t, ignore_index=-100, split_hint=0):
     """(logp fp32 [N...], stats fp32 [N, 2]) -- vws_logprobs_fwd."""
+    dev = _device(z, t)
     L = lib()
     logp, stats = _outputs(z, 2)
     ws, nb = _workspace(OP_LOGPROBS, z, split_hint)
     r, ti = rows(z), ids(t, z)
-    _check("vws_logprobs_fwd", L.vws_logprobs_fwd(ctypes.byref(r), ctypes.byref(ti), ignore_index, _ptr(logp),
-                                                  _ptr(stats), _ptr(ws), nb, split_hint, _stream(z.device)))
+    with torch.cuda.device(dev):
+        _check("vws_logprobs_fwd", L.vws_logprobs_fwd(ctypes.byref(r), ctypes.byref(ti), ignore_index, _ptr(logp),
+                                                      _ptr(stats), _ptr(ws), nb, split_hint, _stream(dev)))
     return logp, stats
 
 
 def logprobs_bwd(z, t, stats, g, ignore_index=-100):
     """dz [shape of z, contiguous, dtype of z] -- vws_logprobs_bwd."""
+    dev = _device(z, t, stats, g)
     L = lib()
     g, gs = _g_arg(g, z)
     dz = torch.empty(z.shape, dtype=z.dtype, device=z.device)
     r, ti = rows(z), ids(t, z)
-    _check("vws_logprobs_bwd", L.vws_logprobs_bwd(ctypes.byref(r), ctypes.byref(ti), ignore_index, _ptr(stats),
-                                                  _ptr(g), gs, _ptr(dz), _stream(z.device)))
+    with torch.cuda.device(dev):
+        _check("vws_logprobs_bwd", L.vws_logprobs_bwd(ctypes.byref(r), ctypes.byref(ti), ignore_index, _ptr(stats),
+                                                      _ptr(g), gs, _ptr(dz), _stream(dev)))
     return dz
 
 
 def logprobs_topk_fwd(z, ids, ignore_index=-100, split_hint=0):
     """(logp fp32 [N..., K], stats fp32 [N, 2]) for K ids per row -- vws_logprobs_topk_fwd."""
+    dev = _device(z, ids)
     L = lib()
     ti = ids_k(ids, z)
     n = _n_rows(z)
@@ -230,14 +253,16 @@ def logprobs_topk_fwd(z, ids, ignore_index=-100, split_hint=0):
     stats = torch.empty((n, 2), dtype=torch.float32, device=z.device)
     ws, nb = _workspace(OP_LOGPROBS, z, split_hint)
     r = rows(z)
-    _check("vws_logprobs_topk_fwd", L.vws_logprobs_topk_fwd(ctypes.byref(r), ctypes.byref(ti), ignore_index,
-                                                            _ptr(logp), _ptr(stats), _ptr(ws), nb, split_hint,
-                                                            _stream(z.device)))
+    with torch.cuda.device(dev):
+        _check("vws_logprobs_topk_fwd", L.vws_logprobs_topk_fwd(ctypes.byref(r), ctypes.byref(ti), ignore_index,
+                                                                _ptr(logp), _ptr(stats), _ptr(ws), nb, split_hint,
+                                                                _stream(dev)))
     return logp, stats
 
 
 def logprobs_topk_bwd(z, ids, stats, g, ignore_index=-100):
     """dz [shape of z, contiguous, dtype of z] of sum g * logp over the K slots -- vws_logprobs_topk_bwd."""
+    dev = _device(z, ids, stats, g)
     L = lib()
     ti = ids_k(ids, z)
     n = _n_rows(z)
@@ -250,77 +275,90 @@ def logprobs_topk_bwd(z, ids, stats, g, ignore_index=-100):
         gs_r, gs_k = g.stride(0), g.stride(1)
     dz = torch.empty(z.shape, dtype=z.dtype, device=z.device)
     r = rows(z)
-    _check("vws_logprobs_topk_bwd", L.vws_logprobs_topk_bwd(ctypes.byref(r), ctypes.byref(ti), ignore_index,
-                                                            _ptr(stats), _ptr(g), gs_r, gs_k, _ptr(dz),
-                                                            _stream(z.device)))
+    with torch.cuda.device(dev):
+        _check("vws_logprobs_topk_bwd", L.vws_logprobs_topk_bwd(ctypes.byref(r), ctypes.byref(ti), ignore_index,
+                                                                _ptr(stats), _ptr(g), gs_r, gs_k, _ptr(dz),
+                                                                _stream(dev)))
     return dz
 
 
 def entropy_fwd(z, split_hint=0):
     """(H fp32 [N...], stats fp32 [N, 2]) -- vws_entropy_fwd."""
+    dev = _device(z)
     L = lib()
     H, stats = _outputs(z, 2)
     ws, nb = _workspace(OP_ENTROPY, z, split_hint)
     r = rows(z)
-    _check("vws_entropy_fwd", L.vws_entropy_fwd(ctypes.byref(r), _ptr(H), _ptr(stats), _ptr(ws), nb, split_hint,
-                                                _stream(z.device)))
+    with torch.cuda.device(dev):
+        _check("vws_entropy_fwd", L.vws_entropy_fwd(ctypes.byref(r), _ptr(H), _ptr(stats), _ptr(ws), nb, split_hint,
+                                                    _stream(dev)))
     return H, stats
 
 
 def entropy_bwd(z, stats, H, g):
     """dz -- vws_entropy_bwd."""
+    dev = _device(z, stats, H, g)
     L = lib()
     g, gs = _g_arg(g, z)
     dz = torch.empty(z.shape, dtype=z.dtype, device=z.device)
     r = rows(z)
-    _check("vws_entropy_bwd", L.vws_entropy_bwd(ctypes.byref(r), _ptr(stats), _ptr(H), _ptr(g), gs, _ptr(dz),
-                                                _stream(z.device)))
+    with torch.cuda.device(dev):
+        _check("vws_entropy_bwd", L.vws_entropy_bwd(ctypes.byref(r), _ptr(stats), _ptr(H), _ptr(g), gs, _ptr(dz),
+                                                    _stream(dev)))
     return dz
 
 
 def kl_fwd(a, b, split_hint=0):
     """(KL(A||B) fp32 [N...], stats fp32 [N, 4]) -- vws_kl_fwd."""
+    dev = _device(a, b)
     L = lib()
     kl, stats = _outputs(a, 4)
     ws, nb = _workspace(OP_KL, a, split_hint)
     ra, rb = rows(a), rows(b)
-    _check("vws_kl_fwd", L.vws_kl_fwd(ctypes.byref(ra), ctypes.byref(rb), _ptr(kl), _ptr(stats), _ptr(ws), nb,
-                                      split_hint, _stream(a.device)))
+    with torch.cuda.device(dev):
+        _check("vws_kl_fwd", L.vws_kl_fwd(ctypes.byref(ra), ctypes.byref(rb), _ptr(kl), _ptr(stats), _ptr(ws), nb,
+                                          split_hint, _stream(dev)))
     return kl, stats
 
 
 def kl_bwd(a, b, stats, kl, g, need_a=True, need_b=True):
     """(da or None, db or None) -- vws_kl_bwd."""
+    dev = _device(a, b, stats, kl, g)
     L = lib()
     g, gs = _g_arg(g, a)
     da = torch.empty(a.shape, dtype=a.dtype, device=a.device) if need_a else None
     db = torch.empty(b.shape, dtype=b.dtype, device=b.device) if need_b else None
     ra, rb = rows(a), rows(b)
-    _check("vws_kl_bwd", L.vws_kl_bwd(ctypes.byref(ra), ctypes.byref(rb), _ptr(stats), _ptr(kl), _ptr(g), gs,
-                                      _ptr(da), _ptr(db), _stream(a.device)))
+    with torch.cuda.device(dev):
+        _check("vws_kl_bwd", L.vws_kl_bwd(ctypes.byref(ra), ctypes.byref(rb), _ptr(stats), _ptr(kl), _ptr(g), gs,
+                                          _ptr(da), _ptr(db), _stream(dev)))
     return da, db
 
 
 def jsd_fwd(s, t, beta=0.5, split_hint=0):
     """(JSD fp32 [N...], stats fp32 [N, 6]) of student s and teacher t -- vws_jsd_fwd."""
+    dev = _device(s, t)
     L = lib()
     out, stats = _outputs(s, 6)
     ws, nb = _workspace(OP_JSD, s, split_hint)
     rs, rt = rows(s), rows(t)
-    _check("vws_jsd_fwd", L.vws_jsd_fwd(ctypes.byref(rs), ctypes.byref(rt), float(beta), _ptr(out), _ptr(stats),
-                                        _ptr(ws), nb, split_hint, _stream(s.device)))
+    with torch.cuda.device(dev):
+        _check("vws_jsd_fwd", L.vws_jsd_fwd(ctypes.byref(rs), ctypes.byref(rt), float(beta), _ptr(out), _ptr(stats),
+                                            _ptr(ws), nb, split_hint, _stream(dev)))
     return out, stats
 
 
 def jsd_bwd(s, t, beta, stats, out, g, need_s=True, need_t=True):
     """(ds or None, dt or None) -- vws_jsd_bwd."""
+    dev = _device(s, t, stats, out, g)
     L = lib()
     g, gs = _g_arg(g, s)
     ds = torch.empty(s.shape, dtype=s.dtype, device=s.device) if need_s else None
     dt = torch.empty(t.shape, dtype=t.dtype, device=t.device) if need_t else None
     rs, rt = rows(s), rows(t)
-    _check("vws_jsd_bwd", L.vws_jsd_bwd(ctypes.byref(rs), ctypes.byref(rt), float(beta), _ptr(stats), _ptr(out),
-                                        _ptr(g), gs, _ptr(ds), _ptr(dt), _stream(s.device)))
+    with torch.cuda.device(dev):
+        _check("vws_jsd_bwd", L.vws_jsd_bwd(ctypes.byref(rs), ctypes.byref(rt), float(beta), _ptr(stats), _ptr(out),
+                                            _ptr(g), gs, _ptr(ds), _ptr(dt), _stream(dev)))
     return ds, dt
 
 
@@ -346,6 +384,7 @@ def linear_workspace_bytes(pass_, n, hidden, v):
 
 def linear_logp_fwd(h, W, t, ignore_index=-100):
     """(logp fp32 [N], stats fp32 [N, 2]) of the target under logits h W^T -- vws_linear_logp_fwd."""
+    dev = _device(h, W, t)
     L = lib()
     _lin_check(h, W, t)
     n, hidden = h.shape
@@ -354,14 +393,16 @@ def linear_logp_fwd(h, W, t, ignore_index=-100):
     stats = torch.empty((n, 2), dtype=torch.float32, device=h.device)
     nb = linear_workspace_bytes(0, n, hidden, v)
     ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=h.device)
-    _check("vws_linear_logp_fwd", L.vws_linear_logp_fwd(h.data_ptr(), h.stride(0), W.data_ptr(), W.stride(0),
-                                                        VWS_BF16, n, hidden, v, t.data_ptr(), ignore_index,
-                                                        _ptr(logp), _ptr(stats), _ptr(ws), nb, _stream(h.device)))
+    with torch.cuda.device(dev):
+        _check("vws_linear_logp_fwd", L.vws_linear_logp_fwd(h.data_ptr(), h.stride(0), W.data_ptr(), W.stride(0),
+                                                            VWS_BF16, n, hidden, v, t.data_ptr(), ignore_index,
+                                                            _ptr(logp), _ptr(stats), _ptr(ws), nb, _stream(dev)))
     return logp, stats
 
 
 def linear_logp_bwd(h, W, t, stats, g, ignore_index=-100, need_h=True, need_w=True):
     """(dh bf16 [N, H] or None, dW bf16 [V, H] or None) -- vws_linear_logp_bwd."""
+    dev = _device(h, W, t, stats, g)
     L = lib()
     _lin_check(h, W, t)
     n, hidden = h.shape
@@ -371,8 +412,9 @@ def linear_logp_bwd(h, W, t, stats, g, ignore_index=-100, need_h=True, need_w=Tr
     dW = torch.empty((v, hidden), dtype=torch.bfloat16, device=h.device) if need_w else None
     nb = linear_workspace_bytes(1, n, hidden, v)
     ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=h.device)
-    _check("vws_linear_logp_bwd", L.vws_linear_logp_bwd(h.data_ptr(), h.stride(0), W.data_ptr(), W.stride(0),
-                                                        VWS_BF16, n, hidden, v, t.data_ptr(), ignore_index,
-                                                        _ptr(stats), _ptr(g), gs, _ptr(dh), _ptr(dW), _ptr(ws), nb,
-                                                        _stream(h.device)))
+    with torch.cuda.device(dev):
+        _check("vws_linear_logp_bwd", L.vws_linear_logp_bwd(h.data_ptr(), h.stride(0), W.data_ptr(), W.stride(0),
+                                                            VWS_BF16, n, hidden, v, t.data_ptr(), ignore_index,
+                                                            _ptr(stats), _ptr(g), gs, _ptr(dh), _ptr(dW), _ptr(ws), nb,
+                                                            _stream(dev)))
     return dh, dW
