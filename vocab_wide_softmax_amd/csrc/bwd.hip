@@ -99,7 +99,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_kernel(BwdArgs p) {
   const int32_t G = (V + 7) / 8;
   const int32_t g_full = VEC ? V / 8 : 0;  // groups below this use 16-byte loads and stores
   for (int64_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
-    const int64_t row = vb / tpr;
+    const int64_t row = udiv(vb, tpr);
     const int32_t tile = (int32_t)(vb - row * tpr);
     const int32_t g0 = tile * (BLOCK * UB);
     RowBwd r;

@@ -292,14 +292,22 @@ struct IdsDev {
   int64_t s_outer, s_inner;
 };
 
+// a / b for a >= 0 and b >= 1. The callers' operands are almost always wave-uniform and
+// below 2^32, where the 32-bit sequence replaces the much longer 64-bit one.
+__device__ __forceinline__ int64_t udiv(int64_t a, int64_t b) {
+  if (b == 1) return a;
+  if (((uint64_t)a | (uint64_t)b) <= 0xffffffffull) return (int64_t)((uint32_t)a / (uint32_t)b);
+  return a / b;
+}
+
 template <int DT>
 __device__ __forceinline__ const char* row_ptr(const RowsDev& r, int64_t row) {
-  const int64_t ro = row / r.n_inner, ri = row - ro * r.n_inner;
+  const int64_t ro = udiv(row, r.n_inner), ri = row - ro * r.n_inner;
   return r.data + (ro * r.s_outer + ri * r.s_inner) * ElemSize<DT>::value;
 }
 
 __device__ __forceinline__ int64_t load_id(const IdsDev& t, int64_t row, int64_t n_inner) {
-  const int64_t ro = row / n_inner, ri = row - ro * n_inner;
+  const int64_t ro = udiv(row, n_inner), ri = row - ro * n_inner;
   return t.data[ro * t.s_outer + ri * t.s_inner];
 }
 

@@ -156,7 +156,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs p) {
   const int32_t parts = p.parts;
   const int64_t total = p.N * parts;
   for (int64_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
-  const int64_t row = vb / parts;
+  const int64_t row = udiv(vb, parts);
   const int32_t part = (int32_t)(vb - row * parts);
   const int32_t G = (int32_t)((p.V + 7) / 8);
   const int32_t g_full = (int32_t)(p.V / 8);

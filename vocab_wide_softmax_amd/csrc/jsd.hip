@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kJsdBlock) void jsd_div_kernel(JsdArgs p) {
   const int32_t g_full = VEC ? (int32_t)(p.V / 8) : 0;
   const int32_t V = (int32_t)p.V;
   for (int64_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
-    const int64_t row = vb / parts;
+    const int64_t row = udiv(vb, parts);
     const int32_t part = (int32_t)(vb - row * parts);
     const int32_t g0 = part * p.groups_per_part;
     const int32_t g1 = min(G, g0 + p.groups_per_part);
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kJsdBlock) void jsd_bwd_kernel(JsdArgs p) {
   const int32_t G = (V + 7) / 8;
   const int32_t g_full = VEC ? V / 8 : 0;
   for (int64_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
-    const int64_t row = vb / tpr;
+    const int64_t row = udiv(vb, tpr);
     const int32_t tile = (int32_t)(vb - row * tpr);
     const int32_t g0 = tile * (kJsdBlock * kJsdUB);
     const float* st = p.stats + 6 * row;

@@ -28,7 +28,7 @@ constexpr int kTopkUB = 4;  // groups of 8 columns per lane per tile (8192-colum
 }  // namespace
 
 __device__ __forceinline__ int64_t topk_id(const TopkArgs& p, int64_t row, int32_t k) {
-  const int64_t ro = row / p.a.n_inner, ri = row - ro * p.a.n_inner;
+  const int64_t ro = udiv(row, p.a.n_inner), ri = row - ro * p.a.n_inner;
   return p.ids[ro * p.ids_so + ri * p.ids_si + (int64_t)k * p.ids_sk];
 }
 
@@ -36,7 +36,7 @@ template <int DT>
 __global__ __launch_bounds__(256) void topk_gather_kernel(TopkArgs p) {
   const int64_t total = p.N * p.K;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    const int64_t row = i / p.K;
+    const int64_t row = udiv(i, p.K);
     const int32_t k = (int32_t)(i - row * p.K);
     const int64_t t = topk_id(p, row, k);
     float out;
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kTopkBlock) void topk_bwd_kernel(TopkArgs p) {
   const int32_t G = (V + 7) / 8;
   const int32_t g_full = VEC ? V / 8 : 0;
   for (int64_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
-    const int64_t row = vb / tpr;
+    const int64_t row = udiv(vb, tpr);
     const int32_t tile = (int32_t)(vb - row * tpr);
     const int32_t g0 = tile * (kTopkBlock * UB);
     const int32_t c0 = g0 * 8, c1 = min(V, c0 + kTopkBlock * UB * 8);
