@@ -189,7 +189,7 @@ def _timed(fwd, bwd, steps, warmup):
     return sorted(f)[steps // 2], sorted(b)[steps // 2]
 
 
-def extras_bench(wl, device, steps=7, warmup=2):
+def extras_bench(wl, device, steps=10, warmup=5):
     """The other ops on the same 8192 x 75968 pair, each fwd+bwd, with their algorithmic bytes:
     top-k logprobs (K = 16 ids per row), the generalized JSD (beta = 0.5: two reads of both
     inputs forward, one read of both and two writes backward), the four-op step on fp16 copies

@@ -140,13 +140,16 @@ __global__ __launch_bounds__(kTopkBlock) void topk_bwd_kernel(TopkArgs p) {
       int32_t col = 0;
       float gk = 0.0f;
       if (k < p.K) {
+        // the id and its upstream gradient are loaded together (both exist for every slot),
+        // so the gradient's latency does not follow the id's
         const int64_t t = topk_id(p, row, k);
+        const float gl = p.g[row * p.g_sr + (int64_t)k * p.g_sk];
         if (t != p.ignore_index) {
           flags |= 1;
           if (t < 0 || t >= V) {
             flags |= 2;
           } else {
-            gk = p.g[row * p.g_sr + (int64_t)k * p.g_sk];
+            gk = gl;
             gpart += gk;
             hit = t >= c0 && t < c1;
             col = (int32_t)(t - c0);
