@@ -189,38 +189,50 @@ __global__ __launch_bounds__(C::NT) void lin_dz_kernel(LinArgs p) {
   const int wm = wave / C::WN, wn = wave % C::WN;
   const Operand A{p.h, p.ldh, p.N, p.H};
   const Operand B{p.W, p.ldw, p.V, p.H};
-  Acc<C> acc;
-  gemm::mainloop<C>(A, B, m0, n0, p.H, lds, acc);
-  // per-token constants of this tile into LDS: m, log S, g, target
-  float* cst = reinterpret_cast<float*>(lds);
-  int64_t* tgt = reinterpret_cast<int64_t*>(lds + C::BM * 3 * sizeof(float));
-  for (int r = threadIdx.x; r < C::BM; r += C::NT) {
-    const int64_t n = m0 + r < p.N ? m0 + r : p.N - 1;
-    cst[3 * r + 0] = p.stats[2 * n];
-    cst[3 * r + 1] = p.stats[2 * n + 1];
-    cst[3 * r + 2] = p.g[n * p.g_stride];
-    tgt[r] = p.t[n];
+  // This tile's per-token constants, read before the main loop so that their latency is
+  // hidden behind it: m, log S, the upstream gradient (NaN when the target is out of range,
+  // which makes the whole row NaN) and the target's column inside the tile (-1 when it lies
+  // in another tile, -2 for an ignored token, whose row is zero).
+  f32x4 rowc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (threadIdx.x < C::BM) {
+    const int64_t n = m0 + threadIdx.x < p.N ? m0 + threadIdx.x : p.N - 1;
+    const int64_t t = p.t[n];
+    const float m = p.stats[2 * n], ls = p.stats[2 * n + 1], gv = p.g[n * p.g_stride];
+    const bool ignored = t == p.ignore_index, bad = !ignored && (t < 0 || t >= p.V);
+    const int32_t tc = ignored ? -2 : (t >= n0 && t < n0 + C::BN ? (int32_t)(t - n0) : -1);
+    rowc = (f32x4){m, ls, bad ? __builtin_nanf("") : gv, __int_as_float(tc)};
   }
+  Acc<C> acc;
+  gemm::mainloop<C>(A, B, m0, n0, p.H, lds, acc);  // ends with a barrier: LDS is free again
+  f32x4* cst = reinterpret_cast<f32x4*>(lds);
+  if (threadIdx.x < C::BM) cst[threadIdx.x] = rowc;
   __syncthreads();
+  // dz = g (1[v = t] - p) = fma(-g, p, g 1[v = t]); interior tiles store without guards.
+  const bool interior = m0 + C::BM <= p.N && n0 + C::BN <= p.V;
+  uint16_t* tile = p.dz + m0 * p.ldz + n0;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int r = wm * C::TM + gemm::acc_row(i, v, lane);
-      const int64_t n = m0 + r;
-      const float m = cst[3 * r], ls = cst[3 * r + 1], gv = cst[3 * r + 2];
-      const int64_t t = tgt[r];
-      const bool ignored = t == p.ignore_index, bad = !ignored && (t < 0 || t >= p.V);
+      const f32x4 c = cst[r];
+      const float m = c.x, ls = c.y, gv = c.z;
+      const int32_t tc = __float_as_int(c.w);
+      uint16_t* rowp = tile + (int64_t)r * p.ldz;
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
-        const int64_t col = n0 + wn * C::TN + gemm::acc_col(j, lane);
+        const int lc = wn * C::TN + gemm::acc_col(j, lane);
         const float pz = expf_fast((acc.c[i][j][v] - m) - ls);
-        float d = (col == t) ? gv * (1.0f - pz) : -gv * pz;
-        d = ignored ? 0.0f : (bad ? __builtin_nanf("") : d);
-        d = col < p.V ? d : 0.0f;  // columns [V, ldz) pad the rows with zeros for the dh contraction
-        if (n < p.N && col < p.ldz) {
-          const bf16x2 hb = __builtin_convertvector((f32x2){d, 0.0f}, bf16x2);
-          p.dz[n * p.ldz + col] = (uint16_t)(__builtin_bit_cast(uint32_t, hb) & 0xffffu);
+        float d = __builtin_fmaf(-gv, pz, lc == tc ? gv : 0.0f);
+        d = tc == -2 ? 0.0f : d;
+        const bf16x2 hb = __builtin_convertvector((f32x2){d, 0.0f}, bf16x2);
+        const uint16_t bits = (uint16_t)(__builtin_bit_cast(uint32_t, hb) & 0xffffu);
+        if (interior) {
+          rowp[lc] = bits;
+        } else {
+          // columns [V, ldz) pad the rows with zeros for the dh contraction
+          const int64_t col = n0 + lc;
+          if (m0 + r < p.N && col < p.ldz) rowp[lc] = col < p.V ? bits : (uint16_t)0;
         }
       }
     }
