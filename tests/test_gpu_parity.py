@@ -9,7 +9,8 @@ Workloads (vocab_wide_softmax_amd.workloads):
             columns): every element of every output and gradient; the
             automatic launch splits the vocabulary here.
 * pair8192  8192 x 75968 bf16 pair: the full launch the benchmark times,
-            checked on sampled rows (row 0, offset rows, masked rows, random).
+            checked on sampled rows (row 0, offset rows, masked rows, random),
+            for the four ops and for top-k logprobs (K = 16) and the JSD.
 * shifted   [4, 2049, 75968] fp32 pair read through base[:, :-1, :]: the full
             in-place strided launch, checked on sampled rows.
 """
@@ -121,10 +122,59 @@ def run_device_sampled(op, a, b, t, g, idx):
     return res
 
 
+@pytest.fixture(scope="module")
+def pair8192():
+    return W.workload("pair8192")
+
+
 @pytest.mark.slow
-def test_pair8192_sampled_rows(device):
-    wl = W.workload("pair8192")
-    _sampled_parity(wl, device, OPS, "bf16")
+def test_pair8192_sampled_rows(device, pair8192):
+    _sampled_parity(pair8192, device, OPS, "bf16")
+
+
+@pytest.mark.slow
+def test_pair8192_topk_and_jsd_sampled_rows(device, pair8192):
+    """Top-k logprobs (K = 16) and the JSD at beta = 0.5 in the launch the benchmark times
+    (8192 rows: one workgroup per row, no vocabulary split), the same seeded ids and
+    upstream gradients, checked against the oracle on sampled rows."""
+    from oracle import compare, jsd as J, topk as TK
+
+    wl = pair8192
+    a, b, _ = _to_device(wl, device)
+    n, V = a.shape
+    assert B.split_parts(B.OP_LOGPROBS, n, V) == 1 and B.split_parts(B.OP_JSD, n, V) == 1
+    rows = _sample_rows(wl, n)
+    idx = torch.from_numpy(rows).to(device)
+    ids = torch.randint(0, V, (n, 16), generator=torch.Generator().manual_seed(5))
+    ids[rows[1], 3] = ids[rows[1], 2]  # a duplicate id in a sampled row
+    ids[rows[2], :] = -100  # a fully ignored sampled row
+    gk = torch.randn(n, 16, generator=torch.Generator().manual_seed(6))
+    trows = torch.from_numpy(rows)
+    ha, hb = f64(wl.a[trows]), f64(wl.b[trows])
+    print("pair8192 topk16", flush=True)
+    di, dg = ids.to(device), gk.to(device)
+    lp, st = B.logprobs_topk_fwd(a, di, -100)
+    dz = B.logprobs_topk_bwd(a, di, st, dg, -100)
+    hi, hg = ids.numpy()[rows], gk.double().numpy()[rows]
+    rep = compare.check(f64(lp[idx]), TK.logprobs_topk_fwd(ha, hi)[0], TK.cond_logprobs_topk_fwd(ha, hi), "f32")
+    assert rep["fail"] == 0 and rep["nan_mismatch"] == 0, rep
+    rep = compare.check(f64(dz[idx]), TK.logprobs_topk_bwd(ha, hi, hg), TK.cond_logprobs_topk_bwd(ha, hi, hg), "bf16")
+    assert rep["fail"] == 0 and rep["nan_mismatch"] == 0, rep
+    del dz, lp, st
+    print("pair8192 jsd0.5", flush=True)
+    g = wl.g["kl_ab"]
+    out, st = B.jsd_fwd(a, b, 0.5)
+    ds, dt = B.jsd_bwd(a, b, 0.5, st, out, g.to(device))
+    hgj = g.double().numpy()[rows]
+    rep = compare.check(f64(out[idx]), J.jsd_fwd(ha, hb, 0.5)[0], J.cond_jsd_fwd(ha, hb, 0.5), "f32")
+    assert rep["fail"] == 0 and rep["nan_mismatch"] == 0, rep
+    rs, rt = J.jsd_bwd(ha, hb, hgj, 0.5)
+    cs, ct = J.cond_jsd_bwd(ha, hb, hgj, 0.5)
+    for x, y, c in ((ds, rs, cs), (dt, rt, ct)):
+        rep = compare.check(f64(x[idx]), y, c, "bf16")
+        assert rep["fail"] == 0 and rep["nan_mismatch"] == 0, rep
+    del ds, dt, out, st
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.slow
