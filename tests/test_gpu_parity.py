@@ -10,7 +10,8 @@ Workloads (vocab_wide_softmax_amd.workloads):
             automatic launch splits the vocabulary here.
 * pair8192  8192 x 75968 bf16 pair: the full launch the benchmark times,
             checked on sampled rows (row 0, offset rows, masked rows, random),
-            for the four ops and for top-k logprobs (K = 16) and the JSD.
+            for the four ops (bf16 and the fp16 rounding of the pair) and for
+            top-k logprobs (K = 16) and the JSD.
 * shifted   [4, 2049, 75968] fp32 pair read through base[:, :-1, :]: the full
             in-place strided launch, checked on sampled rows.
 """
@@ -130,6 +131,16 @@ def pair8192():
 @pytest.mark.slow
 def test_pair8192_sampled_rows(device, pair8192):
     _sampled_parity(pair8192, device, OPS, "bf16")
+
+
+@pytest.mark.slow
+def test_pair8192_fp16_sampled_rows(device, pair8192):
+    """The same pair rounded to fp16, as in the benchmark's fp16 step (8192-row launch)."""
+    import dataclasses
+
+    wl = dataclasses.replace(pair8192, name="pair8192_fp16", a_base=pair8192.a_base.half(),
+                             b_base=pair8192.b_base.half())
+    _sampled_parity(wl, device, OPS, "f16")
 
 
 @pytest.mark.slow
