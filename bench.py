@@ -459,8 +459,8 @@ def main():
         counters(*args.counters)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: --gpus %d is not supported by this build (rows would shard across "
-              "GPUs with no communication; the one-GPU figure is each GPU's share). Use --gpus 1." % args.gpus,
+        print("bench.py measures one GPU only; --gpus %d is not supported (rows would shard across GPUs with "
+              "no communication, so the one-GPU figure is each GPU's share). Use --gpus 1." % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
