@@ -232,3 +232,17 @@ def test_binding_rejects_host_tensors():
     for call in calls:
         with pytest.raises(ValueError, match="GPU tensors"):
             call()
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without libvws.so every entry point raises: there is no CPU or PyTorch fallback."""
+    import torch
+
+    monkeypatch.setattr(B, "_LIB_PATH", os.path.join(ROOT, "no_such_dir", "libvws.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(ImportError, match="not built"):
+        B.lib()
+    if torch.cuda.is_available():  # on a GPU machine the call itself must raise too
+        z = torch.zeros(4, 16, dtype=torch.bfloat16, device="cuda:0")
+        with pytest.raises(ImportError):
+            B.entropy_fwd(z)
