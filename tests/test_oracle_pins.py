@@ -399,3 +399,147 @@ def test_pins_catch_planted_mistakes():
     dh = linear_logp.linear_logp_bwd_dh(h, W, tt, gg)
     dh_wrong = R.logprobs_bwd(h @ W.T, tt, gg) @ W.T
     assert not np.allclose(dh, dh_wrong)
+
+
+# ------------------------------------------------------ rounding-scale pins
+
+def test_condition_scales_closed_forms():
+    """The rounding scales of the parity rule on rows where every term is known by hand:
+    a uniform row (p = 1/V, z - m = 0, log S = log V, H = log V) and a two-level row."""
+    V, off, t = 7, 5.0, 3
+    z = np.full((1, V), off)
+    g = np.array([-2.0])
+    L = np.log(V)
+    assert np.isclose(R.cond_logprobs_fwd(z, np.array([t]))[0], L)
+    assert np.isclose(R.cond_entropy_fwd(z)[0], L)
+    assert np.isclose(R.cond_kl_fwd(z, z)[0], 2 * L)
+    cl = R.cond_logprobs_bwd(z, np.array([t]), g)[0]
+    want = 2.0 * (np.eye(V)[t] + (1.0 + L) / V)
+    np.testing.assert_allclose(cl, want, rtol=1e-13)
+    np.testing.assert_allclose(R.cond_entropy_bwd(z, g)[0], 2.0 * (1.0 + 2 * L) / V, rtol=1e-13)
+    ca, cb = R.cond_kl_bwd(z, z, g)
+    np.testing.assert_allclose(ca[0], 2.0 * (1.0 + 2 * L) / V, rtol=1e-13)
+    np.testing.assert_allclose(cb[0], 2.0 * 2 * (1.0 + L) / V, rtol=1e-13)
+    # two levels: z = (0, -1): m = 0, p = (1, e^-1) / (1 + e^-1), |z - m| = (0, 1)
+    z2 = np.array([[0.0, -1.0]])
+    S = 1.0 + np.exp(-1.0)
+    p1 = np.exp(-1.0) / S
+    assert np.isclose(R.cond_entropy_fwd(z2)[0], np.log(S) + p1)
+    assert np.isclose(R.cond_logprobs_fwd(z2, np.array([1]))[0], 1.0 + np.log(S))
+    # a KL pair with KL != 0: a = (0, -1), b = (-1, 0); both have log S = log(1 + e^-1),
+    # p_A = (1, e^-1) / S, p_B = (e^-1, 1) / S, KL = (1 - e^-1) / S
+    a2, b2 = np.array([[0.0, -1.0]]), np.array([[-1.0, 0.0]])
+    lS = np.log(S)
+    pa = np.array([1.0, np.exp(-1.0)]) / S
+    pb = pa[::-1]
+    kl = (1.0 - np.exp(-1.0)) / S
+    assert np.isclose(R.kl_fwd(a2, b2)[0][0], kl)
+    assert np.isclose(R.cond_kl_fwd(a2, b2)[0], 1.0 + 2 * lS)
+    ca, cb = R.cond_kl_bwd(a2, b2, np.array([0.5]))
+    np.testing.assert_allclose(ca[0], 0.5 * pa * (2.0 + 2 * lS + kl), rtol=1e-13)
+    np.testing.assert_allclose(cb[0], 0.5 * (pa * (1.0 + np.array([0.0, 1.0]) + lS) +
+                                             pb * (1.0 + np.array([1.0, 0.0]) + lS)), rtol=1e-13)
+    # masked entries add nothing
+    z3 = np.array([[0.0, -1.0, -np.inf]])
+    assert np.isclose(R.cond_entropy_fwd(z3)[0], np.log(S) + p1)
+    assert R.cond_entropy_bwd(z3, np.array([1.0]))[0, 2] == 0.0
+
+
+def test_condition_scales_keep_the_rule_tight():
+    """On realistic rows the rounding allowance stays far below the errors a wrong kernel
+    makes: every forward value off by 0.2% of max(|y|, 1) (KL near 0 is a difference of
+    terms of size log S, so its allowance is absolute) is rejected, the scales stay of the
+    order of log V, and a bf16 gradient entry off by 2 ulps is rejected wherever the
+    computation is not near a cancellation."""
+    rng = np.random.default_rng(11)
+    n, V = 16, 3000
+    a = 3.0 * rng.standard_normal((n, V))
+    b = a + 0.5 * rng.standard_normal((n, V))
+    a[0] += 1e4
+    b[0] += 1e4
+    t = rng.integers(0, V, n)
+    g = rng.standard_normal(n)
+    cases = [
+        (R.logprobs_fwd(a, t)[0], R.cond_logprobs_fwd(a, t)),
+        (R.entropy_fwd(a)[0], R.cond_entropy_fwd(a)),
+        (R.kl_fwd(a, b)[0], R.cond_kl_fwd(a, b)),
+    ]
+    for y, c in cases:
+        assert compare.check(y, y, c, "f32")["fail"] == 0
+        assert np.all(c < 4 * (np.log(V) + 30.0))
+        off = y + 2e-3 * np.maximum(np.abs(y), 1.0)
+        assert compare.check(off, y, c, "f32")["fail"] == n
+    # (gradient, scale, largest share of entries near a cancellation): the KL gradient
+    # w.r.t. A cancels wherever log p_A - log p_B is close to KL, which for B = A + noise is
+    # common, so only the logprobs and entropy shares are bounded
+    grads = [
+        (R.logprobs_bwd(a, t, g), R.cond_logprobs_bwd(a, t, g), 0.0),
+        (R.entropy_bwd(a, g), R.cond_entropy_bwd(a, g), 1e-3),
+        (R.kl_bwd(a, b, g)[0], R.cond_kl_bwd(a, b, g)[0], 1.0),
+        (R.kl_bwd(a, b, g)[1], R.cond_kl_bwd(a, b, g)[1], 1.0),
+    ]
+    for y, c, share in grads:
+        yb = compare.bf16_rne(y)
+        assert compare.check(yb, y, c, "bf16")["fail"] == 0
+        u = compare.ulp_bf16(yb)
+        live = np.abs(yb) > 1e-30
+        # entries near a cancellation may carry more than half an ulp of fp32 rounding;
+        # every other entry is held to one ulp
+        loose = live & (compare.COND * c >= 0.5 * u)  # 2 ulps off rne(y) is >= 1.5 ulps off y
+        assert loose.sum() <= share * live.sum()
+        tight = live & ~loose
+        off = np.where(live, yb + 2 * u * np.sign(yb), yb)
+        assert compare.check(off[tight], y[tight], c[tight], "bf16")["fail"] == int(tight.sum())
+
+
+def test_condition_scales_of_topk_jsd_and_linear():
+    """The rounding scales of the other oracles: top-k with one slot reduces to the single-id
+    scales and a duplicated id adds the slots' |g|; the JSD scales on an identical uniform
+    pair and their KL endpoints; the linear-logp scales on constant logits."""
+    from oracle import jsd as J, topk as TK
+
+    rng = np.random.default_rng(4)
+    z = 2.0 * rng.standard_normal((5, 40))
+    t = rng.integers(0, 40, 5)
+    g = rng.standard_normal(5)
+    np.testing.assert_allclose(TK.cond_logprobs_topk_fwd(z, t[:, None])[:, 0], R.cond_logprobs_fwd(z, t))
+    np.testing.assert_allclose(TK.cond_logprobs_topk_bwd(z, t[:, None], g[:, None]), R.cond_logprobs_bwd(z, t, g))
+    ids = np.stack([t, t], axis=1)
+    gg = np.stack([g, -0.5 * g], axis=1)
+    c2 = TK.cond_logprobs_topk_bwd(z, ids, gg)
+    c1 = R.cond_logprobs_bwd(z, t, 1.5 * np.abs(g))
+    np.testing.assert_allclose(c2, c1)  # |g1| + |g2| on the one-hot and on the softmax part
+    # JSD on s = t uniform over V: p = 1/V, log p = log M = -log V, no centring term, K = 0
+    V, beta = 9, 0.3
+    L = np.log(V)
+    u = np.zeros((1, V))
+    assert np.isclose(J.cond_jsd_fwd(u, u, beta)[0], 6 * L)
+    cs, ct = J.cond_jsd_bwd(u, u, np.array([2.0]), beta)
+    np.testing.assert_allclose(cs[0], 2.0 * (1 - beta) * (1 + 3 * L) / V, rtol=1e-13)
+    np.testing.assert_allclose(ct[0], 2.0 * beta * (1 + 3 * L) / V, rtol=1e-13)
+    np.testing.assert_allclose(J.cond_jsd_fwd(z, z[::-1], 0.0), R.cond_kl_fwd(z[::-1], z))
+    np.testing.assert_allclose(J.cond_jsd_fwd(z, z[::-1], 1.0), R.cond_kl_fwd(z, z[::-1]))
+    ks, kt = J.cond_jsd_bwd(z, z[::-1], g, 0.0)
+    rt, rs = R.cond_kl_bwd(z[::-1], z, g)
+    np.testing.assert_allclose(ks, rs)
+    np.testing.assert_allclose(kt, rt)
+    # linear-logp: W a column of ones (H = 1) makes every logit of token n equal to h_n
+    n, Vl = 4, 6
+    h = rng.standard_normal((n, 1))
+    W = np.ones((Vl, 1))
+    tl = np.array([0, 5, 2, -100])
+    gl = np.array([1.0, -2.0, 0.5, 3.0])
+    np.testing.assert_allclose(linear_logp.cond_logits(np.abs(h), W), np.abs(h) @ W.T)
+    cf = linear_logp.cond_linear_fwd(h, W, tl)
+    # |z_t - m| = 0, |log S| = log V, cz = |h_n| for every v, sum_v p_v cz_v = |h_n|
+    np.testing.assert_allclose(cf[:3], np.log(Vl) + 2 * np.abs(h[:3, 0]), rtol=1e-13)
+    np.testing.assert_allclose(cf[3], np.log(Vl) + np.abs(h[3, 0]), rtol=1e-13)
+    # dz = g (1[v = t] - 1/V): sum_v |dz_v| = 2 |g| (1 - 1/V); an ignored token adds nothing
+    cdh = linear_logp.cond_linear_dh(h, W, tl, gl)[:, 0]
+    np.testing.assert_allclose(cdh[:3], 2 * np.abs(gl[:3]) * (1 - 1 / Vl), rtol=1e-13)
+    assert cdh[3] == 0.0
+    cdw = linear_logp.cond_linear_dw(h, W, tl, gl)[:, 0]
+    want = np.zeros(Vl)
+    for i in range(3):
+        want += np.abs(gl[i]) * np.abs(h[i, 0]) * np.where(np.arange(Vl) == tl[i], 1 - 1 / Vl, 1 / Vl)
+    np.testing.assert_allclose(cdw, want, rtol=1e-13)
