@@ -34,9 +34,10 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kFltMin = 1.17549435e-38f;
 }  // namespace
 
-// Per-row constants: (m, log S) of both inputs, beta and 1 - beta.
+// Per-row constants: (m, log S) of both inputs, log S in base 2, beta and 1 - beta.
 struct JsdRow {
   float ms, lss, mt, lst;
+  float lss2, lst2;  // log S * log2 e
   float wt, ws;
   bool bad;
 };
@@ -47,6 +48,8 @@ __device__ __forceinline__ JsdRow jsd_row(const float* st4, float beta) {
   r.lss = st4[1];
   r.mt = st4[2];
   r.lst = st4[3];
+  r.lss2 = r.lss * kLog2e;
+  r.lst2 = r.lst * kLog2e;
   r.wt = beta;
   r.ws = 1.0f - beta;
   // a defined row has a finite max and a finite log S >= 0; an all -inf row has
@@ -70,8 +73,10 @@ __device__ __forceinline__ void jsd_group(const JsdRow& r, const float (&xs)[8],
   bool small = false;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    q.us[j] = ((xs[j] - r.ms) - r.lss) * kLog2e;
-    q.ut[j] = ((xt[j] - r.mt) - r.lst) * kLog2e;
+    // (z - m) log2 e - log2 S: the centred difference is exact for entries near the max,
+    // and the fma rounds once
+    q.us[j] = __builtin_fmaf(xs[j] - r.ms, kLog2e, -r.lss2);
+    q.ut[j] = __builtin_fmaf(xt[j] - r.mt, kLog2e, -r.lst2);
     q.ps[j] = __builtin_amdgcn_exp2f(q.us[j]);
     q.pt[j] = __builtin_amdgcn_exp2f(q.ut[j]);
     const float mix = __builtin_fmaf(r.wt, q.pt[j], r.ws * q.ps[j]);
