@@ -169,24 +169,26 @@ def gpu_bench(wl, steps, warmup, device):
 # ------------------------------------------------------------------------- other ops
 
 def _timed(fwd, bwd, steps, warmup):
-    """Median fwd and bwd milliseconds (HIP events on the current stream)."""
+    """Median fwd and bwd milliseconds (HIP events on the current stream). All steps are
+    enqueued before one synchronisation, so the host runs ahead and an event interval holds
+    the kernels only, not the host work of issuing them."""
     import torch
 
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         bwd(fwd())
-    f, b = [], []
-    for _ in range(steps):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in evs:
         e[0].record(stream)
         r = fwd()
         e[1].record(stream)
         bwd(r)
         e[2].record(stream)
-        torch.cuda.synchronize()
-        f.append(e[0].elapsed_time(e[1]))
-        b.append(e[1].elapsed_time(e[2]))
-    return sorted(f)[steps // 2], sorted(b)[steps // 2]
+    torch.cuda.synchronize()
+    f = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    b = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    return f[steps // 2], b[steps // 2]
 
 
 def extras_bench(wl, device, steps=10, warmup=5):
