@@ -135,6 +135,8 @@ def test_linear_validation(L):
                1 << 20, None) == 0  # no gradient requested
     assert bwd(0x1000, 64, 0x2000, 64, B.VWS_BF16, 4, 64, 100, 0x3000, -100, 0x5000, 0x7000, 1, 0x8000, None, 0x6000,
                16, None) == EWORKSPACE
+    # more (token, vocabulary) tiles than a launch can hold: rejected before any launch
+    assert fwd(N=1 << 31, V=(1 << 31) - 1, nb=1 << 62) == EINVAL
 
 
 def test_topk_validation(L):

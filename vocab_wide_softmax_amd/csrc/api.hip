@@ -259,6 +259,8 @@ int lin_check(const void* h, int64_t ldh, const void* W, int64_t ldw, int dtype,
   if (!aligned(h, 16) || !aligned(W, 16) || !aligned(t, 8)) return VWS_ELAYOUT;
   int64_t x;
   if (!mul_ok(N, ldh, &x) || !mul_ok(V, ldw, &x) || !mul_ok(N, round_up8(V), &x)) return VWS_EINVAL;
+  // the backward launches one workgroup per 256 x 256 (token, vocabulary) tile
+  if (((N + 255) / 256) * ((V + 255) / 256) > (int64_t)INT32_MAX) return VWS_EINVAL;
   return VWS_OK;
 }
 
