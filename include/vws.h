@@ -272,6 +272,8 @@ VWS_API int vws_jsd_bwd(const vws_rows* s, const vws_rows* t, float beta, const 
  *   ws      workspace of vws_linear_workspace_bytes(pass, N, H, V) bytes
  *           (pass 0: forward, 1: backward), 16-byte aligned
  * H must be a multiple of 8. h, W, dh, dW must be 16-byte aligned. dtype must be VWS_BF16.
+ * Sizes: N <= 2^31, H and V <= INT32_MAX, and ceil(N / 256) * ceil(V / 256) <= INT32_MAX
+ * (one backward workgroup per 256 x 256 tile); larger shapes give VWS_EINVAL.
  */
 VWS_API size_t vws_linear_workspace_bytes(int pass, int64_t N, int64_t H, int64_t V);
 
