@@ -29,25 +29,82 @@ struct RowBwd {
   int tj;
 };
 
-template <int OP, int DT, bool FULL>
-__device__ __forceinline__ void bwd_groups(const RowBwd& r, const char* ra, const char* rb, char* oa, char* ob,
-                                           int32_t g, int32_t stride, int n, int32_t G, int32_t V, int32_t g_full) {
+// The row's constants, loaded first so that the tile's loads issued after them stay in
+// flight while these are used; derived without branches.
+template <int OP>
+__device__ __forceinline__ RowBwd row_consts(const BwdArgs& p, int64_t row, int32_t V) {
+  RowBwd r;
+  r.gv = p.g[row * p.g_stride];
+  r.zero = false;
+  r.tg = -1;
+  r.tj = 0;
+  if constexpr (OP == kKL) {
+    r.m = p.stats[4 * row + 0];
+    r.ls = p.stats[4 * row + 1];
+    r.mb = p.stats[4 * row + 2];
+    r.lsb = p.stats[4 * row + 3];
+    r.res = p.res[row];
+    r.nan_a = !(r.res < kInf);  // +inf (support mismatch) or NaN
+    r.nan_b = r.res != r.res;
+  } else {
+    r.m = p.stats[2 * row + 0];
+    r.ls = p.stats[2 * row + 1];
+    r.mb = r.lsb = 0.0f;
+    r.nan_b = false;
+    if constexpr (OP == kEntropy) {
+      r.res = p.res[row];
+      r.nan_a = r.res != r.res;
+    } else {
+      r.res = 0.0f;
+      const int64_t t = load_id(p.ids, row, p.a.n_inner);
+      r.zero = t == p.ignore_index;
+      r.nan_a = !r.zero && (t < 0 || t >= V);
+      const bool ok = !r.zero && !r.nan_a;
+      r.tg = ok ? (int32_t)(t >> 3) : -1;
+      r.tj = ok ? (int)(t & 7) : 0;
+    }
+  }
+  return r;
+}
+
+// Issues the loads of this lane's UB groups (g, g + BLOCK, ...) of one row; groups past the
+// row end read as -inf and are not stored.
+template <int DT, bool FULL, int BLOCK, int UB>
+__device__ __forceinline__ void bwd_load(const char* row, int32_t g, int32_t G, int32_t V, int32_t g_full,
+                                         float (&x)[UB][8]) {
+#pragma unroll
+  for (int u = 0; u < UB; ++u, g += BLOCK) {
+    if (FULL) {
+      load_group_vec<DT>(row, g, x[u]);
+    } else if (g < G) {
+      load_group<DT, true>(row, g, V, g_full, x[u]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[u][j] = -kInf;
+    }
+  }
+}
+
+// The B tile of KL, or (unused) the A tile for the single-input ops.
+template <int OP, int UB, int NB>
+__device__ __forceinline__ const float (&xb_ref(const float (&xa)[UB][8], const float (&xb)[NB][8]))[UB][8] {
+  if constexpr (OP == kKL) return xb;
+  else return xa;
+}
+
+template <int OP, int DT, bool FULL, int BLOCK, int UB>
+__device__ __forceinline__ void bwd_store(const RowBwd& r, const float (&xa)[UB][8], const float (&xb)[UB][8],
+                                          char* oa, char* ob, int32_t g, int32_t G, int32_t V, int32_t g_full) {
   const float qnan = __builtin_nanf("");
-  for (int k = 0; k < n; ++k, g += stride) {
+#pragma unroll
+  for (int u = 0; u < UB; ++u, g += BLOCK) {
     if (!FULL && g >= G) break;
     if constexpr (OP == kKL) {
-      float xa[8], xb[8], ya[8], yb[8];
-      if (FULL) {
-        load_group_vec<DT>(ra, g, xa);
-        load_group_vec<DT>(rb, g, xb);
-      } else {
-        load_group<DT, true>(ra, g, V, g_full, xa);
-        load_group<DT, true>(rb, g, V, g_full, xb);
-      }
+      float ya[8], yb[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float ua = (xa[j] - r.m) - r.ls;
-        const float ub = (xb[j] - r.mb) - r.lsb;
+        const float ua = (xa[u][j] - r.m) - r.ls;
+        const float ub = (xb[u][j] - r.mb) - r.lsb;
         const float pa = expf_fast(ua);
         const float pb = expf_fast(ub);
         ya[j] = r.nan_a ? qnan : mul0(pa, (ua - ub) - r.res) * r.gv;
@@ -61,21 +118,19 @@ __device__ __forceinline__ void bwd_groups(const RowBwd& r, const char* ra, cons
         if (ob) store_group<DT, true>(ob, g, V, g_full, yb);
       }
     } else {
-      float x[8], y[8];
-      if (FULL) load_group_vec<DT>(ra, g, x);
-      else load_group<DT, true>(ra, g, V, g_full, x);
+      float y[8];
       if constexpr (OP == kEntropy) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float u = (x[j] - r.m) - r.ls;  // log p_j
-          const float pj = expf_fast(u);
-          y[j] = r.nan_a ? qnan : mul0(pj, u + r.res) * (-r.gv);
+          const float lp = (xa[u][j] - r.m) - r.ls;  // log p_j
+          const float pj = expf_fast(lp);
+          y[j] = r.nan_a ? qnan : mul0(pj, lp + r.res) * (-r.gv);
         }
       } else {
         float pr[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          pr[j] = expf_fast((x[j] - r.m) - r.ls);
+          pr[j] = expf_fast((xa[u][j] - r.m) - r.ls);
           y[j] = r.zero ? 0.0f : (r.nan_a ? qnan : -r.gv * pr[j]);
         }
         if (g == r.tg) {
@@ -102,61 +157,48 @@ __global__ __launch_bounds__(BLOCK) void bwd_kernel(BwdArgs p) {
     const int64_t row = udiv(vb, tpr);
     const int32_t tile = (int32_t)(vb - row * tpr);
     const int32_t g0 = tile * (BLOCK * UB);
-    RowBwd r;
-    r.gv = p.g[row * p.g_stride];
-    r.zero = false;
-    r.tg = -1;
-    r.tj = 0;
     const char* ra = row_ptr<DT>(p.a, row);
-    const char* rb = nullptr;
+    const char* rb = OP == kKL ? row_ptr<DT>(p.b, row) : nullptr;
     char* oa = p.da ? p.da + row * (int64_t)V * ES : nullptr;
-    char* ob = nullptr;
-    if constexpr (OP == kKL) {
-      rb = row_ptr<DT>(p.b, row);
-      ob = p.db ? p.db + row * (int64_t)V * ES : nullptr;
-      r.m = p.stats[4 * row + 0];
-      r.ls = p.stats[4 * row + 1];
-      r.mb = p.stats[4 * row + 2];
-      r.lsb = p.stats[4 * row + 3];
-      r.res = p.res[row];
-      r.nan_a = !(r.res < kInf);  // +inf (support mismatch) or NaN
-      r.nan_b = r.res != r.res;
-    } else {
-      r.m = p.stats[2 * row + 0];
-      r.ls = p.stats[2 * row + 1];
-      r.mb = r.lsb = 0.0f;
-      r.nan_b = false;
-      if constexpr (OP == kEntropy) {
-        r.res = p.res[row];
-        r.nan_a = r.res != r.res;
-      } else {
-        r.res = 0.0f;
-        const int64_t t = load_id(p.ids, row, p.a.n_inner);
-        r.zero = t == p.ignore_index;
-        r.nan_a = !r.zero && (t < 0 || t >= V);
-        if (!r.zero && !r.nan_a) {
-          r.tg = (int32_t)(t >> 3);
-          r.tj = (int)(t & 7);
-        }
-      }
-    }
+    char* ob = OP == kKL && p.db ? p.db + row * (int64_t)V * ES : nullptr;
     const int32_t g = g0 + threadIdx.x;
+    float xa[UB][8], xb[OP == kKL ? UB : 1][8];
     if (VEC && g0 + BLOCK * UB <= g_full) {
-      bwd_groups<OP, DT, true>(r, ra, rb, oa, ob, g, BLOCK, UB, G, V, g_full);
+      // the whole tile's loads first, then the row constants: one memory latency per tile
+      RawGroup<DT> wa[UB], wb[OP == kKL ? UB : 1];
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        load_group_raw<DT>(ra, g + u * BLOCK, wa[u]);
+        if constexpr (OP == kKL) load_group_raw<DT>(rb, g + u * BLOCK, wb[u]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const RowBwd r = row_consts<OP>(p, row, V);
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        raw_to_float<DT>(wa[u], xa[u]);
+        if constexpr (OP == kKL) raw_to_float<DT>(wb[u], xb[u]);
+      }
+      bwd_store<OP, DT, true, BLOCK, UB>(r, xa, xb_ref<OP, UB>(xa, xb), oa, ob, g, G, V, g_full);
     } else {
-      bwd_groups<OP, DT, false>(r, ra, rb, oa, ob, g, BLOCK, UB, G, V, g_full);
+      const RowBwd r = row_consts<OP>(p, row, V);
+      bwd_load<DT, false, BLOCK, UB>(ra, g, G, V, g_full, xa);
+      if constexpr (OP == kKL) bwd_load<DT, false, BLOCK, UB>(rb, g, G, V, g_full, xb);
+      bwd_store<OP, DT, false, BLOCK, UB>(r, xa, xb_ref<OP, UB>(xa, xb), oa, ob, g, G, V, g_full);
     }
   }
 }
 
 namespace {
 constexpr int kBwdBlock = 256;
-constexpr int kBwdUB = 2;
+// Groups of 8 columns per lane per tile: 2 for the single-input ops (4096-column tiles),
+// 1 for KL, which reads two inputs (2048-column tiles); the fastest by measurement.
+constexpr int bwd_ub(int op) { return op == kKL ? 1 : 2; }
 
 template <int OP, int DT, bool VEC>
 hipError_t launch_bwd_t(const BwdArgs& p, hipStream_t stream) {
   const int64_t blocks = grid_cap(p.N * p.tiles_per_row);
-  hipLaunchKernelGGL((bwd_kernel<OP, DT, VEC, kBwdBlock, kBwdUB>), dim3((uint32_t)blocks), dim3(kBwdBlock), 0, stream, p);
+  hipLaunchKernelGGL((bwd_kernel<OP, DT, VEC, kBwdBlock, bwd_ub(OP)>), dim3((uint32_t)blocks), dim3(kBwdBlock), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -169,9 +211,10 @@ hipError_t launch_bwd_op(const BwdArgs& p, int dtype, bool vec, hipStream_t stre
 }
 }  // namespace
 
-int32_t bwd_tiles_per_row(int64_t V) {
+int32_t bwd_tiles_per_row(int op, int64_t V) {
   const int64_t G = (V + 7) / 8;
-  return (int32_t)((G + kBwdBlock * kBwdUB - 1) / (kBwdBlock * kBwdUB));
+  const int64_t per = (int64_t)kBwdBlock * bwd_ub(op);
+  return (int32_t)((G + per - 1) / per);
 }
 
 hipError_t launch_bwd(int op, const BwdArgs& p, int dtype, bool vec, hipStream_t stream) {

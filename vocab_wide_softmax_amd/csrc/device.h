@@ -90,6 +90,50 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t hi16) { return __ui
 // Group g of a row covers columns [8g, 8g + 8). The vector form needs the row
 // start 16-byte aligned and the whole group inside the row.
 
+// The same load split in two: the raw 16-byte words of a group (issued now), and their
+// conversion to fp32 (done later), so that a kernel can put several groups' loads in flight
+// before it uses any of them.
+template <int DT>
+struct RawGroup {
+  u32x4 w[DT == kF32 ? 2 : 1];
+};
+
+template <int DT>
+__device__ __forceinline__ void load_group_raw(const char* __restrict__ row, int32_t g, RawGroup<DT>& r) {
+  if constexpr (DT == kF32) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(row) + 2 * g;
+    r.w[0] = stream_load(p);
+    r.w[1] = stream_load(p + 1);
+  } else {
+    r.w[0] = stream_load(reinterpret_cast<const u32x4*>(row) + g);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void raw_to_float(const RawGroup<DT>& r, float (&x)[8]) {
+  if constexpr (DT == kF16) {
+    const f16x8 h = __builtin_bit_cast(f16x8, r.w[0]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = (float)h[k];
+  } else if constexpr (DT == kBF16) {
+    const u32x4 w = r.w[0];
+    x[0] = __uint_as_float(w.x << 16);
+    x[1] = __uint_as_float(w.x & 0xffff0000u);
+    x[2] = __uint_as_float(w.y << 16);
+    x[3] = __uint_as_float(w.y & 0xffff0000u);
+    x[4] = __uint_as_float(w.z << 16);
+    x[5] = __uint_as_float(w.z & 0xffff0000u);
+    x[6] = __uint_as_float(w.w << 16);
+    x[7] = __uint_as_float(w.w & 0xffff0000u);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[k] = __uint_as_float(r.w[0][k]);
+      x[4 + k] = __uint_as_float(r.w[1][k]);
+    }
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ void load_group_vec(const char* __restrict__ row, int32_t g, float (&x)[8]) {
   if constexpr (DT == kF16) {
