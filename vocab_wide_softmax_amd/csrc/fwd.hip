@@ -63,19 +63,19 @@ __device__ __forceinline__ void update_kl(StateKL& st, const float (&xa)[U][8], 
       bmb = fmaxf(bmb, xb[k][j]);
       bminb = fminf(bminb, xb[k][j]);
     }
-  if (bma > st.ma) {
-    const float d = st.ma - bma;
-    const float s = expf_fast(d);
-    st.W = mul0(s, st.W + d * st.Sa);
+  const bool ga = bma > st.ma, gb = bmb > st.mb;
+  if (ga || gb) {
+    // W holds e_a ((a - ref_a) - (b - ref_b)). Moving the references to the new maxima scales
+    // e_a by s = e^(ma - ma') and shifts every bracket by (ref_a - ref_a') - (ref_b - ref_b');
+    // both shifts are applied as one difference, so identical inputs (A = B) keep W exactly 0.
+    const float nma = ga ? bma : st.ma, nmb = gb ? bmb : st.mb;
+    const float sh = (ref_of(st.ma) - ref_of(nma)) - (ref_of(st.mb) - ref_of(nmb));
+    const float s = ga ? expf_fast(st.ma - nma) : 1.0f;  // 0 when the state was empty
+    st.W = mul0(s, st.W + sh * st.Sa);
     st.Sa = s * st.Sa;
-    st.ma = bma;
-  }
-  if (bmb > st.mb) {
-    // W holds e_a ((a - ref_a) - (b - ref_b)); moving ref_b up by delta adds delta * S_A.
-    const float delta = bmb - ref_of(st.mb);
-    st.W += mul0(st.Sa, delta);
-    st.Sb = expf_fast(st.mb - bmb) * st.Sb;
-    st.mb = bmb;
+    if (gb) st.Sb = expf_fast(st.mb - nmb) * st.Sb;
+    st.ma = nma;
+    st.mb = nmb;
   }
   if (bminb == -kInf) {  // some B entry is masked: decide the support flag on the logits
     uint32_t f = 0;
@@ -174,11 +174,19 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs p) {
     // batches in which every group of every lane is a full vector group: no predicates
     const int32_t nfull = VEC ? (min(g1, g_full) - g0) / (BLOCK * U) : 0;
     for (int32_t it = 0; it < nfull; ++it, gb += BLOCK * U) {
+      // all of the batch's loads in flight before any is used (one latency per batch)
+      RawGroup<DT> wa[U], wb[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        load_group_raw<DT>(ra, gb + k * BLOCK, wa[k]);
+        load_group_raw<DT>(rb, gb + k * BLOCK, wb[k]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       float xa[U][8], xb[U][8];
 #pragma unroll
       for (int k = 0; k < U; ++k) {
-        load_group_vec<DT>(ra, gb + k * BLOCK, xa[k]);
-        load_group_vec<DT>(rb, gb + k * BLOCK, xb[k]);
+        raw_to_float<DT>(wa[k], xa[k]);
+        raw_to_float<DT>(wb[k], xb[k]);
       }
       update_kl<U>(st, xa, xb);
     }
@@ -286,12 +294,15 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdArgs p) {
 
 namespace {
 constexpr int kFwdBlock = 256;
-constexpr int kFwdU = 4;
+// Groups of 8 columns per lane per batch: 4 for one input, 2 for KL's two (the same bytes
+// in flight per batch; the fastest by measurement).
+constexpr int fwd_u(int op) { return op == kKL ? 2 : 4; }
 
 template <int OP, int DT, bool VEC>
 hipError_t launch_fwd_t(const FwdArgs& p, hipStream_t stream) {
   const int64_t blocks = grid_cap(p.N * p.parts);
-  hipLaunchKernelGGL((fwd_kernel<OP, DT, VEC, kFwdBlock, kFwdU>), dim3((uint32_t)blocks), dim3(kFwdBlock), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<OP, DT, VEC, kFwdBlock, fwd_u(OP)>), dim3((uint32_t)blocks), dim3(kFwdBlock), 0,
+                     stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.parts == 1) return e;
   hipLaunchKernelGGL((combine_kernel<OP, DT>), dim3((uint32_t)grid_cap((p.N + 255) / 256)), dim3(256), 0, stream, p);

@@ -148,14 +148,21 @@ __global__ __launch_bounds__(kJsdBlock) void jsd_div_kernel(JsdArgs p) {
     // whole vector groups of every lane: no predicates
     const int32_t nfull = VEC ? (min(g1, g_full) - g0) / (kJsdBlock * U) : 0;
     for (int32_t it = 0; it < nfull; ++it, gb += kJsdBlock * U) {
-      float xs[U][8], xt[U][8];
+      // all of the batch's loads in flight before any is used
+      RawGroup<DT> ws_[U], wt_[U];
 #pragma unroll
       for (int k = 0; k < U; ++k) {
-        load_group_vec<DT>(rs, gb + k * kJsdBlock, xs[k]);
-        load_group_vec<DT>(rt, gb + k * kJsdBlock, xt[k]);
+        load_group_raw<DT>(rs, gb + k * kJsdBlock, ws_[k]);
+        load_group_raw<DT>(rt, gb + k * kJsdBlock, wt_[k]);
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int k = 0; k < U; ++k) accumulate(xs[k], xt[k]);
+      for (int k = 0; k < U; ++k) {
+        float xs[8], xt[8];
+        raw_to_float<DT>(ws_[k], xs);
+        raw_to_float<DT>(wt_[k], xt);
+        accumulate(xs, xt);
+      }
     }
     for (; gb < g1; gb += kJsdBlock * U) {
 #pragma unroll
