@@ -6,7 +6,10 @@
 * the full hidden and vocabulary widths (4096 x 151936) at 512 tokens: every
   logp and dh element, sampled dW rows;
 * the full 8192 x 4096 x 151936 launch (slow): sampled rows of logp and dh,
-  sampled vocabulary rows of dW.
+  sampled vocabulary rows of dW;
+* 8548 tokens x vocabulary 16684 (34 token tiles, 66 vocabulary tiles): every
+  element, with every branch of the forward's and the dz pass's block-to-tile
+  orders in use (whole groups and the tiles past them in both dimensions).
 
 dh and dW are compared with the conditioned factor 2^-8: the backward feeds dz to
 its two contractions rounded to bf16 (2^-9 relative per term), as the pages'
@@ -121,6 +124,29 @@ def test_linear_full_size_sampled(device):
     dw_ref, dw_c = OL.linear_logp_bwd_dw_cond(hh, hw, ht, hg, vocab_rows=cols)
     _assert_ok(compare.check(f64(dW[torch.from_numpy(cols).to(device)]), dw_ref, dw_c, "bf16", GEMM_FACTOR),
                "full dW rows")
+
+
+@pytest.mark.slow
+def test_linear_tile_orders_all_elements(device):
+    """34 token tiles (one whole group of 32 plus 2, the last partial) and 66 vocabulary
+    tiles (one whole super-tile of 64 plus 2, the last partial): a tile the block orders
+    skipped or visited twice would leave a wrong logp, dh or dW element."""
+    wl = W.linear_logp(n=8548, hidden=128, v=16684, seed=9, w_std=0.1)
+    wl.t[::97] = -100
+    logp, stats, dh, dW = _run(wl.h, wl.W, wl.t, wl.g, device)
+    hh, hw, ht, hg = f64(wl.h), f64(wl.W), wl.t.numpy(), wl.g.double().numpy()
+    for r0 in range(0, hh.shape[0], 1024):
+        rows = np.arange(r0, min(r0 + 1024, hh.shape[0]))
+        lp, m, ls = OL.linear_logp_fwd(hh, hw, ht, rows=rows)
+        c = OL.cond_linear_fwd(hh, hw, ht, rows=rows)
+        _assert_ok(compare.check(f64(logp[r0:rows[-1] + 1]), lp, c, "f32"), "orders logp %d" % r0)
+        lse_dev = f64(stats[r0:rows[-1] + 1, 0]) + f64(stats[r0:rows[-1] + 1, 1])
+        _assert_ok(compare.check(lse_dev, m + ls, c, "f32"), "orders lse %d" % r0)
+        _assert_ok(compare.check(f64(dh[r0:rows[-1] + 1]), OL.linear_logp_bwd_dh(hh, hw, ht, hg, rows=rows),
+                                 OL.cond_linear_dh(hh, hw, ht, hg, rows=rows), "bf16", GEMM_FACTOR),
+                   "orders dh %d" % r0)
+    dw_ref, dw_c = OL.linear_logp_bwd_dw_cond(hh, hw, ht, hg)
+    _assert_ok(compare.check(f64(dW), dw_ref, dw_c, "bf16", GEMM_FACTOR), "orders dW")
 
 
 def test_linear_strided_rows_broadcast_g_and_partial_stage(device):

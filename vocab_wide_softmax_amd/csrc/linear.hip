@@ -40,12 +40,33 @@ __device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 
 
 // ---- forward -----------------------------------------------------------------------
 
+// Block -> (token tile, vocabulary chunk). Block b runs on XCD b % 8, and an XCD runs 32
+// blocks at a time. Token tiles go in groups of 32, 4 per XCD; an XCD's blocks take its 4
+// token tiles fastest, then the chunks, so the 32 it runs at once are 4 token tiles x 8
+// chunks: its L2 streams 4 h panels and 8 W tiles per vocabulary step (a one-chunk order
+// streams 32 h panels for 1 W tile). Token tiles past the last whole group of 32 follow in
+// plain order.
+__device__ __forceinline__ void fwd_tile(int64_t b, int64_t ntt, int nchunks, int64_t& tt, int& c) {
+  const int64_t ntt_full = (ntt / 32) * 32;
+  if (b < ntt_full * nchunks) {
+    const int64_t x = b % 8, q = b / 8;
+    const int64_t r = q / 4;
+    c = (int)(r % nchunks);
+    tt = ((r / nchunks) * 8 + x) * 4 + q % 4;
+  } else {
+    const int64_t r = b - ntt_full * nchunks;
+    tt = ntt_full + r / nchunks;
+    c = (int)(r % nchunks);
+  }
+}
+
 template <class C>
 __global__ __launch_bounds__(C::NT) void lin_fwd_kernel(LinArgs p) {
   extern __shared__ __align__(16) char lds[];
   const int nchunks = p.chunks;
-  const int64_t tt = blockIdx.x / nchunks;   // token tile
-  const int c = blockIdx.x - tt * nchunks;  // vocabulary chunk (consecutive ids -> distinct XCDs)
+  int64_t tt;  // token tile
+  int c;       // vocabulary chunk
+  fwd_tile((int64_t)blockIdx.x, (p.N + C::BN - 1) / C::BN, nchunks, tt, c);
   const int64_t n0 = tt * C::BN;
   const int64_t vt0 = (int64_t)c * p.tiles_per_chunk;
   const int64_t vt1 = min(vt0 + p.tiles_per_chunk, (p.V + C::BM - 1) / C::BM);
@@ -158,16 +179,30 @@ __global__ __launch_bounds__(256) void lin_combine_kernel(LinArgs p) {
 
 // ---- backward ------------------------------------------------------------------------
 
-// Tile (token tile, vocabulary tile) -> block id, so that the token tiles of one
-// vocabulary tile are consecutive on one XCD (block b runs on XCD b % 8): W tiles are
-// fetched into that XCD's L2 once and shared.
-__device__ __forceinline__ void xcd_tile(int64_t b, int64_t ntt, int64_t nvt, int64_t& tt, int64_t& vt) {
-  const int64_t x = b % 8, q = b / 8;
-  tt = q % ntt;
-  vt = (q / ntt) * 8 + x;
-  if (vt >= nvt) {  // the last, partial group of 8 vocabulary tiles: plain order
-    tt = b % ntt;
-    vt = b / ntt;
+// Block -> (token tile, vocabulary tile) for the dz pass. Block b runs on XCD b % 8, and an
+// XCD runs 32 blocks at a time; those 32 form a patch of 4 token tiles x 8 vocabulary tiles,
+// so its L2 streams 4 h panels and 8 W tiles per k-step (one vocabulary tile at a time would
+// stream 32 h panels for 1 W tile). The 8 XCDs' patches lie side by side along the
+// vocabulary (a super-tile of 4 x 64 tiles), and super-tiles go token group fastest, so a
+// group of 64 W tiles is reused from the MALL by every token group in turn. Tiles outside
+// the whole super-tiles follow in plain order.
+__device__ __forceinline__ void dz_tile(int64_t b, int64_t ntt, int64_t nvt, int64_t& tt, int64_t& vt) {
+  const int64_t ntt4 = (ntt / 4) * 4, nvt64 = (nvt / 64) * 64;
+  const int64_t nfull = ntt4 * nvt64;
+  if (b < nfull) {
+    const int64_t x = b % 8, q = b / 8, s = q / 32, ngt = ntt4 / 4;
+    tt = (s % ngt) * 4 + q % 4;
+    vt = (s / ngt) * 64 + x * 8 + (q / 4) % 8;
+    return;
+  }
+  const int64_t r = b - nfull, r1 = ntt4 * (nvt - nvt64);
+  if (r < r1) {  // whole token groups, vocabulary tiles past the last super-tile
+    tt = r % ntt4;
+    vt = nvt64 + r / ntt4;
+  } else {  // the last ntt - ntt4 token tiles, every vocabulary tile
+    const int64_t r2 = r - r1, nt2 = ntt - ntt4;
+    tt = ntt4 + r2 % nt2;
+    vt = r2 / nt2;
   }
 }
 
@@ -176,14 +211,7 @@ __global__ __launch_bounds__(C::NT) void lin_dz_kernel(LinArgs p) {
   extern __shared__ __align__(16) char lds[];
   const int64_t ntt = (p.N + C::BM - 1) / C::BM, nvt = (p.V + C::BN - 1) / C::BN;
   int64_t tt, vt;
-  const int64_t full = (nvt / 8) * 8 * ntt;  // blocks covered by whole groups of 8 vocabulary tiles
-  if ((int64_t)blockIdx.x < full) {
-    xcd_tile(blockIdx.x, ntt, nvt, tt, vt);
-  } else {
-    const int64_t r = blockIdx.x - full;
-    tt = r % ntt;
-    vt = (nvt / 8) * 8 + r / ntt;
-  }
+  dz_tile((int64_t)blockIdx.x, ntt, nvt, tt, vt);
   const int64_t m0 = tt * C::BM, n0 = vt * C::BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
