@@ -5,7 +5,8 @@ ignored row): duplicates, ignored slots, a fully ignored row, an out-of-range
 slot (NaN logp, NaN gradient row), a target on a masked column, a +1e4 row,
 ragged V, the element-wise (unaligned) load path, forced vocabulary splits, a
 3-D [B, S, V] view with strided ids, a broadcast upstream gradient, the largest
-K with every id in one column tile, and the full 75968-column width.
+K of each backward kernel (64 and 2048) with every id in one column tile,
+K = 64 and 65 on either side of the kernel switch, and the full 75968-column width.
 Every element of logp [N, K] and dz [N, V] is compared.
 """
 
@@ -66,7 +67,7 @@ def _run_and_check(z_dev, ids_dev, g_dev, z_host, ids_host, g_host, label, split
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("v,K", [(1024, 8), (4097, 5), (9, 3), (75968, 16)])
+@pytest.mark.parametrize("v,K", [(1024, 8), (4097, 5), (9, 3), (75968, 16), (9000, 64), (9000, 65)])
 def test_topk_all_elements(device, dtype, v, K):
     n = 24 if v == 75968 else 40
     print("topk v", v, "K", K, dtype, flush=True)
@@ -107,14 +108,17 @@ def test_topk_broadcast_upstream_gradient(device):
     _run_and_check(z.to(device), ids.to(device), gd, z, ids, g, "broadcast g")
 
 
-def test_topk_max_k_all_in_one_tile(device):
-    n, v, K = 3, 6000, 2048
+@pytest.mark.parametrize("K", [64, 2048])
+def test_topk_max_k_all_in_one_tile(device, K):
+    """The largest K of each backward kernel (slots in lane registers up to 64, in LDS above)
+    with every id in one column tile and many duplicates."""
+    n, v = 3, 6000
     gen = torch.Generator().manual_seed(8)
     z = 2.0 * torch.randn(n, v, generator=gen)
-    ids = torch.randint(4096, 4200, (n, K), generator=gen)  # all in the second column tile, many duplicates
+    ids = torch.randint(4096, 4200, (n, K), generator=gen)  # all in one column tile, many duplicates
     ids[1, ::5] = IGN
     g = torch.randn(n, K, generator=gen)
-    _run_and_check(z.to(device), ids.to(device), g.to(device), z, ids, g, "K=2048 one tile")
+    _run_and_check(z.to(device), ids.to(device), g.to(device), z, ids, g, "K=%d one tile" % K)
 
 
 def test_topk_single_slot_matches_single_id_op(device):

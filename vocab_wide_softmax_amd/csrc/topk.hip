@@ -14,9 +14,11 @@
 // The forward reuses the single-read (m, S) pass of the logprobs forward, which
 // writes the row statistics; a gather kernel (one thread per slot) then forms
 // out[n, k]. The backward is one pass over the logits per (row, column tile),
-// like the single-id backward; each workgroup first collects, in slot order,
-// the live ids that fall in its tile into LDS, so the per-column hit sums are
-// formed in the same order in every run.
+// like the single-id backward. For K <= 64 each wave holds the row's slots one per
+// lane and works on them with ballots and lane reads; for larger K each workgroup
+// first collects, in slot order, the live ids that fall in its tile into LDS.
+// Either way G is summed in a fixed order and the per-column hit sums in slot
+// order, the same in every run.
 #include "device.h"
 #include "launch.h"
 
@@ -24,7 +26,10 @@ namespace vws {
 
 namespace {
 constexpr int kTopkBlock = 256;
-constexpr int kTopkUB = 4;  // groups of 8 columns per lane per tile (8192-column tiles)
+constexpr int kTopkUB = 4;         // LDS slot kernel: groups of 8 columns per lane per tile (8192-column tiles)
+constexpr int kTopkSmallK = 64;    // K up to this: slots in lane registers, one per lane of a wave
+constexpr int kTopkSmallUB = 2;    // ... with 4096-column tiles (the fastest by measurement)
+constexpr int topk_ub(int32_t K) { return K <= kTopkSmallK ? kTopkSmallUB : kTopkUB; }
 }  // namespace
 
 __device__ __forceinline__ int64_t topk_id(const TopkArgs& p, int64_t row, int32_t k) {
@@ -190,9 +195,99 @@ __global__ __launch_bounds__(kTopkBlock) void topk_bwd_kernel(TopkArgs p) {
   }
 }
 
-int32_t topk_tiles_per_row(int64_t V) {
-  const int64_t G = (V + 7) / 8;
-  return (int32_t)((G + kTopkBlock * kTopkUB - 1) / (kTopkBlock * kTopkUB));
+// Lane k's value (k wave-uniform).
+__device__ __forceinline__ float lane_f(float v, int k) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
+}
+
+// Small K (K <= 64): lane k of every wave loads slot k together with the tile's logits, and
+// the slot logic runs on wave-uniform values: ballots give the flags and the live ids that
+// fall in the tile, G is a butterfly sum over the wave's lanes (the same value, bit for bit,
+// in every lane and every run), and each group of 8 columns adds the hits it owns in slot
+// order. No LDS and no barriers: a tile costs about what the single-id backward's does.
+template <int DT, bool VEC, int UB>
+__global__ __launch_bounds__(kTopkBlock) void topk_bwd_small_kernel(TopkArgs p) {
+  constexpr int ES = ElemSize<DT>::value;
+  constexpr int TG = kTopkBlock * UB;  // groups of 8 columns per tile
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int32_t tpr = p.tiles_per_row;
+  const int64_t total = p.N * tpr;
+  const int32_t V = (int32_t)p.V;
+  const int32_t G = (V + 7) / 8;
+  const int32_t g_full = VEC ? V / 8 : 0;
+  const int32_t K = p.K;
+  for (int64_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
+    const int64_t row = udiv(vb, tpr);
+    const int32_t tile = (int32_t)(vb - row * tpr);
+    const int32_t g0 = tile * TG;
+    const char* ra = row_ptr<DT>(p.a, row);
+    const int32_t g = g0 + tid;
+    const bool full = VEC && g0 + TG <= g_full;
+    // the tile's loads and the slot loads first: one memory latency per tile
+    RawGroup<DT> w[UB];
+    float x[UB][8];
+    if (full) {
+#pragma unroll
+      for (int u = 0; u < UB; ++u) load_group_raw<DT>(ra, g + u * kTopkBlock, w[u]);
+    } else {
+      topk_load<DT, false, UB>(ra, g, G, V, g_full, x);
+    }
+    int64_t tv = p.ignore_index;
+    float gl = 0.0f;
+    if (lane < K) {
+      tv = topk_id(p, row, lane);
+      gl = p.g[row * p.g_sr + (int64_t)lane * p.g_sk];
+    }
+    const float m = p.stats[2 * row], ls = p.stats[2 * row + 1];
+    __builtin_amdgcn_sched_barrier(0);
+
+    const bool live = lane < K && tv != p.ignore_index;
+    const bool oor = live && (tv < 0 || tv >= V);
+    const bool in_tile = live && !oor && (tv >> 3) >= g0 && (tv >> 3) < g0 + TG;
+    const bool zero_row = __ballot(live) == 0ull, nan_row = __ballot(oor) != 0ull;
+    const uint64_t hits = __ballot(in_tile);
+    float Gs = live && !oor ? gl : 0.0f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) Gs += __shfl_xor(Gs, off, 64);
+
+    char* oa = p.dz + row * (int64_t)V * ES;
+    const float qnan = __builtin_nanf("");
+    if (full) {
+#pragma unroll
+      for (int u = 0; u < UB; ++u) raw_to_float<DT>(w[u], x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int32_t gu = g + u * kTopkBlock;
+      if (!full && gu >= G) break;
+      float y[8], hu[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) hu[j] = 0.0f;
+      for (uint64_t hm = hits; hm; hm &= hm - 1) {  // slot order
+        const int k = __builtin_ctzll(hm);
+        const int32_t t = __builtin_amdgcn_readlane((int32_t)tv, k);
+        const int32_t rel = (t >> 3) - g0;
+        if (rel / kTopkBlock != u) continue;
+        const float gk = lane_f(gl, k);
+        const float add = (rel % kTopkBlock) == tid ? gk : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j == (t & 7)) hu[j] += add;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float pj = expf_fast((x[u][j] - m) - ls);
+        y[j] = zero_row ? 0.0f : (nan_row ? qnan : __builtin_fmaf(-Gs, pj, hu[j]));
+      }
+      if (full) store_group_vec<DT>(oa, gu, y);
+      else store_group<DT, true>(oa, gu, V, g_full, y);
+    }
+  }
+}
+
+int32_t topk_tiles_per_row(int64_t V, int32_t K) {
+  const int64_t G = (V + 7) / 8, per = (int64_t)kTopkBlock * topk_ub(K);
+  return (int32_t)((G + per - 1) / per);
 }
 
 hipError_t launch_topk_gather(const TopkArgs& p, int dtype, hipStream_t stream) {
@@ -208,8 +303,14 @@ hipError_t launch_topk_bwd(const TopkArgs& p, int dtype, bool vec, hipStream_t s
   const dim3 grid((uint32_t)blocks), block(kTopkBlock);
   return dispatch_dtype(dtype, [&](auto dt) {
     constexpr int DT = decltype(dt)::value;
-    if (vec) hipLaunchKernelGGL((topk_bwd_kernel<DT, true, kTopkUB>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((topk_bwd_kernel<DT, false, kTopkUB>), grid, block, 0, stream, p);
+    if (p.K <= kTopkSmallK) {
+      if (vec) hipLaunchKernelGGL((topk_bwd_small_kernel<DT, true, kTopkSmallUB>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((topk_bwd_small_kernel<DT, false, kTopkSmallUB>), grid, block, 0, stream, p);
+    } else if (vec) {
+      hipLaunchKernelGGL((topk_bwd_kernel<DT, true, kTopkUB>), grid, block, 0, stream, p);
+    } else {
+      hipLaunchKernelGGL((topk_bwd_kernel<DT, false, kTopkUB>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
   });
 }
