@@ -125,7 +125,8 @@ __global__ __launch_bounds__(kTopkBlock) void topk_bwd_kernel(TopkArgs p) {
     const int64_t row = udiv(vb, tpr);
     const int32_t tile = (int32_t)(vb - row * tpr);
     const int32_t g0 = tile * (kTopkBlock * UB);
-    const int32_t c0 = g0 * 8, c1 = min(V, c0 + kTopkBlock * UB * 8);
+    // the tile's end column in 64 bits: c0 + 8192 passes INT32_MAX on the last tile of the widest rows
+    const int32_t c0 = g0 * 8, c1 = (int32_t)min((int64_t)V, (int64_t)c0 + kTopkBlock * UB * 8);
     const char* ra = row_ptr<DT>(p.a, row);
     const int32_t g = g0 + tid;
     const bool full = VEC && g0 + kTopkBlock * UB <= g_full;
