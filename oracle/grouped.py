@@ -13,8 +13,9 @@ DeepSpeed PR #8838 "Add Triton kernels for vocab-parallel logprobs, entropy and
 KL" (ops listed in the JSD squash-commit text; gradients per logit, second
 commit message), the logprobs gradient printed in the review nitpick of
 RL-Kernel PR #208, and the multi-id (top-k) form whose duplicate and ignored
-ids that PR's test list names. The readings are those of oracle.reductions and
-oracle.topk: -inf entries are masked (probability 0, left out of every sum,
+ids that PR's test list names, and the generalized JSD of the JSD pull request
+pasted into PR #8838 (the GKD-style mixture read in oracle.jsd). The readings
+are those of oracle.reductions, oracle.topk and oracle.jsd: -inf entries are masked (probability 0, left out of every sum,
 zero gradient); a row with a NaN or +inf entry or no entry above -inf is
 undefined (NaN); KL(A||B) is +inf when B masks a column A supports, with a NaN
 gradient for A.
@@ -24,8 +25,8 @@ A target or a top-k id names one column; its pair must be a group of its own
 same value. Every function takes one row: z (or a, b) [k] values and cnt [k]
 positive integer counts, and returns per-group values for the gradients.
 
-Pinned in tests/test_oracle_grouped.py against oracle.reductions and oracle.topk
-on the same rows expanded to dense form.
+Pinned in tests/test_oracle_grouped.py against oracle.reductions, oracle.topk
+and oracle.jsd on the same rows expanded to dense form.
 """
 
 import numpy as np
@@ -48,6 +49,10 @@ __all__ = [
     "cond_kl_bwd",
     "cond_logprobs_topk_fwd",
     "cond_logprobs_topk_bwd",
+    "jsd_fwd",
+    "jsd_bwd",
+    "cond_jsd_fwd",
+    "cond_jsd_bwd",
 ]
 
 _ERR = dict(invalid="ignore", over="ignore", divide="ignore", under="ignore")
@@ -282,3 +287,95 @@ def cond_logprobs_topk_bwd(z, cnt, slots, gk):
     np.add.at(c, slots, ga)
     with np.errstate(**_ERR):
         return c + np.sum(ga) * p * (1.0 + dz + als)
+
+
+# ---- generalized JSD (student s, teacher t): M = (1 - beta) p_S + beta p_T,
+# JSD = beta KL(T||M) + (1 - beta) KL(S||M) inside (0, 1); KL(T||S) at beta = 0, KL(S||T) at 1
+
+
+def _jsd_interior(s, t, cnt, beta):
+    ls, ms, lss = log_softmax(s, cnt)
+    lt, mt, lst = log_softmax(t, cnt)
+    with np.errstate(**_ERR):
+        ps, pt = np.exp(ls), np.exp(lt)
+        lm = np.log((1.0 - beta) * ps + beta * pt)
+        Ks = np.sum(np.where(ps > 0, cnt * ps * (ls - lm), 0.0))
+        Kt = np.sum(np.where(pt > 0, cnt * pt * (lt - lm), 0.0))
+    bad = not _defined(s) or not _defined(t)
+    return ps, pt, ls, lt, lm, Ks, Kt, bad, (ms, lss, mt, lst)
+
+
+def jsd_fwd(s, t, cnt, beta):
+    """(JSD, (K_S, K_T) inside (0, 1), None at the endpoints)."""
+    s, cnt = _row(s, cnt)
+    t, _ = _row(t, cnt)
+    beta = float(beta)
+    if beta == 0.0:
+        return kl_fwd(t, s, cnt)[0], None
+    if beta == 1.0:
+        return kl_fwd(s, t, cnt)[0], None
+    _, _, _, _, _, Ks, Kt, bad, _ = _jsd_interior(s, t, cnt, beta)
+    if bad:
+        return np.nan, (np.nan, np.nan)
+    return beta * Kt + (1.0 - beta) * Ks, (Ks, Kt)
+
+
+def jsd_bwd(s, t, cnt, g, beta):
+    """Per group: (g (1 - beta) p_S ((log p_S - log M) - K_S), g beta p_T ((log p_T - log M) - K_T)),
+    0 where the probability is 0; the KL gradients at the endpoints."""
+    s, cnt = _row(s, cnt)
+    t, _ = _row(t, cnt)
+    beta, g = float(beta), float(g)
+    if beta == 0.0:
+        dt, ds = kl_bwd(t, s, cnt, g)
+        return ds, dt
+    if beta == 1.0:
+        return kl_bwd(s, t, cnt, g)
+    ps, pt, ls, lt, lm, Ks, Kt, bad, _ = _jsd_interior(s, t, cnt, beta)
+    if bad:
+        return np.full(s.shape, np.nan), np.full(s.shape, np.nan)
+    with np.errstate(**_ERR):
+        ds = np.where(ps > 0, g * (1.0 - beta) * ps * ((ls - lm) - Ks), 0.0)
+        dt = np.where(pt > 0, g * beta * pt * ((lt - lm) - Kt), 0.0)
+    return ds, dt
+
+
+def cond_jsd_fwd(s, t, cnt, beta):
+    """Count-weighted form of oracle.jsd.cond_jsd_fwd."""
+    s, cnt = _row(s, cnt)
+    t, _ = _row(t, cnt)
+    beta = float(beta)
+    if beta == 0.0:
+        return cond_kl_fwd(t, s, cnt)
+    if beta == 1.0:
+        return cond_kl_fwd(s, t, cnt)
+    ps, pt, ls, lt, lm, _, _, _, (ms, lss, mt, lst) = _jsd_interior(s, t, cnt, beta)
+    with np.errstate(**_ERR):
+        ws = np.where(ps > 0, cnt * ps * (np.abs(ls) + np.abs(lm) + np.abs(s - ms)), 0.0)
+        wt = np.where(pt > 0, cnt * pt * (np.abs(lt) + np.abs(lm) + np.abs(t - mt)), 0.0)
+        return np.sum(ws) + np.sum(wt) + abs(lss) + abs(lst)
+
+
+def cond_jsd_bwd(s, t, cnt, g, beta):
+    """Count-weighted form of oracle.jsd.cond_jsd_bwd: per group (c_s, c_t)."""
+    s, cnt = _row(s, cnt)
+    t, _ = _row(t, cnt)
+    beta = float(beta)
+    if beta == 0.0:
+        ct, cs = cond_kl_bwd(t, s, cnt, g)
+        return cs, ct
+    if beta == 1.0:
+        return cond_kl_bwd(s, t, cnt, g)
+    g = abs(float(g))
+    ps, pt, ls, lt, lm, Ks, Kt, _, (ms, lss, mt, lst) = _jsd_interior(s, t, cnt, beta)
+    live_s, live_t = s > -np.inf, t > -np.inf
+    with np.errstate(**_ERR):
+        base = 1.0 + np.abs(lm)
+        cs = np.where(ps > 0, (1.0 - beta) * ps * (base + np.abs(s - ms) + abs(lss) + abs(Ks)), 0.0)
+        ct = np.where(pt > 0, beta * pt * (base + np.abs(t - mt) + abs(lst) + abs(Kt)), 0.0)
+        # the other side's share of log M
+        cs = cs + np.where((ps > 0) & live_t, (1.0 - beta) * ps * (np.abs(t - mt) + abs(lst)), 0.0)
+        ct = ct + np.where((pt > 0) & live_s, beta * pt * (np.abs(s - ms) + abs(lss)), 0.0)
+    cs = np.where(np.isnan(cs), 0.0, cs)
+    ct = np.where(np.isnan(ct), 0.0, ct)
+    return g * cs, g * ct

@@ -13,8 +13,9 @@ output and every gradient entry:
 
 Layouts: one row at the limit (16-byte loads, ragged last group), two rows at the limit (odd
 row pitch: the element-wise path) and two rows at V - 7 (a multiple of 8: 16-byte loads in
-every row). Each runs logprobs, entropy, KL(A||B), KL(B||A) and top-k logprobs (K = 3 with a
-duplicate id, and K = 65 with ids in the last column tile) forward and backward, in the automatic and the batch-invariant split. Forward
+every row). Each runs logprobs, entropy, KL(A||B), KL(B||A), the generalized JSD at beta = 0.5
+and top-k logprobs (K = 3 with a duplicate id, and K = 65 with ids in the last column tile)
+forward and backward, in the automatic and the batch-invariant split. Forward
 values and the special columns' gradients are compared with the grouped forms under the parity
 rule; every bulk gradient entry is checked at once: the number of entries equal to the bulk's
 value must be the bulk's size (plus the special columns that share that value), and that value
@@ -131,6 +132,18 @@ def test_max_vocab(device, n, V, split):
             _check_grad(dx, r, V, rx, cx, "%s bwd first row %d" % (name, r))
             _check_grad(dy, r, V, ry, cy, "%s bwd second row %d" % (name, r))
         del dx, dy
+
+    # generalized JSD at beta = 0.5 (student A, teacher B)
+    jv, st = B.jsd_fwd(a, b, 0.5, split)
+    _check_fwd(jv, [Gr.jsd_fwd(ga, gb, cnt, 0.5)[0] for ga, gb, cnt, _, _ in G],
+               [Gr.cond_jsd_fwd(ga, gb, cnt, 0.5) for ga, gb, cnt, _, _ in G], "jsd fwd")
+    ds, dt = B.jsd_bwd(a, b, 0.5, st, jv, g)
+    for r, (ga, gb, cnt, _, _) in enumerate(G):
+        rs, rt = Gr.jsd_bwd(ga, gb, cnt, g[r].item(), 0.5)
+        cs, ct = Gr.cond_jsd_bwd(ga, gb, cnt, g[r].item(), 0.5)
+        _check_grad(ds, r, V, rs, cs, "jsd bwd student row %d" % r)
+        _check_grad(dt, r, V, rt, ct, "jsd bwd teacher row %d" % r)
+    del ds, dt
 
     out, st = B.logprobs_topk_fwd(a, ids, IGN, split)
     for r, (ga, gb, cnt, _, sl) in enumerate(G):

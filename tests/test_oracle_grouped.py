@@ -1,5 +1,5 @@
 """Pins of oracle.grouped (count-weighted forms for rows of repeated values) against the dense
-definitions of oracle.reductions and oracle.topk (CPU only).
+definitions of oracle.reductions, oracle.topk and oracle.jsd (CPU only).
 
 Every grouped row is expanded to its dense form (each value repeated its count times) and every
 output, saved statistic, per-column gradient and conditioning scale of the grouped forms must
@@ -12,7 +12,7 @@ wrong sign or a term left out of a sum fails here.
 import numpy as np
 import pytest
 
-from oracle import grouped as Gr, reductions as R, topk as TK
+from oracle import grouped as Gr, jsd as J, reductions as R, topk as TK
 
 NINF = -np.inf
 
@@ -109,6 +109,28 @@ def test_grouped_matches_dense(case):
                label + " cond topk fwd")
         _close(rep(Gr.cond_logprobs_topk_bwd(a, cnt, slots, gk)), TK.cond_logprobs_topk_bwd(da, sc[None], gk[None])[0],
                label + " cond topk bwd")
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.3, 0.5, 1.0])
+@pytest.mark.parametrize("case", range(len(_rows())))
+def test_grouped_jsd_matches_dense(case, beta):
+    a, b, cnt, t, slots, label = _rows()[case]
+    da, db, _, _ = _dense(a, b, cnt, t, slots)
+    g = -0.625
+    rep = lambda v: np.repeat(np.asarray(v, dtype=np.float64), cnt)
+    label = "%s jsd beta=%g" % (label, beta)
+    v, _ = Gr.jsd_fwd(a, b, cnt, beta)
+    _close(v, J.jsd_fwd(da, db, beta)[0][0], label + " fwd", J.cond_jsd_fwd(da, db, beta)[0])
+    gs, gt = Gr.jsd_bwd(a, b, cnt, g, beta)
+    rs, rt = J.jsd_bwd(da, db, [g], beta)
+    cs, ct = J.cond_jsd_bwd(da, db, [g], beta)
+    _close(rep(gs), rs[0], label + " bwd s", cs[0])
+    _close(rep(gt), rt[0], label + " bwd t", ct[0])
+    if np.isfinite(v):
+        _close(Gr.cond_jsd_fwd(a, b, cnt, beta), J.cond_jsd_fwd(da, db, beta)[0], label + " cond fwd")
+        gcs, gct = Gr.cond_jsd_bwd(a, b, cnt, g, beta)
+        _close(rep(gcs), cs[0], label + " cond bwd s")
+        _close(rep(gct), ct[0], label + " cond bwd t")
 
 
 def test_grouped_rejects_shared_target_group():
