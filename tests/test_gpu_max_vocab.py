@@ -1,4 +1,5 @@
-"""The widest rows the library accepts, on the GPU, checked against oracle.grouped.
+"""The largest inputs the library accepts, on the GPU: the widest rows (against oracle.grouped)
+and the most rows (against the dense oracle).
 
 V = INT32_MAX - 4096 = 2147479551 columns (4.3 GB per bf16 row) is the largest vocabulary the
 C ABI takes (column and group indexes are 32-bit). Rows this wide cannot be held on the host as
@@ -20,13 +21,19 @@ values and the special columns' gradients are compared with the grouped forms un
 rule; every bulk gradient entry is checked at once: the number of entries equal to the bulk's
 value must be the bulk's size (plus the special columns that share that value), and that value
 must meet the rule too.
+
+Most rows: N = INT32_MAX rows of V = 8 columns (one backward tile per row, the most the
+backward grid takes), cycling through three row patterns. The first three rows are compared
+with the dense oracle under the parity rule; every other row's output, statistics and gradient
+must equal, bit for bit, those of the first row with the same pattern (each row is reduced by
+the same code in the same order, wherever it sits).
 """
 
 import numpy as np
 import pytest
 import torch
 
-from oracle import compare, grouped as Gr
+from oracle import compare, grouped as Gr, reductions as R
 from vocab_wide_softmax_amd import binding as B
 
 pytestmark = pytest.mark.gpu
@@ -170,4 +177,55 @@ def test_max_vocab(device, n, V, split):
         _check_grad(d, r, V, Gr.logprobs_topk_bwd(ga, cnt, sl, gr), Gr.cond_logprobs_topk_bwd(ga, cnt, sl, gr),
                     "topk65 bwd row %d" % r)
     del d, a, b
+    torch.cuda.empty_cache()
+
+
+def _same_as_pattern(x, P, label):
+    """Every row of x [N, ...] equals row (r mod P) of x bit for bit."""
+    N = x.shape[0]
+    flat = x.reshape(N, -1)
+    bits = flat.view(torch.int16) if flat.element_size() == 2 else flat.view(torch.int32)
+    head = bits[:P]
+    M = (N // P) * P
+    step = P * (1 << 22)
+    for c in range(0, M, step):
+        e = min(M, c + step)
+        blk = bits[c:e].reshape(-1, P, bits.shape[1])
+        assert torch.equal(blk, head.unsqueeze(0).expand_as(blk)), (label, c)
+    assert torch.equal(bits[M:], head[: N - M]), (label, "tail")
+
+
+@pytest.mark.slow
+def test_max_rows(device):
+    N, V, P = 2**31 - 1, 8, 3
+    print("max rows N", N, "V", V, flush=True)
+    pats = torch.tensor([[0.5, -1.0, 2.0, 0.0, 1.5, -3.0, 0.25, 1.0],
+                         [NINF, 4.0, 3.0, NINF, -2.0, 3.5, 0.0, 1.0],
+                         [1e4, 1e4 + 8, 1e4 - 8, 1e4, 1e4 + 16, 1e4, 1e4 - 16, 1e4 + 8]]).bfloat16()
+    tpat = torch.tensor([2, 5, 4])
+    reps = N // P + 1
+    a = pats.to(device).repeat(reps, 1)[:N]
+    t = tpat.to(device).repeat(reps)[:N]
+    g = torch.tensor(0.75, device=device).expand(N)
+    z3, t3, g3 = pats.double().numpy(), tpat.numpy(), np.full(P, 0.75)
+
+    lp, st = B.logprobs_fwd(a, t, IGN)
+    ref, _, _ = R.logprobs_fwd(z3, t3, IGN)
+    _check_fwd(lp[:P], ref, R.cond_logprobs_fwd(z3, t3, IGN), "max rows logprobs fwd")
+    _same_as_pattern(lp, P, "logprobs out")
+    _same_as_pattern(st, P, "logprobs stats")
+    d = B.logprobs_bwd(a, t, st, g, IGN)
+    _ok(compare.check(d[:P].double().cpu().numpy(), R.logprobs_bwd(z3, t3, g3, IGN),
+                      R.cond_logprobs_bwd(z3, t3, g3, IGN), "bf16"), "max rows logprobs bwd")
+    _same_as_pattern(d, P, "logprobs grad")
+    del d, lp, st
+
+    H, st = B.entropy_fwd(a)
+    _check_fwd(H[:P], R.entropy_fwd(z3)[0], R.cond_entropy_fwd(z3), "max rows entropy fwd")
+    _same_as_pattern(H, P, "entropy out")
+    d = B.entropy_bwd(a, st, H, g)
+    _ok(compare.check(d[:P].double().cpu().numpy(), R.entropy_bwd(z3, g3), R.cond_entropy_bwd(z3, g3), "bf16"),
+        "max rows entropy bwd")
+    _same_as_pattern(d, P, "entropy grad")
+    del d, H, st, a, t
     torch.cuda.empty_cache()
