@@ -89,7 +89,11 @@ typedef enum vws_op { VWS_OP_LOGPROBS = 0, VWS_OP_ENTROPY = 1, VWS_OP_KL = 2, VW
  * starts at element  r_o * s_outer + r_i * s_inner  of `data`; columns are
  * contiguous (col_stride must be 1; other layouts are copied by the caller).
  * Strides are in elements and must be >= 0. `data` must be aligned to the
- * element size. N = n_outer * n_inner.
+ * element size. N = n_outer * n_inner. Rows hold 1 <= V <= INT32_MAX - 4096
+ * columns (column and group indexes are 32-bit); V = 0 is VWS_EINVAL: on one
+ * GPU a row without columns has no entry above -inf, and an empty vocabulary
+ * shard of a tensor-parallel split is the caller's neutral partial (m = -inf,
+ * S = 0), not a call into this library.
  */
 typedef struct vws_rows {
   const void* data;

@@ -71,6 +71,7 @@ def _ent(L, r, out=0x2000, stats=0x3000, ws=None, nb=0, hint=0):
 def test_forward_validation(L):
     assert _ent(L, _rows(dtype=5)) == EDTYPE
     assert _ent(L, _rows(V=0)) == EINVAL
+    assert _ent(L, _rows(V=(1 << 31) - 1 - 4096 + 1, s_outer=1 << 31)) == EINVAL  # one past the widest row
     assert _ent(L, _rows(n_outer=-1)) == EINVAL
     assert _ent(L, _rows(col_stride=2)) == ELAYOUT
     assert _ent(L, _rows(s_outer=-64)) == ELAYOUT
