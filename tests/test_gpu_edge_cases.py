@@ -1,6 +1,7 @@
 """GPU edge cases and GPU-vs-GPU invariants, through the C ABI.
 
-* ragged and tiny V, N = 1, the element-wise (unaligned) load path, forced splits;
+* ragged and tiny V, N = 1, the element-wise (unaligned) load path, forced splits, split
+  parts whose columns are all -inf;
 * rows the pages single out: a row spanning -3e38..3e38 (entropy 0, KL(p||p) 0,
   zero gradients), support mismatch with an underflowing p_A (+inf), all -inf
   rows, NaN / +inf entries, a target on a masked column, ignored and
@@ -70,6 +71,25 @@ def test_single_row_long_vocab_split(device):
     a, b, t, g = _pair(1, 151936, seed=2, dtype=torch.bfloat16)
     assert B.split_parts(B.OP_KL, 1, 151936) > 1
     _check_all_ops(a, b, t, g, device)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_fully_masked_split_parts(device, dtype):
+    """Split parts whose columns are all -inf send the neutral partial (m = -inf, S = W = 0),
+    which the merge must skip by the zero-weight rule: the first part masked in both inputs,
+    the last part masked in both, and one part masked in A only (KL(B||A) = +inf there), with
+    V = 1024 in 4 parts of 256 columns."""
+    assert B.split_parts(B.OP_KL, 4, 1024, 4) == 4
+    a, b, t, g = _pair(4, 1024, seed=31, dtype=torch.float32)
+    a[0, :256] = NINF
+    b[0, :256] = NINF
+    t[0] = 300
+    a[1, 768:] = NINF
+    b[1, 768:] = NINF
+    t[1] = 5
+    a[2, 256:512] = NINF
+    t[2] = 900
+    _check_all_ops(a.to(dtype), b.to(dtype), t, g, device, split=4)
 
 
 def _special_rows():
