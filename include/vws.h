@@ -273,17 +273,26 @@ VWS_API int vws_jsd_bwd(const vws_rows* s, const vws_rows* t, float beta, const 
  *   logp    out fp32 [N];  stats out fp32 [N, 2] = (m, log S) of each row's logits
  *   dh      out bf16 [N, H] contiguous, may be NULL
  *   dW      out bf16 [V, H] contiguous, may be NULL
- *   ws      workspace of vws_linear_workspace_bytes(pass, N, H, V) bytes
- *           (pass 0: forward, 1: backward), 16-byte aligned
+ *   ws      workspace of vws_linear_workspace_bytes(pass, N, H, V, split_hint) bytes
+ *           (pass 0: forward, 1: backward, where split_hint is ignored), 16-byte aligned
+ *   split_hint  forward vocabulary chunking, as for the logits ops: 0 automatic (about two
+ *           workgroups per CU for this N; the order in which a token's chunk partials
+ *           merge then follows the batch size), k >= 1 k chunks, VWS_SPLIT_INVARIANT
+ *           chunks of 1024 columns. The last two depend on V alone: a token's logp and
+ *           stats are then the same bits in every batch (batch invariance); < -1 is
+ *           VWS_EINVAL. The backward reduces each dz and dh entry in an order fixed by
+ *           V and H, so dh is batch invariant when the stats it is given are (dW sums
+ *           over the batch by definition).
  * H must be a multiple of 8. h, W, dh, dW must be 16-byte aligned. dtype must be VWS_BF16.
- * Sizes: N <= 2^31, H and V <= INT32_MAX, and ceil(N / 256) * ceil(V / 256) <= INT32_MAX
- * (one backward workgroup per 256 x 256 tile); larger shapes give VWS_EINVAL.
+ * Sizes: N <= 2^31, H and V <= INT32_MAX, and with T(x) = ceil(x / 256) each of
+ * T(N) T(V), T(N) T(H) and T(V) T(H) below 2^23 (one 512-thread workgroup per 256 x 256
+ * tile, fewer than 2^32 work-items per launch); larger shapes give VWS_EINVAL.
  */
-VWS_API size_t vws_linear_workspace_bytes(int pass, int64_t N, int64_t H, int64_t V);
+VWS_API size_t vws_linear_workspace_bytes(int pass, int64_t N, int64_t H, int64_t V, int split_hint);
 
 VWS_API int vws_linear_logp_fwd(const void* h, int64_t ldh, const void* W, int64_t ldw, int dtype, int64_t N,
                                 int64_t H, int64_t V, const int64_t* t, int64_t ignore_index, float* logp,
-                                float* stats, void* ws, size_t ws_bytes, void* stream);
+                                float* stats, void* ws, size_t ws_bytes, int split_hint, void* stream);
 
 VWS_API int vws_linear_logp_bwd(const void* h, int64_t ldh, const void* W, int64_t ldw, int dtype, int64_t N,
                                 int64_t H, int64_t V, const int64_t* t, int64_t ignore_index, const float* stats,

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(L):
     assert len(names) >= 10
     for n in names:
         assert hasattr(L, n), n
-    assert L.vws_version() == 101
+    assert L.vws_version() == 102
 
 
 def test_strerror(L):
@@ -113,8 +113,8 @@ def test_linear_validation(L):
     c_i64 = ctypes.c_int64
 
     def fwd(h=0x1000, ldh=64, W=0x2000, ldw=64, dtype=B.VWS_BF16, N=4, H=64, V=100, t=0x3000, logp=0x4000,
-            stats=0x5000, ws=0x6000, nb=1 << 20):
-        return L.vws_linear_logp_fwd(h, ldh, W, ldw, dtype, N, H, V, t, -100, logp, stats, ws, nb, None)
+            stats=0x5000, ws=0x6000, nb=1 << 20, split=0):
+        return L.vws_linear_logp_fwd(h, ldh, W, ldw, dtype, N, H, V, t, -100, logp, stats, ws, nb, split, None)
 
     assert fwd(dtype=B.VWS_F32) == EDTYPE
     assert fwd(H=0) == EINVAL
@@ -136,8 +136,20 @@ def test_linear_validation(L):
                1 << 20, None) == 0  # no gradient requested
     assert bwd(0x1000, 64, 0x2000, 64, B.VWS_BF16, 4, 64, 100, 0x3000, -100, 0x5000, 0x7000, 1, 0x8000, None, 0x6000,
                16, None) == EWORKSPACE
-    # more (token, vocabulary) tiles than a launch can hold: rejected before any launch
+    # more tiles than a launch of 512-thread workgroups can hold (2^23): rejected before any launch
     assert fwd(N=1 << 31, V=(1 << 31) - 1, nb=1 << 62) == EINVAL
+    assert fwd(N=1 << 24, V=1 << 15, nb=1 << 62) == EINVAL  # 2^16 token x 2^7 vocabulary tiles
+    assert fwd(N=1 << 31, V=100, nb=1 << 62) == EINVAL  # 2^23 token x 1 hidden tiles (dh)
+    assert fwd(N=4, V=(1 << 31) - 1, nb=1 << 62) == EINVAL  # 2^23 vocabulary x 1 hidden tiles (dW)
+    # forward chunking: split_hint below VWS_SPLIT_INVARIANT is invalid; the fixed modes size
+    # the partials by V alone
+    assert fwd(split=-2) == EINVAL
+    with pytest.raises(ValueError):
+        B.linear_workspace_bytes(0, 8, 64, 100, -2)
+    per_row = lambda sp, v: (B.linear_workspace_bytes(0, 512, 64, v, sp) - 512 * 4) / (512 * 8)
+    assert per_row(B.SPLIT_INVARIANT, 151936) == 149  # 594 vocabulary tiles in chunks of 4
+    assert per_row(5, 151936) == 5
+    assert B.linear_workspace_bytes(1, 8, 64, 100, B.SPLIT_INVARIANT) == 8 * 104 * 2
 
 
 def test_topk_validation(L):

@@ -9,7 +9,10 @@
   sampled vocabulary rows of dW;
 * 8548 tokens x vocabulary 16684 (34 token tiles, 66 vocabulary tiles): every
   element, with every branch of the forward's and the dz pass's block-to-tile
-  orders in use (whole groups and the tiles past them in both dimensions).
+  orders in use (whole groups and the tiles past them in both dimensions);
+* the batch-invariant forward chunkings (fixed 1024-column chunks, and a fixed
+  chunk count): every element against the oracle, and sub-batches whose logp,
+  stats and dh equal the full batch's rows bit for bit.
 
 dh and dW are compared with the conditioned factor 2^-8: the backward feeds dz to
 its two contractions rounded to bf16 (2^-9 relative per term), as the pages'
@@ -47,9 +50,9 @@ def _small(n=300, hidden=200, v=3000, seed=11):
     return h, Wm, t, g
 
 
-def _run(h, Wm, t, g, device, need_h=True, need_w=True):
+def _run(h, Wm, t, g, device, need_h=True, need_w=True, split=0):
     dh_, Wd, td, gd = h.to(device), Wm.to(device), t.to(device), g.to(device)
-    logp, stats = B.linear_logp_fwd(dh_, Wd, td, -100)
+    logp, stats = B.linear_logp_fwd(dh_, Wd, td, -100, split)
     dh, dW = B.linear_logp_bwd(dh_, Wd, td, stats, gd, -100, need_h=need_h, need_w=need_w)
     torch.cuda.synchronize()
     return logp, stats, dh, dW
@@ -147,6 +150,28 @@ def test_linear_tile_orders_all_elements(device):
                    "orders dh %d" % r0)
     dw_ref, dw_c = OL.linear_logp_bwd_dw_cond(hh, hw, ht, hg)
     _assert_ok(compare.check(f64(dW), dw_ref, dw_c, "bf16", GEMM_FACTOR), "orders dW")
+
+
+@pytest.mark.parametrize("split", [B.SPLIT_INVARIANT, 3])
+def test_linear_batch_invariant(device, split):
+    """Fixed vocabulary chunking (depending on V alone): 600 tokens (three token tiles, the last
+    ragged) over a 5000-column vocabulary, then sub-batches cut at other offsets; logp, stats and
+    dh of each sub-batch row must be the full batch's bits."""
+    h, Wm, t, g = _small(n=600, hidden=128, v=5000, seed=17)
+    logp, stats, dh, dW = _run(h, Wm, t, g, device, split=split)
+    hh, hw, ht, hg = f64(h), f64(Wm), t.numpy(), g.double().numpy()
+    lp, m, ls = OL.linear_logp_fwd(hh, hw, ht)
+    c = OL.cond_linear_fwd(hh, hw, ht)
+    _assert_ok(compare.check(f64(logp), lp, c, "f32"), "invariant logp")
+    _assert_ok(compare.check(f64(dh), OL.linear_logp_bwd_dh(hh, hw, ht, hg), OL.cond_linear_dh(hh, hw, ht, hg),
+                             "bf16", GEMM_FACTOR), "invariant dh")
+    _assert_ok(compare.check(f64(dW), OL.linear_logp_bwd_dw(hh, hw, ht, hg), OL.cond_linear_dw(hh, hw, ht, hg),
+                             "bf16", GEMM_FACTOR), "invariant dW")
+    for r0, r1 in ((0, 37), (300, 301), (513, 600)):
+        lp_s, st_s, dh_s, _ = _run(h[r0:r1], Wm, t[r0:r1], g[r0:r1], device, need_w=False, split=split)
+        assert torch.equal(lp_s, logp[r0:r1]), (split, r0, r1)
+        assert torch.equal(st_s, stats[r0:r1]), (split, r0, r1)
+        assert torch.equal(dh_s.view(torch.int16), dh[r0:r1].view(torch.int16)), (split, r0, r1)
 
 
 def test_linear_strided_rows_broadcast_g_and_partial_stage(device):

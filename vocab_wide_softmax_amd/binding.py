@@ -81,8 +81,8 @@ def lib():
             "vws_kl_bwd": (I32, [R, R, FP, FP, FP, I64, VP, VP, VP]),
             "vws_jsd_fwd": (I32, [R, R, ctypes.c_float, FP, FP, VP, SZ, I32, VP]),
             "vws_jsd_bwd": (I32, [R, R, ctypes.c_float, FP, FP, FP, I64, VP, VP, VP]),
-            "vws_linear_workspace_bytes": (SZ, [I32, I64, I64, I64]),
-            "vws_linear_logp_fwd": (I32, [VP, I64, VP, I64, I32, I64, I64, I64, VP, I64, FP, FP, VP, SZ, VP]),
+            "vws_linear_workspace_bytes": (SZ, [I32, I64, I64, I64, I32]),
+            "vws_linear_logp_fwd": (I32, [VP, I64, VP, I64, I32, I64, I64, I64, VP, I64, FP, FP, VP, SZ, I32, VP]),
             "vws_linear_logp_bwd": (I32, [VP, I64, VP, I64, I32, I64, I64, I64, VP, I64, FP, FP, I64, VP, VP, VP,
                                           SZ, VP]),
             "vws_strerror": (ctypes.c_char_p, [I32]),
@@ -375,15 +375,17 @@ def _lin_check(h, W, t):
         raise ValueError("targets must be a contiguous int64 [N] tensor")
 
 
-def linear_workspace_bytes(pass_, n, hidden, v):
-    r = lib().vws_linear_workspace_bytes(pass_, n, hidden, v)
+def linear_workspace_bytes(pass_, n, hidden, v, split_hint=0):
+    r = lib().vws_linear_workspace_bytes(pass_, n, hidden, v, split_hint)
     if r == ctypes.c_size_t(-1).value:
         raise ValueError("invalid workspace query")
     return r
 
 
-def linear_logp_fwd(h, W, t, ignore_index=-100):
-    """(logp fp32 [N], stats fp32 [N, 2]) of the target under logits h W^T -- vws_linear_logp_fwd."""
+def linear_logp_fwd(h, W, t, ignore_index=-100, split_hint=0):
+    """(logp fp32 [N], stats fp32 [N, 2]) of the target under logits h W^T -- vws_linear_logp_fwd.
+    split_hint: 0 automatic vocabulary chunking, k >= 1 k chunks, SPLIT_INVARIANT fixed
+    1024-column chunks (batch invariant)."""
     dev = _device(h, W, t)
     L = lib()
     _lin_check(h, W, t)
@@ -391,12 +393,13 @@ def linear_logp_fwd(h, W, t, ignore_index=-100):
     v = W.shape[0]
     logp = torch.empty(n, dtype=torch.float32, device=h.device)
     stats = torch.empty((n, 2), dtype=torch.float32, device=h.device)
-    nb = linear_workspace_bytes(0, n, hidden, v)
+    nb = linear_workspace_bytes(0, n, hidden, v, split_hint)
     ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=h.device)
     with torch.cuda.device(dev):
         _check("vws_linear_logp_fwd", L.vws_linear_logp_fwd(h.data_ptr(), h.stride(0), W.data_ptr(), W.stride(0),
                                                             VWS_BF16, n, hidden, v, t.data_ptr(), ignore_index,
-                                                            _ptr(logp), _ptr(stats), _ptr(ws), nb, _stream(dev)))
+                                                            _ptr(logp), _ptr(stats), _ptr(ws), nb, split_hint,
+                                                            _stream(dev)))
     return logp, stats
 
 

@@ -237,12 +237,14 @@ int jsd_check_pair(const vws_rows* s, const vws_rows* t, int64_t* N) {
 
 int64_t round_up8(int64_t x) { return (x + 7) / 8 * 8; }
 
+constexpr int64_t kLinMaxBlocks = (int64_t)1 << 23;  // 512-thread workgroups per linear-logp launch
+
 // Workspace layout of the fused linear-logp.
 //   forward:  part [N, chunks, 2] fp32, then zt [N] fp32
 //   backward: dz [N, round_up8(V)] bf16
-size_t lin_ws_bytes(int pass, int64_t N, int64_t V) {
+size_t lin_ws_bytes(int pass, int64_t N, int64_t V, int split_hint) {
   if (pass == 0) {
-    const size_t part = (size_t)N * (size_t)vws::lin_chunks(N, V) * 2 * sizeof(float);
+    const size_t part = (size_t)N * (size_t)vws::lin_chunks(N, V, split_hint) * 2 * sizeof(float);
     return (part + 255) / 256 * 256 + (size_t)N * sizeof(float);
   }
   return (size_t)N * (size_t)round_up8(V) * 2;
@@ -259,8 +261,11 @@ int lin_check(const void* h, int64_t ldh, const void* W, int64_t ldw, int dtype,
   if (!aligned(h, 16) || !aligned(W, 16) || !aligned(t, 8)) return VWS_ELAYOUT;
   int64_t x;
   if (!mul_ok(N, ldh, &x) || !mul_ok(V, ldw, &x) || !mul_ok(N, round_up8(V), &x)) return VWS_EINVAL;
-  // the backward launches one workgroup per 256 x 256 (token, vocabulary) tile
-  if (((N + 255) / 256) * ((V + 255) / 256) > (int64_t)INT32_MAX) return VWS_EINVAL;
+  // every launch has one 512-thread workgroup per 256 x 256 tile and a launch holds fewer than
+  // 2^32 work-items: (token, vocabulary) tiles for dz, (token, hidden) for dh, (vocabulary,
+  // hidden) for dW, and (token tile, chunk) pairs for the forward (at most the first)
+  const int64_t ntt = (N + 255) / 256, nvt = (V + 255) / 256, nht = (H + 255) / 256;
+  if (ntt * nvt >= kLinMaxBlocks || ntt * nht >= kLinMaxBlocks || nvt * nht >= kLinMaxBlocks) return VWS_EINVAL;
   return VWS_OK;
 }
 
@@ -268,21 +273,22 @@ int lin_check(const void* h, int64_t ldh, const void* W, int64_t ldw, int dtype,
 
 extern "C" {
 
-VWS_API size_t vws_linear_workspace_bytes(int pass, int64_t N, int64_t H, int64_t V) {
-  if ((pass != 0 && pass != 1) || N < 0 || H < 1 || V < 1) return (size_t)-1;
+VWS_API size_t vws_linear_workspace_bytes(int pass, int64_t N, int64_t H, int64_t V, int split_hint) {
+  if ((pass != 0 && pass != 1) || N < 0 || H < 1 || V < 1 || split_hint < VWS_SPLIT_INVARIANT) return (size_t)-1;
   if (N == 0) return 0;
-  return lin_ws_bytes(pass, N, V);
+  return lin_ws_bytes(pass, N, V, split_hint);
 }
 
 VWS_API int vws_linear_logp_fwd(const void* h, int64_t ldh, const void* W, int64_t ldw, int dtype, int64_t N,
                                 int64_t H, int64_t V, const int64_t* t, int64_t ignore_index, float* logp,
-                                float* stats, void* ws, size_t ws_bytes, void* stream) {
+                                float* stats, void* ws, size_t ws_bytes, int split_hint, void* stream) {
+  if (split_hint < VWS_SPLIT_INVARIANT) return VWS_EINVAL;
   int rc = lin_check(h, ldh, W, ldw, dtype, N, H, V, t);
   if (rc) return rc;
   if (N == 0) return VWS_OK;
   if (!logp || !stats) return VWS_EINVAL;
   if (!aligned(logp, 4) || !aligned(stats, 4)) return VWS_ELAYOUT;
-  const size_t need = lin_ws_bytes(0, N, V);
+  const size_t need = lin_ws_bytes(0, N, V, split_hint);
   if (!ws || ws_bytes < need) return VWS_EWORKSPACE;
   if (!aligned(ws, 16)) return VWS_ELAYOUT;
   vws::LinArgs p{};
@@ -297,10 +303,10 @@ VWS_API int vws_linear_logp_fwd(const void* h, int64_t ldh, const void* W, int64
   p.ignore_index = ignore_index;
   p.logp = logp;
   p.stats = stats;
-  const size_t part = (size_t)N * (size_t)vws::lin_chunks(N, V) * 2 * sizeof(float);
+  const size_t part = (size_t)N * (size_t)vws::lin_chunks(N, V, split_hint) * 2 * sizeof(float);
   p.part = static_cast<float*>(ws);
   p.zt = reinterpret_cast<float*>(static_cast<char*>(ws) + (part + 255) / 256 * 256);
-  hipError_t e = vws::launch_lin_fwd(p, static_cast<hipStream_t>(stream));
+  hipError_t e = vws::launch_lin_fwd(p, split_hint, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? VWS_OK : VWS_EHIP;
 }
 
@@ -314,7 +320,7 @@ VWS_API int vws_linear_logp_bwd(const void* h, int64_t ldh, const void* W, int64
   if (N == 0 || (!dh && !dW)) return VWS_OK;
   if (!stats || !g) return VWS_EINVAL;
   if (!aligned(stats, 4) || !aligned(g, 4) || !aligned(dh, 16) || !aligned(dW, 16)) return VWS_ELAYOUT;
-  const size_t need = lin_ws_bytes(1, N, V);
+  const size_t need = lin_ws_bytes(1, N, V, 0);
   if (!ws || ws_bytes < need) return VWS_EWORKSPACE;
   if (!aligned(ws, 16)) return VWS_ELAYOUT;
   vws::LinArgs p{};
@@ -521,6 +527,6 @@ VWS_API const char* vws_strerror(int status) {
   }
 }
 
-VWS_API int vws_version(void) { return 101; }
+VWS_API int vws_version(void) { return 102; }
 
 }  // extern "C"

@@ -116,8 +116,11 @@ struct GemmArgs {
   int64_t ldc, M, Nc, K;
 };
 
-int lin_chunks(int64_t N, int64_t V);
-hipError_t launch_lin_fwd(LinArgs p, hipStream_t stream);
+// Forward vocabulary chunking; split_hint as for the logits ops (0 automatic, >= 1 that many
+// chunks, -1 fixed 1024-column chunks).
+int32_t lin_tiles_per_chunk(int64_t N, int64_t V, int split_hint);
+int lin_chunks(int64_t N, int64_t V, int split_hint);
+hipError_t launch_lin_fwd(LinArgs p, int split_hint, hipStream_t stream);
 hipError_t launch_lin_bwd(LinArgs p, uint16_t* dh, uint16_t* dW, hipStream_t stream);
 
 // Workgroups per launch: kernels loop over virtual blocks beyond this, which

@@ -305,22 +305,40 @@ size_t lds_bytes() {
 }
 }  // namespace
 
-int lin_chunks(int64_t N, int64_t V) {
-  // one workgroup per (256-token tile, vocabulary chunk); aim for ~2 workgroups per CU
-  const int64_t ntt = (N + CfgNT::BN - 1) / CfgNT::BN;
-  const int64_t nvt = (V + CfgNT::BM - 1) / CfgNT::BM;
-  int64_t c = (512 + ntt - 1) / ntt;
-  if (c > nvt) c = nvt;
-  if (c < 1) c = 1;
-  return (int)c;
+// Vocabulary tiles per forward chunk. Automatic (split_hint 0): about 2 workgroups per CU for
+// this N, so the chunking, and the order in which a token's chunk partials merge, follow the
+// batch. split_hint >= 1 asks for that many chunks, and VWS_SPLIT_INVARIANT (-1) fixes chunks of
+// kLinInvariantTiles tiles (1024 vocabulary columns); both depend on V alone, so a token's logp
+// and statistics are the same bits in every batch (each logit is the same MFMA k-sequence
+// whichever tile holds it).
+namespace {
+constexpr int kLinInvariantTiles = 4;
 }
 
-hipError_t launch_lin_fwd(LinArgs p, hipStream_t stream) {
+int32_t lin_tiles_per_chunk(int64_t N, int64_t V, int split_hint) {
+  const int64_t nvt = (V + CfgNT::BM - 1) / CfgNT::BM;
+  if (split_hint == -1) return kLinInvariantTiles;
+  int64_t c;
+  if (split_hint >= 1) {
+    c = split_hint;
+  } else {
+    const int64_t ntt = (N + CfgNT::BN - 1) / CfgNT::BN;
+    c = (512 + ntt - 1) / ntt;
+  }
+  c = c < 1 ? 1 : (c > nvt ? nvt : c);
+  return (int32_t)((nvt + c - 1) / c);
+}
+
+int lin_chunks(int64_t N, int64_t V, int split_hint) {
+  const int64_t nvt = (V + CfgNT::BM - 1) / CfgNT::BM;
+  const int64_t tpc = lin_tiles_per_chunk(N, V, split_hint);
+  return (int)((nvt + tpc - 1) / tpc);
+}
+
+hipError_t launch_lin_fwd(LinArgs p, int split_hint, hipStream_t stream) {
   const int64_t ntt = (p.N + CfgNT::BN - 1) / CfgNT::BN;
-  const int64_t nvt = (p.V + CfgNT::BM - 1) / CfgNT::BM;
-  p.chunks = lin_chunks(p.N, p.V);
-  p.tiles_per_chunk = (int32_t)((nvt + p.chunks - 1) / p.chunks);
-  p.chunks = (int)((nvt + p.tiles_per_chunk - 1) / p.tiles_per_chunk);
+  p.tiles_per_chunk = lin_tiles_per_chunk(p.N, p.V, split_hint);
+  p.chunks = lin_chunks(p.N, p.V, split_hint);
   hipLaunchKernelGGL(lin_target_kernel, dim3((uint32_t)((p.N + 3) / 4)), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -92,8 +92,8 @@ class _JSD(torch.autograd.Function):
 
 class _LinearLogp(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, h, W, t, ignore_index):
-        logp, stats = B.linear_logp_fwd(h, W, t, ignore_index)
+    def forward(ctx, h, W, t, ignore_index, split_hint):
+        logp, stats = B.linear_logp_fwd(h, W, t, ignore_index, split_hint)
         ctx.save_for_backward(h, W, t, stats)
         ctx.ignore_index = ignore_index
         return logp
@@ -103,14 +103,15 @@ class _LinearLogp(torch.autograd.Function):
         h, W, t, stats = ctx.saved_tensors
         nh, nw = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
         if not (nh or nw):
-            return None, None, None, None
+            return None, None, None, None, None
         dh, dW = B.linear_logp_bwd(h, W, t, stats, g, ctx.ignore_index, need_h=nh, need_w=nw)
-        return dh, dW, None, None
+        return dh, dW, None, None, None
 
 
-def linear_logp(h, W, t, ignore_index=-100):
-    """Per-token log p_t under logits h W^T, without materialising the logits (bf16 h, W)."""
-    return _LinearLogp.apply(h, W, t, ignore_index)
+def linear_logp(h, W, t, ignore_index=-100, split_hint=0):
+    """Per-token log p_t under logits h W^T, without materialising the logits (bf16 h, W).
+    ``split_hint=SPLIT_INVARIANT`` (or any k >= 1) makes logp, and so dh, batch invariant."""
+    return _LinearLogp.apply(h, W, t, ignore_index, split_hint)
 
 
 def logprobs(z, t, ignore_index=-100, split_hint=0):
