@@ -2,6 +2,7 @@
 
 * small ragged shape (300 tokens, hidden 200, vocabulary 3000: partial tiles in
   every dimension, ignored targets): every element of logp, lse, dh and dW;
+* degenerate shapes: one token, a one-column vocabulary, hidden size 8;
 * an out-of-range target: NaN logp and dh row, NaN dW (the row's dz is NaN);
 * the full hidden and vocabulary widths (4096 x 151936) at 512 tokens: every
   logp and dh element, sampled dW rows;
@@ -150,6 +151,29 @@ def test_linear_tile_orders_all_elements(device):
                    "orders dh %d" % r0)
     dw_ref, dw_c = OL.linear_logp_bwd_dw_cond(hh, hw, ht, hg)
     _assert_ok(compare.check(f64(dW), dw_ref, dw_c, "bf16", GEMM_FACTOR), "orders dW")
+
+
+@pytest.mark.parametrize("n,hidden,v", [(1, 8, 1), (3, 8, 1), (1, 8, 7), (2, 16, 300)])
+def test_linear_degenerate_shapes(device, n, hidden, v):
+    """One token, a one-column vocabulary (logp 0, zero gradients: p = 1 at the target) and the
+    smallest hidden size; every element against the oracle."""
+    gen = torch.Generator().manual_seed(n * 1000 + v)
+    h = torch.randn(n, hidden, generator=gen).to(torch.bfloat16)
+    Wm = (0.3 * torch.randn(v, hidden, generator=gen)).to(torch.bfloat16)
+    t = torch.randint(0, v, (n,), generator=gen)
+    g = torch.randn(n, generator=gen)
+    logp, stats, dh, dW = _run(h, Wm, t, g, device)
+    hh, hw, ht, hg = f64(h), f64(Wm), t.numpy(), g.double().numpy()
+    lp, m, ls = OL.linear_logp_fwd(hh, hw, ht)
+    c = OL.cond_linear_fwd(hh, hw, ht)
+    _assert_ok(compare.check(f64(logp), lp, c, "f32"), "degenerate logp")
+    _assert_ok(compare.check(f64(dh), OL.linear_logp_bwd_dh(hh, hw, ht, hg), OL.cond_linear_dh(hh, hw, ht, hg),
+                             "bf16", GEMM_FACTOR), "degenerate dh")
+    _assert_ok(compare.check(f64(dW), OL.linear_logp_bwd_dw(hh, hw, ht, hg), OL.cond_linear_dw(hh, hw, ht, hg),
+                             "bf16", GEMM_FACTOR), "degenerate dW")
+    if v == 1:
+        assert (logp.cpu() == 0).all()
+        assert torch.count_nonzero(dh) == 0 and torch.count_nonzero(dW) == 0
 
 
 @pytest.mark.parametrize("split", [B.SPLIT_INVARIANT, 3])
