@@ -118,6 +118,46 @@ __device__ __forceinline__ void dma_tile(const Operand& op, int64_t r0, int64_t 
 }
 
 // LDS byte address of a generic pointer into the workgroup's LDS.
+// Buffer-resource form of dma_tile for interior tiles: the resource covers one stage of the
+// operand tile (the rows r0 .. r0 + R of a ROWK operand from column k0, or the k-rows k0 .. k0 + BK
+// of a KROW operand from column r0), so each lane's byte offset inside it is the same in every
+// stage and only the scalar base moves. The loads take the buffer path (buffer_load ... lds),
+// which on gfx950 costs the main loop less than the flat-address form. Usable when a stage spans
+// fewer than 2^32 bytes (stage_span_fits).
+template <int L, int R, int BK>
+__device__ __forceinline__ bool stage_span_fits(const Operand& op) {
+  return (int64_t)(L == ROWK ? R : BK) * op.ld * 2 <= (int64_t)0xFFFFFFFF;
+}
+
+template <int L, int R, int BK>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stage_rsrc(const Operand& op, int64_t r0, int64_t k0) {
+  const uint16_t* base = L == ROWK ? op.base + r0 * op.ld + k0 : op.base + k0 * op.ld + r0;
+  const int64_t span = (int64_t)(L == ROWK ? R : BK) * op.ld * 2;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(uint32_t)span, 0x00020000);
+}
+
+template <int L, int R, int BK, int NW, int NINSTR>
+__device__ __forceinline__ void dma_tile_buf(const Operand& op, int64_t r0, int64_t k0, char* lds_tile, int wave,
+                                             int lane) {
+  const __amdgpu_buffer_rsrc_t rsrc = stage_rsrc<L, R, BK>(op, r0, k0);
+#pragma unroll
+  for (int j = 0; j < NINSTR; ++j) {
+    const int instr = wave * NINSTR + j;
+    const int o = instr * 1024 + lane * 16;  // byte offset this lane fills
+    uint32_t voff;
+    if constexpr (L == ROWK) {
+      const int r = o / (BK * 2), pc = (o % (BK * 2)) / 16;
+      const int c = pc ^ swz_rowk<BK>(r);
+      voff = (uint32_t)(((int64_t)r * op.ld + c * 8) * 2);
+    } else {
+      const int kr = o / (R * 2), pc = (o % (R * 2)) / 16;
+      const int c = pc ^ swz_krow(kr);
+      voff = (uint32_t)(((int64_t)kr * op.ld + c * 8) * 2);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds_tile + instr * 1024), 16, (int)voff, 0, 0, 0);
+  }
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
@@ -229,9 +269,10 @@ __device__ __forceinline__ void stage_ready(int s, int nk) {
 // one run; at the last slice of stage s the workgroup waits for stage s + 1, refills the
 // stage-s buffer with stage s + NSTAGE, and reads stage s + 1's first fragments before
 // stage s's last MFMAs.
-template <class C, bool EDGE>
+template <class C, bool EDGE, bool BUF>
 __device__ __forceinline__ void mainloop_t(const Operand& A, const Operand& B, int64_t m0, int64_t n0, int64_t K,
                                            char* lds, Acc<C>& acc) {
+  static_assert(!(EDGE && BUF), "the buffer loads serve interior tiles");
   constexpr int KQ = C::BK / 16;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS targets stay scalar
@@ -242,8 +283,13 @@ __device__ __forceinline__ void mainloop_t(const Operand& A, const Operand& B, i
   auto issue = [&](int s) {
     char* st = lds + (s % C::NSTAGE) * C::STAGE_BYTES;
     const int64_t k0 = (int64_t)s * C::BK;
-    dma_tile<C::LA, C::BM, C::BK, C::NW, C::A_INSTR, EDGE>(A, m0, k0, st, wave, lane);
-    dma_tile<C::LB, C::BN, C::BK, C::NW, C::B_INSTR, EDGE>(B, n0, k0, st + C::A_BYTES, wave, lane);
+    if constexpr (BUF) {
+      dma_tile_buf<C::LA, C::BM, C::BK, C::NW, C::A_INSTR>(A, m0, k0, st, wave, lane);
+      dma_tile_buf<C::LB, C::BN, C::BK, C::NW, C::B_INSTR>(B, n0, k0, st + C::A_BYTES, wave, lane);
+    } else {
+      dma_tile<C::LA, C::BM, C::BK, C::NW, C::A_INSTR, EDGE>(A, m0, k0, st, wave, lane);
+      dma_tile<C::LB, C::BN, C::BK, C::NW, C::B_INSTR, EDGE>(B, n0, k0, st + C::A_BYTES, wave, lane);
+    }
   };
   auto stage_a = [&](int s) -> const char* { return lds + (s % C::NSTAGE) * C::STAGE_BYTES; };
 
@@ -276,13 +322,16 @@ __device__ __forceinline__ void mainloop_t(const Operand& A, const Operand& B, i
 }
 
 // Interior tiles (every row of both operand tiles exists and K is a whole number of stages)
-// take the unchecked loads.
+// take the unchecked loads, through buffer resources when a stage of each operand spans fewer
+// than 2^32 bytes.
 template <class C>
 __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int64_t m0, int64_t n0, int64_t K,
                                          char* lds, Acc<C>& acc) {
   const bool interior = m0 + C::BM <= A.rows && n0 + C::BN <= B.rows && K % C::BK == 0 && A.K >= K && B.K >= K;
-  if (interior) mainloop_t<C, false>(A, B, m0, n0, K, lds, acc);
-  else mainloop_t<C, true>(A, B, m0, n0, K, lds, acc);
+  const bool fits = stage_span_fits<C::LA, C::BM, C::BK>(A) && stage_span_fits<C::LB, C::BN, C::BK>(B);
+  if (interior && fits) mainloop_t<C, false, true>(A, B, m0, n0, K, lds, acc);
+  else if (interior) mainloop_t<C, false, false>(A, B, m0, n0, K, lds, acc);
+  else mainloop_t<C, true, false>(A, B, m0, n0, K, lds, acc);
 }
 
 // Row / column of accumulator v of block (i, j) for this lane, relative to the wave tile.
