@@ -206,83 +206,96 @@ __device__ __forceinline__ float lane_f(float v, int k) {
 // fall in the tile, G is a butterfly sum over the wave's lanes (the same value, bit for bit,
 // in every lane and every run), and each group of 8 columns adds the hits it owns in slot
 // order. No LDS and no barriers: a tile costs about what the single-id backward's does.
-template <int DT, bool VEC, int UB>
-__global__ __launch_bounds__(kTopkBlock) void topk_bwd_small_kernel(TopkArgs p) {
+// One tile (row, groups g0 .. g0 + TG) of the small-K backward. FULL: every group of the tile is
+// a whole 16-byte group (vector loads and stores, no bounds checks); kept as its own instance so
+// the interior tile's code has no predicated element loads to merge with.
+template <int DT, bool VEC, int UB, bool FULL>
+__device__ __forceinline__ void topk_small_tile(const TopkArgs& p, int64_t row, int32_t g0, int tid, int lane) {
   constexpr int ES = ElemSize<DT>::value;
   constexpr int TG = kTopkBlock * UB;  // groups of 8 columns per tile
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int32_t tpr = p.tiles_per_row;
-  const int64_t total = p.N * tpr;
   const int32_t V = (int32_t)p.V;
   const int32_t G = (V + 7) / 8;
   const int32_t g_full = VEC ? V / 8 : 0;
   const int32_t K = p.K;
+  const char* ra = row_ptr<DT>(p.a, row);
+  const int32_t g = g0 + tid;
+  // The slot and row-constant loads go out first, then the tile's logit loads. Loads complete
+  // in issue order, so the slot logic below (ballots, the G butterfly, the hit masks) waits only
+  // for the small loads and runs while the tile is in flight: one memory latency per tile.
+  int64_t tv = p.ignore_index;
+  float gl = 0.0f;
+  if (lane < K) {
+    tv = topk_id(p, row, lane);
+    gl = p.g[row * p.g_sr + (int64_t)lane * p.g_sk];
+  }
+  const float m = p.stats[2 * row], ls = p.stats[2 * row + 1];
+  __builtin_amdgcn_sched_barrier(0);
+  RawGroup<DT> w[UB];
+  float x[UB][8];
+  if constexpr (FULL) {
+#pragma unroll
+    for (int u = 0; u < UB; ++u) load_group_raw<DT>(ra, g + u * kTopkBlock, w[u]);
+  } else {
+    topk_load<DT, false, UB>(ra, g, G, V, g_full, x);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  const bool live = lane < K && tv != p.ignore_index;
+  const bool oor = live && (tv < 0 || tv >= V);
+  const bool in_tile = live && !oor && (tv >> 3) >= g0 && (tv >> 3) < g0 + TG;
+  const bool zero_row = __ballot(live) == 0ull, nan_row = __ballot(oor) != 0ull;
+  const uint64_t hits = __ballot(in_tile);
+  float Gs = live && !oor ? gl : 0.0f;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) Gs += __shfl_xor(Gs, off, 64);
+
+  char* oa = p.dz + row * (int64_t)V * ES;
+  const float qnan = __builtin_nanf("");
+  if constexpr (FULL) {
+#pragma unroll
+    for (int u = 0; u < UB; ++u) raw_to_float<DT>(w[u], x[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < UB; ++u) {
+    const int32_t gu = g + u * kTopkBlock;
+    if (!FULL && gu >= G) break;
+    float y[8], hu[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) hu[j] = 0.0f;
+    for (uint64_t hm = hits; hm; hm &= hm - 1) {  // slot order
+      const int k = __builtin_ctzll(hm);
+      const int32_t t = __builtin_amdgcn_readlane((int32_t)tv, k);
+      const int32_t rel = (t >> 3) - g0;
+      if (rel / kTopkBlock != u) continue;
+      const float gk = lane_f(gl, k);
+      const float add = (rel % kTopkBlock) == tid ? gk : 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j == (t & 7)) hu[j] += add;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float pj = expf_fast((x[u][j] - m) - ls);
+      y[j] = zero_row ? 0.0f : (nan_row ? qnan : __builtin_fmaf(-Gs, pj, hu[j]));
+    }
+    if constexpr (FULL) store_group_vec<DT>(oa, gu, y);
+    else store_group<DT, true>(oa, gu, V, g_full, y);
+  }
+}
+
+template <int DT, bool VEC, int UB>
+__global__ __launch_bounds__(kTopkBlock) void topk_bwd_small_kernel(TopkArgs p) {
+  constexpr int TG = kTopkBlock * UB;  // groups of 8 columns per tile
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int32_t tpr = p.tiles_per_row;
+  const int64_t total = p.N * tpr;
+  const int32_t g_full = VEC ? (int32_t)(p.V / 8) : 0;
   for (int64_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
     const int64_t row = udiv(vb, tpr);
     const int32_t tile = (int32_t)(vb - row * tpr);
     const int32_t g0 = tile * TG;
-    const char* ra = row_ptr<DT>(p.a, row);
-    const int32_t g = g0 + tid;
-    const bool full = VEC && g0 + TG <= g_full;
-    // the tile's loads and the slot loads first: one memory latency per tile
-    RawGroup<DT> w[UB];
-    float x[UB][8];
-    if (full) {
-#pragma unroll
-      for (int u = 0; u < UB; ++u) load_group_raw<DT>(ra, g + u * kTopkBlock, w[u]);
-    } else {
-      topk_load<DT, false, UB>(ra, g, G, V, g_full, x);
-    }
-    int64_t tv = p.ignore_index;
-    float gl = 0.0f;
-    if (lane < K) {
-      tv = topk_id(p, row, lane);
-      gl = p.g[row * p.g_sr + (int64_t)lane * p.g_sk];
-    }
-    const float m = p.stats[2 * row], ls = p.stats[2 * row + 1];
-    __builtin_amdgcn_sched_barrier(0);
-
-    const bool live = lane < K && tv != p.ignore_index;
-    const bool oor = live && (tv < 0 || tv >= V);
-    const bool in_tile = live && !oor && (tv >> 3) >= g0 && (tv >> 3) < g0 + TG;
-    const bool zero_row = __ballot(live) == 0ull, nan_row = __ballot(oor) != 0ull;
-    const uint64_t hits = __ballot(in_tile);
-    float Gs = live && !oor ? gl : 0.0f;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) Gs += __shfl_xor(Gs, off, 64);
-
-    char* oa = p.dz + row * (int64_t)V * ES;
-    const float qnan = __builtin_nanf("");
-    if (full) {
-#pragma unroll
-      for (int u = 0; u < UB; ++u) raw_to_float<DT>(w[u], x[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < UB; ++u) {
-      const int32_t gu = g + u * kTopkBlock;
-      if (!full && gu >= G) break;
-      float y[8], hu[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) hu[j] = 0.0f;
-      for (uint64_t hm = hits; hm; hm &= hm - 1) {  // slot order
-        const int k = __builtin_ctzll(hm);
-        const int32_t t = __builtin_amdgcn_readlane((int32_t)tv, k);
-        const int32_t rel = (t >> 3) - g0;
-        if (rel / kTopkBlock != u) continue;
-        const float gk = lane_f(gl, k);
-        const float add = (rel % kTopkBlock) == tid ? gk : 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (j == (t & 7)) hu[j] += add;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float pj = expf_fast((x[u][j] - m) - ls);
-        y[j] = zero_row ? 0.0f : (nan_row ? qnan : __builtin_fmaf(-Gs, pj, hu[j]));
-      }
-      if (full) store_group_vec<DT>(oa, gu, y);
-      else store_group<DT, true>(oa, gu, V, g_full, y);
-    }
+    if (VEC && g0 + TG <= g_full) topk_small_tile<DT, VEC, UB, true>(p, row, g0, tid, lane);
+    else topk_small_tile<DT, VEC, UB, false>(p, row, g0, tid, lane);
   }
 }
 
