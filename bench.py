@@ -447,7 +447,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-linear", action="store_true", help="skip the fused linear-logp workload")
     ap.add_argument("--no-extras", action="store_true", help="skip top-k, JSD, fp16 and batch-invariant timings")
