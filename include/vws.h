@@ -23,7 +23,9 @@
  * - All data pointers are DEVICE pointers on the current HIP device; the
  *   caller owns every buffer. Work is enqueued on `stream` (a hipStream_t; NULL
  *   is the null stream). No call synchronises, allocates device memory or
- *   keeps state between calls; calls are reentrant.
+ *   keeps state between calls; calls are reentrant. (The one exception is
+ *   vws_kl_fwd_noalloc, which uses a static per-GPU buffer in place of a
+ *   workspace argument; see there.)
  * - Return value: VWS_OK (0) or a negative vws_status. Argument and layout
  *   errors are detected on the host before anything is launched; VWS_EHIP
  *   reports a failed launch. Data-dependent conditions never produce a status
@@ -73,7 +75,8 @@ typedef enum vws_status {
   VWS_EDTYPE = -2,     /* unknown dtype, or A and B of different dtypes */
   VWS_ELAYOUT = -3,    /* col_stride != 1, negative stride, misaligned pointer, address overflow */
   VWS_EWORKSPACE = -4, /* workspace smaller than vws_workspace_bytes() */
-  VWS_EHIP = -5        /* a HIP launch failed */
+  VWS_EHIP = -5,       /* a HIP launch failed */
+  VWS_ESCRATCH = -6    /* vws_kl_fwd_noalloc: the split needs more than VWS_NOALLOC_SCRATCH_BYTES */
 } vws_status;
 
 typedef enum vws_dtype { VWS_F32 = 0, VWS_BF16 = 1, VWS_F16 = 2 } vws_dtype;
@@ -210,6 +213,23 @@ VWS_API int vws_entropy_bwd(const vws_rows* z, const float* stats, const float* 
  */
 VWS_API int vws_kl_fwd(const vws_rows* a, const vws_rows* b, float* kl, float* stats, void* ws, size_t ws_bytes,
                        int split_hint, void* stream);
+
+/*
+ * vws_kl_fwd without a workspace argument, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. It
+ * computes exactly what vws_kl_fwd computes with the same split_hint (same kernels, same
+ * bits), taking the split path's partial states from a static device buffer of
+ * VWS_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until the process
+ * ends; it calls no allocating routine. A split needing more than that (N * P * 24 bytes for
+ * P > 1 vocabulary parts) returns VWS_ESCRATCH before anything is launched. Every call on one
+ * GPU shares that GPU's buffer, and the buffer keeps the last call's contents (each call writes
+ * every partial state it reads, so nothing needs clearing): calls that overlap on one GPU (on
+ * different streams, or from different threads without ordering) race and must not be made.
+ */
+#define VWS_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+VWS_API int vws_kl_fwd_noalloc(const vws_rows* a, const vws_rows* b, float* kl, float* stats, int split_hint,
+                               void* stream);
 
 /*
  * da_j = g p_A,j (log p_A,j - log p_B,j - KL)  (0 where a_j = -inf),

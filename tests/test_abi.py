@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(L):
     assert len(names) >= 10
     for n in names:
         assert hasattr(L, n), n
-    assert L.vws_version() == 102
+    assert L.vws_version() == 103
 
 
 def test_strerror(L):
@@ -261,3 +261,21 @@ def test_missing_library_fails_loudly(monkeypatch):
         z = torch.zeros(4, 16, dtype=torch.bfloat16, device="cuda:0")
         with pytest.raises(ImportError):
             B.entropy_fwd(z)
+
+
+def test_kl_fwd_noalloc_validation(L):
+    """The allocation-free KL forward validates like vws_kl_fwd and rejects, before any launch,
+    a split whose partial states exceed the static scratch."""
+    a, b = _rows(), _rows(dtype=B.VWS_F32)
+    f = L.vws_kl_fwd_noalloc
+    assert f(ctypes.byref(a), ctypes.byref(b), 0x2000, 0x3000, 0, None) == EDTYPE
+    assert f(ctypes.byref(a), ctypes.byref(a), 0, 0x3000, 0, None) == EINVAL
+    assert f(ctypes.byref(a), ctypes.byref(a), 0x2000, 0x3000, -2, None) == EINVAL
+    e = _rows(n_outer=0, data=0)
+    assert f(ctypes.byref(e), ctypes.byref(e), 0, 0, 0, None) == 0  # empty batch
+    # 8192 rows x 64 parts x 6 floats = 12.6 MB of partial states > 8 MiB
+    big = _rows(n_outer=8192, V=75968, s_outer=75968)
+    need = B.workspace_bytes(B.OP_KL, 8192, 75968, 64)
+    assert need > B.NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), ctypes.byref(big), 0x2000, 0x3000, 64, None) == -6
+    assert "static scratch" in B.strerror(-6)

@@ -23,6 +23,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvws.so"
 
 VWS_F32, VWS_BF16, VWS_F16 = 0, 1, 2
 OP_LOGPROBS, OP_ENTROPY, OP_KL, OP_JSD = 0, 1, 2, 3
+NOALLOC_SCRATCH_BYTES = 8 << 20  # VWS_NOALLOC_SCRATCH_BYTES of vws.h
 SPLIT_INVARIANT = -1  # fixed V-only vocabulary segments: results independent of the batch
 _DTYPES = {torch.float32: VWS_F32, torch.bfloat16: VWS_BF16, torch.float16: VWS_F16}
 
@@ -78,6 +79,7 @@ def lib():
             "vws_entropy_fwd": (I32, [R, FP, FP, VP, SZ, I32, VP]),
             "vws_entropy_bwd": (I32, [R, FP, FP, FP, I64, VP, VP]),
             "vws_kl_fwd": (I32, [R, R, FP, FP, VP, SZ, I32, VP]),
+            "vws_kl_fwd_noalloc": (I32, [R, R, FP, FP, I32, VP]),
             "vws_kl_bwd": (I32, [R, R, FP, FP, FP, I64, VP, VP, VP]),
             "vws_jsd_fwd": (I32, [R, R, ctypes.c_float, FP, FP, VP, SZ, I32, VP]),
             "vws_jsd_bwd": (I32, [R, R, ctypes.c_float, FP, FP, FP, I64, VP, VP, VP]),
@@ -318,6 +320,20 @@ def kl_fwd(a, b, split_hint=0):
     with torch.cuda.device(dev):
         _check("vws_kl_fwd", L.vws_kl_fwd(ctypes.byref(ra), ctypes.byref(rb), _ptr(kl), _ptr(stats), _ptr(ws), nb,
                                           split_hint, _stream(dev)))
+    return kl, stats
+
+
+def kl_fwd_noalloc(a, b, split_hint=0):
+    """(KL(A||B) fp32 [N...], stats fp32 [N, 4]) -- vws_kl_fwd_noalloc: the same results as
+    kl_fwd, with the split's partial states in the library's static per-GPU buffer (the
+    outputs are still allocated here, by torch)."""
+    dev = _device(a, b)
+    L = lib()
+    kl, stats = _outputs(a, 4)
+    ra, rb = rows(a), rows(b)
+    with torch.cuda.device(dev):
+        _check("vws_kl_fwd_noalloc", L.vws_kl_fwd_noalloc(ctypes.byref(ra), ctypes.byref(rb), _ptr(kl), _ptr(stats),
+                                                          split_hint, _stream(dev)))
     return kl, stats
 
 

@@ -1,13 +1,45 @@
 // api.hip -- the C ABI of libvws (declared in include/vws.h): argument and
 // layout validation on the host, then asynchronous launches on the caller's
-// stream. Nothing here allocates, synchronises or keeps state.
+// stream. Nothing here allocates or synchronises; the only state is the static
+// scratch buffer of vws_kl_fwd_noalloc and its per-device address.
 #include <limits.h>
 #include <stdint.h>
+
+#include <atomic>
+#include <mutex>
 
 #include "launch.h"
 #include "vws.h"
 
+// Scratch of vws_kl_fwd_noalloc: the split path's partial states go here instead of into a
+// caller-supplied workspace. Each GPU the library runs on holds its own copy until the process
+// ends. In host code `scratch` names a host-side stand-in, not device memory: host code uses only
+// the device address that hipGetSymbolAddress returns for it (kept per device below).
+static __device__ __align__(256) float scratch[VWS_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device, resolved once per device with that device
+// current (the calling thread's current device is the one the caller launches on).
+int scratch_addr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return VWS_EHIP;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return VWS_EHIP;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return VWS_OK;
+}
 
 using vws::BwdArgs;
 using vws::FwdArgs;
@@ -112,8 +144,11 @@ int parts_for(int op, int64_t N, int64_t V, int hint) {
 }
 
 // stats_only (logprobs): write the row statistics but no per-row output, for the multi-id forward.
+// static_ws: take the workspace from the library's static scratch (vws_kl_fwd_noalloc) instead of
+// ws / ws_bytes.
 int fwd_common(int op, const vws_rows* a, const vws_rows* b, const vws_ids* t, int64_t ignore_index, float* out,
-               float* stats, void* ws, size_t ws_bytes, int split_hint, void* stream, bool stats_only = false) {
+               float* stats, void* ws, size_t ws_bytes, int split_hint, void* stream, bool stats_only = false,
+               bool static_ws = false) {
   int64_t N, Nb;
   int rc = check_rows(a, &N);
   if (rc) return rc;
@@ -130,6 +165,15 @@ int fwd_common(int op, const vws_rows* a, const vws_rows* b, const vws_ids* t, i
   const int P = parts_for(op, N, a->V, split_hint);
   if (N * (int64_t)P > (int64_t)INT32_MAX) return VWS_EINVAL;
   const size_t need = P > 1 ? (size_t)N * (size_t)P * (size_t)state_floats(op) * sizeof(float) : 0;
+  if (static_ws) {
+    if (need > (size_t)VWS_NOALLOC_SCRATCH_BYTES) return VWS_ESCRATCH;
+    ws = nullptr;
+    ws_bytes = 0;
+    if (need > 0) {
+      if ((rc = scratch_addr(&ws))) return rc;
+      ws_bytes = (size_t)VWS_NOALLOC_SCRATCH_BYTES;
+    }
+  }
   if (need > 0 && (!ws || ws_bytes < need)) return VWS_EWORKSPACE;
   if (need > 0 && !aligned(ws, 4)) return VWS_ELAYOUT;
 
@@ -383,6 +427,11 @@ VWS_API int vws_kl_fwd(const vws_rows* a, const vws_rows* b, float* kl, float* s
   return fwd_common(VWS_OP_KL, a, b, nullptr, 0, kl, stats, ws, ws_bytes, split_hint, stream);
 }
 
+VWS_API int vws_kl_fwd_noalloc(const vws_rows* a, const vws_rows* b, float* kl, float* stats, int split_hint,
+                               void* stream) {
+  return fwd_common(VWS_OP_KL, a, b, nullptr, 0, kl, stats, nullptr, 0, split_hint, stream, false, true);
+}
+
 VWS_API int vws_kl_bwd(const vws_rows* a, const vws_rows* b, const float* stats, const float* kl, const float* g,
                        int64_t g_stride, void* da, void* db, void* stream) {
   return bwd_common(VWS_OP_KL, a, b, nullptr, 0, stats, kl, g, g_stride, da, db, stream);
@@ -523,10 +572,11 @@ VWS_API const char* vws_strerror(int status) {
     case VWS_ELAYOUT: return "unsupported layout (col_stride != 1, negative stride, misaligned pointer or address overflow)";
     case VWS_EWORKSPACE: return "workspace too small";
     case VWS_EHIP: return "HIP launch failed";
+    case VWS_ESCRATCH: return "the split needs more than the library's static scratch (VWS_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
 
-VWS_API int vws_version(void) { return 102; }
+VWS_API int vws_version(void) { return 103; }
 
 }  // extern "C"
