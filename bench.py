@@ -14,7 +14,14 @@ single-read method must move: 18 x 1.2447 GB per step), ms per step, the
 per-op split (from an untimed pass with events around every launch), a roofline
 object for the dominant kernel (the KL(A||B) backward, bracketed by HIP events
 on its stream inside the timed steps), and the fp64 oracle's throughput on a
-bounded sample of the same workload on the host cores.
+bounded sample of the same workload on the host cores. Further legs, each in
+its own object: the 1024 x 75968 pair (split-vocabulary path) with and without
+a flush of the 256 MB Infinity Cache before every op, the fp32 causal-shift
+view [4, 2049, 75968][:, :-1, :] read in place, extra peak device memory per op,
+top-k logprobs, the JSD, fp16 and batch-invariant steps, and the fused
+linear-logp with its own oracle baseline. The oracle leg also compares the
+device results with the oracle on sampled rows of every workload and reports
+the strict-rule misses per op and config.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --calibrate          # plain copies of known size, for counter scaling
@@ -239,27 +246,187 @@ def extras_bench(wl, device, steps=15, warmup=30):
     return out
 
 
+# ------------------------------------------------------- per-op legs (configs 1 and 3)
+
+def op_fwd(B, op, a, b, t, split=0):
+    """Forward of one op through the C ABI: (per-row output, saved statistics)."""
+    if op == "logprobs":
+        return B.logprobs_fwd(a, t, -100, split)
+    if op == "entropy":
+        return B.entropy_fwd(a, split)
+    x, y = (a, b) if op == "kl_ab" else (b, a)
+    return B.kl_fwd(x, y, split)
+
+
+def op_bwd(B, op, a, b, t, g, out, st):
+    """Backward of one op: the tuple of gradients (two for KL)."""
+    if op == "logprobs":
+        return (B.logprobs_bwd(a, t, st, g, -100),)
+    if op == "entropy":
+        return (B.entropy_bwd(a, st, out, g),)
+    x, y = (a, b) if op == "kl_ab" else (b, a)
+    return B.kl_bwd(x, y, st, out, g)
+
+
+def op_times(ops, a, b, t, g, steps, warmup, flush=None):
+    """Median fwd and bwd ms per op, the ops interleaved (the pages interleave their timed runs).
+    With `flush`, a device buffer of 512 MB is overwritten before every op's forward, outside the
+    event interval, so that the op starts with nothing of its inputs in the 256 MB Infinity Cache
+    or the L2 caches. All iterations are enqueued before one synchronisation."""
+    import torch
+
+    from vocab_wide_softmax_amd import binding as B
+
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for op in ops:
+            out, st = op_fwd(B, op, a, b, t)
+            op_bwd(B, op, a, b, t, g[op], out, st)
+    evs = {op: [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)] for op in ops}
+    torch.cuda.synchronize()
+    for i in range(steps):
+        for op in ops:
+            if flush is not None:
+                flush.zero_()
+            e = evs[op][i]
+            e[0].record(stream)
+            out, st = op_fwd(B, op, a, b, t)
+            e[1].record(stream)
+            grads = op_bwd(B, op, a, b, t, g[op], out, st)
+            e[2].record(stream)
+            del out, st, grads
+    torch.cuda.synchronize()
+    res = {}
+    for op in ops:
+        f = sorted(e[0].elapsed_time(e[1]) for e in evs[op])
+        bw = sorted(e[1].elapsed_time(e[2]) for e in evs[op])
+        res[op] = (f[steps // 2], bw[steps // 2])
+    return res
+
+
+def _op_entry(f_ms, b_ms, nbytes):
+    gbs = nbytes / ((f_ms + b_ms) * 1e-3) / 1e9
+    return {"fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "fwd_bwd_ms": round(f_ms + b_ms, 4),
+            "bytes": nbytes, "GB/s": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
+
+
+def memory_report(ops, a, b, t, g):
+    """Device memory of one fwd+bwd per op, with the inputs already resident: the peak growth
+    (torch.cuda.max_memory_allocated), the bytes of the gradients and of the per-row outputs and
+    statistics the op returns, and the extra peak beyond those (workspace and anything else the
+    op needs), which the pages report as "extra peak memory"."""
+    import torch
+
+    from vocab_wide_softmax_amd import binding as B
+
+    rep = {}
+    for op in ops:
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        out, st = op_fwd(B, op, a, b, t)
+        grads = op_bwd(B, op, a, b, t, g[op], out, st)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        grad_bytes = sum(x.numel() * x.element_size() for x in grads if x is not None)
+        out_bytes = out.numel() * out.element_size() + st.numel() * st.element_size()
+        rep[op] = {"peak_growth_bytes": int(peak), "grad_bytes": int(grad_bytes), "output_bytes": int(out_bytes),
+                   "extra_peak_bytes": int(max(0, peak - grad_bytes - out_bytes)),
+                   "workspace_bytes": int(B.workspace_bytes(B.OP_KL if op.startswith("kl") else
+                                                            (B.OP_LOGPROBS if op == "logprobs" else B.OP_ENTROPY),
+                                                            out.numel(), a.shape[-1]))}
+        del out, st, grads
+    return rep
+
+
+def pair1024_leg(device, steps, warmup, wl=None):
+    """The 1024 x 75968 bf16 pair (config 1: the shape of one tensor-parallel rank of a 151936-token
+    vocabulary, where the forward splits each row's vocabulary and an in-GPU combine merges the
+    parts): the four ops fwd+bwd, timed as they are (inputs of 156 MB each can sit in the 256 MB
+    Infinity Cache) and with the cache flushed before every op."""
+    import torch
+
+    from vocab_wide_softmax_amd import binding as B
+    from vocab_wide_softmax_amd import workloads as W
+
+    wl = wl or W.workload("pair1024")
+    a, b, t = wl.a.to(device), wl.b.to(device), wl.t.to(device)
+    g = {op: wl.g[op].to(device) for op in W.OPS}
+    n, v = a.shape
+    t1 = n * v * 2
+    nbytes = {"logprobs": 3 * t1, "entropy": 3 * t1, "kl_ab": 6 * t1, "kl_ba": 6 * t1}
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=device)
+    torch.cuda.synchronize()
+    warm = op_times(W.OPS, a, b, t, g, steps, warmup)
+    cold = op_times(W.OPS, a, b, t, g, steps, warmup, flush=flush)
+    out = {"workload": "1024x75968 bf16 pair (A~N(0,3^2), B=A+N(0,0.5^2), 5% rows +1e4, 1% rows with 64 B "
+                       "columns at -inf)", "vocab_parts": B.split_parts(B.OP_KL, n, v),
+           "unflushed": {}, "flushed": {}}
+    for op in W.OPS:
+        out["unflushed"][op] = _op_entry(*warm[op], nbytes[op])
+        out["flushed"][op] = _op_entry(*cold[op], nbytes[op])
+    for k, res in (("unflushed", warm), ("flushed", cold)):
+        tot = sum(sum(res[op]) for op in W.OPS)
+        out[k]["all_four"] = _op_entry(tot, 0.0, sum(nbytes.values()))
+    del flush
+    torch.cuda.empty_cache()
+    return out
+
+
+def shifted_leg(device, steps, warmup, wl=None):
+    """Config 3: fp32 logits of two bases [4, 2049, 75968] read in place through the causal-shift
+    view base[:, :-1, :] (8192 rows, two row strides, no copy): entropy(A) and KL(A||B) fwd+bwd
+    (gradients fp32, contiguous), with the extra peak memory of each."""
+    import torch
+
+    from vocab_wide_softmax_amd import workloads as W
+
+    wl = wl or W.workload("shifted")
+    ab, bb, ib = wl.a_base.to(device), wl.b_base.to(device), wl.ids_base.to(device)
+    a, b, t = wl.views(ab, bb, ib)
+    assert not a.is_contiguous()
+    g = {op: wl.g[op].to(device) for op in W.OPS}
+    n = a.shape[0] * a.shape[1]
+    t3 = n * a.shape[-1] * 4
+    ops = ("entropy", "kl_ab")
+    nbytes = {"entropy": 3 * t3, "kl_ab": 6 * t3}
+    torch.cuda.synchronize()
+    res = op_times(ops, a, b, t, g, steps, warmup)
+    out = {"workload": "fp32 [4, 2049, 75968] pair ~ N(0, 3^2) read as base[:, :-1, :] (8192 rows, strides "
+                       "2049x75968 and 75968 elements)", "ops": {op: _op_entry(*res[op], nbytes[op]) for op in ops},
+           "memory": memory_report(ops, a, b, t, g)}
+    del ab, bb, ib, a, b, t
+    torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------------- fused linear-logp
 
 LIN_N, LIN_H, LIN_V = 8192, 4096, 151936
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def linear_bench(steps, warmup, device):
+def linear_bench(steps, warmup, device, wl=None):
     """Forward + backward of the fused linear-logp on h [8192, 4096], W [151936, 4096] bf16.
-    FLOPs counted: forward 2 N H V; backward 3 x 2 N H V (logits recomputed, dh, dW)."""
+    Algorithmic FLOPs: forward 2 N H V; backward 3 x 2 N H V (logits recomputed, dh, dW). The
+    backward feeds dz to the dh and dW contractions as a bf16 (hi, lo) pair, so the MFMA work it
+    executes is 5 x 2 N H V; both rates are reported."""
     import torch
 
     from vocab_wide_softmax_amd import binding as B
     from vocab_wide_softmax_amd import workloads as W
 
-    wl = W.linear_logp(LIN_N, LIN_H, LIN_V)
+    wl = wl or W.linear_logp(LIN_N, LIN_H, LIN_V)
     h, Wm, t, g = wl.h.to(device), wl.W.to(device), wl.t.to(device), wl.g.to(device)
+    n, hidden = h.shape
+    v = Wm.shape[0]
+    ws_bytes = B.linear_workspace_bytes(1, n, hidden, v)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
     torch.cuda.synchronize()
     log("linear-logp inputs resident; %d warmup steps" % warmup)
     for _ in range(warmup):
         lp, st = B.linear_logp_fwd(h, Wm, t)
-        B.linear_logp_bwd(h, Wm, t, st, g)
+        B.linear_logp_bwd(h, Wm, t, st, g, ws=ws)
     stream = torch.cuda.current_stream()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
@@ -268,22 +435,73 @@ def linear_bench(steps, warmup, device):
         evs[i][0].record(stream)
         lp, st = B.linear_logp_fwd(h, Wm, t)
         evs[i][1].record(stream)
-        B.linear_logp_bwd(h, Wm, t, st, g)
+        B.linear_logp_bwd(h, Wm, t, st, g, ws=ws)
         evs[i][2].record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     fwd = sorted(e[0].elapsed_time(e[1]) for e in evs)[steps // 2]
     bwd = sorted(e[1].elapsed_time(e[2]) for e in evs)[steps // 2]
-    flop = 2.0 * LIN_N * LIN_H * LIN_V
+    flop = 2.0 * n * hidden * v
     tf = lambda f, ms: f / (ms * 1e-3) / 1e12
+    del ws
+    torch.cuda.empty_cache()
     return {
         "workload": "h [8192, 4096] ~ N(0,1), W [151936, 4096] ~ N(0, 0.02^2), bf16; targets U[0, 151936)",
         "ms_per_step": round(wall, 3), "fwd_ms": round(fwd, 3), "bwd_ms": round(bwd, 3),
         "fwd_tflops": round(tf(flop, fwd), 1), "bwd_tflops": round(tf(3 * flop, bwd), 1),
         "step_tflops": round(tf(4 * flop, fwd + bwd), 1),
-        "roofline": {"bound": "mfma", "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf(4 * flop, fwd + bwd) / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "bwd_workspace_bytes": int(ws_bytes),
+        "roofline": {"bound": "mfma", "achieved": round(tf(4 * flop, fwd + bwd), 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf(4 * flop, fwd + bwd) / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flop_per_step": 4 * flop,
+                     "executed_mfma_flop_per_step": 6 * flop,
+                     "executed_frac": round(tf(6 * flop, fwd + bwd) / MFMA_BF16_PEAK_TFLOPS, 4)},
     }
+
+
+def linear_cpu_baseline(wl, rows=512, vocab_rows=512):
+    """The fp64 oracle of the fused linear-logp on a sub-batch of `rows` evenly spaced tokens of
+    the same workload: logp (forward over the full vocabulary), dh of those tokens, and the rows of
+    dW for `vocab_rows` vocabulary entries (targeted and untargeted) summed over that sub-batch.
+    TFLOP/s counts the algorithmic work of those outputs (forward 2 n H V, logits recomputed
+    2 n H V, dh 2 n V H, dW rows 2 n r H); BLAS runs on the host's threads."""
+    import numpy as np
+
+    from oracle import linear_logp as OL
+
+    n_all, hidden = wl.h.shape
+    v = wl.W.shape[0]
+    idx = np.linspace(0, n_all - 1, rows).astype(np.int64)
+    h = wl.h[idx].double().numpy()
+    W = wl.W.double().numpy()
+    t = wl.t[idx].numpy()
+    g = wl.g[idx].double().numpy()
+    rng = np.random.default_rng(7)
+    cols = np.unique(np.concatenate([t[: vocab_rows // 4], rng.choice(v, vocab_rows, replace=False)]))[:vocab_rows]
+    t0 = time.perf_counter()
+    OL.linear_logp_fwd(h, W, t)
+    OL.linear_logp_bwd_dh(h, W, t, g)
+    OL.linear_logp_bwd_dw(h, W, t, g, vocab_rows=cols)
+    el = time.perf_counter() - t0
+    flop = 3 * 2.0 * rows * hidden * v + 2.0 * rows * len(cols) * hidden
+    return {"value": round(flop / el / 1e12, 4), "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": "%d of %d tokens (evenly spaced) of h [8192, 4096] x W [151936, 4096]: float64 logp over the "
+                      "full vocabulary, dh of those tokens, and %d rows of dW (a quarter of them targeted) summed "
+                      "over them; %.1f s wall; TFLOP/s = algorithmic FLOPs of those outputs / wall time"
+                      % (rows, n_all, len(cols), el)}
+
+
+def _blas_threads():
+    """Threads of the host BLAS that the oracle's matrix products run on."""
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
 
 
 # --------------------------------------------------------------------------- CPU oracle
@@ -314,7 +532,7 @@ def cpu_baseline(wl, rows=8192):
 
     from vocab_wide_softmax_amd import workloads as W
 
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    cores = len(os.sched_getaffinity(0))
     idx = np.linspace(0, N_ROWS - 1, rows).astype(np.int64)
     a = wl.a[idx].double().numpy()
     b = wl.b[idx].double().numpy()
@@ -337,6 +555,118 @@ def cpu_baseline(wl, rows=8192):
                   "on %d host threads; %.1f s wall; GB/s = algorithmic bytes of those rows / wall time"
                   % (rows, cores, el),
     }
+
+
+def _sample(wl, n, k, seed=5):
+    """Rows to compare: first and last, offset and masked rows of the recipe, and k random rows."""
+    import numpy as np
+
+    rng = np.random.default_rng(seed)
+    rows = {0, n - 1}
+    rows.update(wl.offset_rows[:4].tolist())
+    rows.update(wl.mask_rows[:4].tolist())
+    rows.update(rng.choice(n, size=min(k, n), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+def _rep(x, y, c, kind):
+    from oracle import compare
+
+    r = compare.check(x, y, c, kind)
+    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+
+
+def _oracle_op(op, a, b, t, g):
+    """(output, gradients, output scale, gradient scales) of the oracle for float64 rows."""
+    from oracle import reductions as R
+
+    if op == "logprobs":
+        return (R.logprobs_fwd(a, t)[0], [R.logprobs_bwd(a, t, g)], R.cond_logprobs_fwd(a, t),
+                [R.cond_logprobs_bwd(a, t, g)])
+    if op == "entropy":
+        return R.entropy_fwd(a)[0], [R.entropy_bwd(a, g)], R.cond_entropy_fwd(a), [R.cond_entropy_bwd(a, g)]
+    x, y = (a, b) if op == "kl_ab" else (b, a)
+    return R.kl_fwd(x, y)[0], list(R.kl_bwd(x, y, g)), R.cond_kl_fwd(x, y), list(R.cond_kl_bwd(x, y, g))
+
+
+def oracle_parity(device, wls, lin_wl, with_dw=True):
+    """Part of the oracle leg: the device results of each workload's launch (the configuration the
+    bench times) against the fp64 oracle on sampled rows, under the acceptance rule of
+    oracle/compare.py. Per config and op: elements compared, strict-rule misses, failures of both
+    rules (must be 0), NaN / inf placement mismatches and the worst error-to-allowance ratio."""
+    import numpy as np
+    import torch
+
+    from oracle import linear_logp as OL
+    from vocab_wide_softmax_amd import binding as B
+    from vocab_wide_softmax_amd import workloads as W
+
+    out = {}
+    cases = (("config0_tiny_64x1024_fp32", "tiny", W.OPS, "f32", None, 0),
+             ("config0_tiny_64x1024_fp32_split16", "tiny", W.OPS, "f32", None, 16),
+             ("config1_pair1024_bf16", "pair1024", W.OPS, "bf16", 24, 0),
+             ("config2_pair8192_bf16", "pair8192", W.OPS, "bf16", 24, 0),
+             ("config3_shifted_fp32", "shifted", ("entropy", "kl_ab"), "f32", 12, 0))
+    for label, key, ops, kind, k, split in cases:
+        wl = wls[key]
+        if wl.shifted:
+            a, b, t = wl.views(wl.a_base.to(device), wl.b_base.to(device), wl.ids_base.to(device))
+        else:
+            a, b, t = wl.a.to(device), wl.b.to(device), wl.t.to(device)
+        V = a.shape[-1]
+        n = a.numel() // V
+        rows = np.arange(n) if k is None else _sample(wl, n, k)
+        idx = torch.from_numpy(rows).to(device)
+        if wl.shifted:  # host rows of the causal-shift view without materialising it
+            s_in = wl.a_base.shape[1] - 1
+            pick = lambda base: torch.stack([base[r // s_in, r % s_in] for r in rows.tolist()]).double().numpy()
+            ha, hb = pick(wl.a_base), pick(wl.b_base)
+            ht = torch.stack([wl.ids_base[r // s_in, r % s_in + 1] for r in rows.tolist()]).numpy()
+        else:
+            ha, hb, ht = wl.a[rows].double().numpy(), wl.b[rows].double().numpy(), wl.t[rows].numpy()
+        res = {}
+        for op in ops:
+            gd = wl.g[op].to(device)
+            o, st = op_fwd(B, op, a, b, t, split)
+            grads = op_bwd(B, op, a, b, t, gd, o, st)
+            do = o.reshape(-1)[idx].double().cpu().numpy()
+            dg = [x.reshape(-1, V)[idx].double().cpu().numpy() for x in grads]
+            del o, st, grads
+            yo, yg, co, cg = _oracle_op(op, ha, hb, ht, wl.g[op][rows].double().numpy())
+            r = {"out": _rep(do, yo, co, "f32")}
+            names = ["grad"] if len(yg) == 1 else (["grad_a", "grad_b"] if op == "kl_ab" else ["grad_b", "grad_a"])
+            for nm, x, y, c in zip(names, dg, yg, cg):
+                r[nm] = _rep(x, y, c, kind)
+            res[op] = r
+        res["rows_compared"] = int(len(rows))
+        out[label] = res
+        del a, b, t
+        torch.cuda.empty_cache()
+        log("parity %s done" % label)
+    # config 4: the fused linear-logp in the benchmark's launch
+    h, Wm, t, g = lin_wl.h.to(device), lin_wl.W.to(device), lin_wl.t.to(device), lin_wl.g.to(device)
+    lp, st = B.linear_logp_fwd(h, Wm, t)
+    dh, dW = B.linear_logp_bwd(h, Wm, t, st, g)
+    hh, hw, ht, hg = (lin_wl.h.double().numpy(), lin_wl.W.double().numpy(), lin_wl.t.numpy(),
+                      lin_wl.g.double().numpy())
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, hh.shape[0] - 1], rng.integers(0, hh.shape[0], 14)]))
+    idx = torch.from_numpy(rows).to(device)
+    r = {"logp": _rep(lp[idx].double().cpu().numpy(), OL.linear_logp_fwd(hh, hw, ht, rows=rows)[0],
+                      OL.cond_linear_fwd(hh, hw, ht, rows=rows), "f32"),
+         "dh": _rep(dh[idx].double().cpu().numpy(), OL.linear_logp_bwd_dh(hh, hw, ht, hg, rows=rows),
+                    OL.cond_linear_dh(hh, hw, ht, hg, rows=rows), "bf16"),
+         "rows_compared": int(len(rows))}
+    if with_dw:
+        untargeted = np.setdiff1d(np.arange(hw.shape[0]), ht)
+        cols = np.unique(np.concatenate([ht[:16], rng.choice(untargeted, 48, replace=False)]))
+        ref, c = OL.linear_logp_bwd_dw_cond(hh, hw, ht, hg, vocab_rows=cols)
+        r["dW"] = _rep(dW[torch.from_numpy(cols).to(device)].double().cpu().numpy(), ref, c, "bf16")
+        r["dW_vocab_rows_compared"] = int(len(cols))
+    out["config4_linear_logp_8192x4096x151936_bf16"] = r
+    del h, Wm, t, g, lp, st, dh, dW
+    torch.cuda.empty_cache()
+    return out
 
 
 # ------------------------------------------------------------------------- calibration
@@ -451,7 +781,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-linear", action="store_true", help="skip the fused linear-logp workload")
     ap.add_argument("--no-extras", action="store_true", help="skip top-k, JSD, fp16 and batch-invariant timings")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the 1024x75968 (flushed / unflushed) and fp32 causal-shift legs")
+    ap.add_argument("--no-parity", action="store_true", help="skip the oracle comparison on sampled rows")
+    ap.add_argument("--parity-no-dw", action="store_true",
+                    help="in the oracle comparison, skip the dW rows of the fused linear-logp (full-batch fp64 logits)")
     ap.add_argument("--cpu-rows", type=int, default=8192)
+    ap.add_argument("--cpu-linear-rows", type=int, default=512)
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--summarize", nargs=2, metavar=("DIR", "MODE"))
     ap.add_argument("--counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"))
@@ -520,12 +856,36 @@ def main():
                      "avg_launch_ms": round(dom_ms, 4)},
     }
     out["cpu_baseline"] = cpu
+    # extra peak device memory of each op at the headline shape (inputs resident)
+    _, a, b, t, g = make_inputs(wl, device)
+    out["memory"] = memory_report(W.OPS, a, b, t, g)
+    del a, b, t, g
+    torch.cuda.empty_cache()
     if not args.no_extras:
         log("other ops: top-k logprobs, JSD, fp16 step, batch-invariant step")
         out["other_ops"] = extras_bench(wl, device)
+    wl1024 = wl_shift = None
+    if not args.no_configs:
+        log("1024x75968 pair: unflushed and flushed")
+        wl1024 = W.workload("pair1024")
+        out["pair1024"] = pair1024_leg(device, args.steps, 5, wl1024)
+        log("fp32 causal-shift view [4, 2049, 75968][:, :-1]")
+        wl_shift = W.workload("shifted")
+        out["shifted_fp32"] = shifted_leg(device, max(5, args.steps // 2), 3, wl_shift)
+    lin_wl = None
     if not args.no_linear:
-        out["linear_logp"] = linear_bench(max(3, args.steps // 4), 2, device)
+        lin_wl = W.linear_logp(LIN_N, LIN_H, LIN_V)
+        out["linear_logp"] = linear_bench(max(3, args.steps // 4), 2, device, lin_wl)
         log("linear-logp: %.2f ms fwd, %.2f ms bwd" % (out["linear_logp"]["fwd_ms"], out["linear_logp"]["bwd_ms"]))
+        if not args.no_cpu_baseline:
+            out["linear_logp"]["cpu_baseline"] = linear_cpu_baseline(lin_wl, args.cpu_linear_rows)
+            log("linear-logp cpu baseline: %s TFLOP/s" % out["linear_logp"]["cpu_baseline"]["value"])
+    if not args.no_cpu_baseline and not args.no_parity:
+        # the oracle leg's comparison of device results with the oracle on sampled rows
+        wls = {"tiny": W.workload("tiny"), "pair8192": wl, "pair1024": wl1024 or W.workload("pair1024"),
+               "shifted": wl_shift or W.workload("shifted")}
+        lin_wl = lin_wl or W.linear_logp(LIN_N, LIN_H, LIN_V)
+        out["parity"] = oracle_parity(device, wls, lin_wl, with_dw=not args.parity_no_dw)
     print(json.dumps(out), flush=True)
 
 

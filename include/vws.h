@@ -281,10 +281,13 @@ VWS_API int vws_jsd_bwd(const vws_rows* s, const vws_rows* t, float beta, const 
  * log-probability of the target under logits z = h W^T, computed on MFMA in
  * vocabulary tiles whose (m, S) feed the online log-sum-exp, so the [N, V]
  * logits are never written. The forward returns logp = z_t - lse and the
- * per-row (m, log S); the backward recomputes the logits tile by tile, forms
- * dz = g (onehot(t) - p) (the chunked backward of the pages' review nitpick),
- * rounds it to bf16 into the workspace, and contracts it into dh = dz W and
- * dW = dz^T h (fp32 accumulation, bf16 round-to-nearest-even outputs).
+ * per-row (m, log S); the backward goes over the vocabulary in chunks (the
+ * chunked backward of the pages' review nitpick): for each chunk it recomputes
+ * the logits tile by tile, forms dz = g (onehot(t) - p) in fp32, keeps it in the
+ * workspace as a bf16 pair (hi = rne(dz), lo = rne(dz - hi), about 2^-17
+ * relative), and contracts both parts into dW of the chunk's vocabulary rows
+ * = dz^T h and into dh += dz W_chunk (fp32 accumulation, dh summed in fp32 over
+ * the chunks; bf16 round-to-nearest-even outputs).
  *
  *   h       bf16 [N, H], row stride ldh (elements, >= H, multiple of 8)
  *   W       bf16 [V, H], row stride ldw (>= H, multiple of 8)
@@ -294,15 +297,19 @@ VWS_API int vws_jsd_bwd(const vws_rows* s, const vws_rows* t, float beta, const 
  *   dh      out bf16 [N, H] contiguous, may be NULL
  *   dW      out bf16 [V, H] contiguous, may be NULL
  *   ws      workspace of vws_linear_workspace_bytes(pass, N, H, V, split_hint) bytes
- *           (pass 0: forward, 1: backward, where split_hint is ignored), 16-byte aligned
- *   split_hint  forward vocabulary chunking, as for the logits ops: 0 automatic (about two
+ *           (pass 0: forward, 1: backward), 256-byte aligned. The backward's holds one
+ *           chunk's dz pair, 2 x N x chunk x 2 bytes, plus the fp32 sum of dh, N x H x 4
+ *           bytes, when V spans more than one chunk (0.40 GB at 8192 x 4096 x 151936).
+ *   split_hint  forward: vocabulary chunking as for the logits ops: 0 automatic (about two
  *           workgroups per CU for this N; the order in which a token's chunk partials
  *           merge then follows the batch size), k >= 1 k chunks, VWS_SPLIT_INVARIANT
  *           chunks of 1024 columns. The last two depend on V alone: a token's logp and
  *           stats are then the same bits in every batch (batch invariance); < -1 is
- *           VWS_EINVAL. The backward reduces each dz and dh entry in an order fixed by
- *           V and H, so dh is batch invariant when the stats it is given are (dW sums
- *           over the batch by definition).
+ *           VWS_EINVAL.
+ *           backward: 0 or VWS_SPLIT_INVARIANT chunks of 8192 columns, k >= 1 k chunks.
+ *           Every choice depends on V alone and reduces each dz and dh entry in an order
+ *           fixed by V, H and the chunking, so dh is batch invariant when the stats it is
+ *           given are (dW sums over the batch by definition).
  * H must be a multiple of 8. h, W, dh, dW must be 16-byte aligned. dtype must be VWS_BF16.
  * Sizes: N <= 2^31, H and V <= INT32_MAX, and with T(x) = ceil(x / 256) each of
  * T(N) T(V), T(N) T(H) and T(V) T(H) below 2^23 (one 512-thread workgroup per 256 x 256
@@ -317,7 +324,7 @@ VWS_API int vws_linear_logp_fwd(const void* h, int64_t ldh, const void* W, int64
 VWS_API int vws_linear_logp_bwd(const void* h, int64_t ldh, const void* W, int64_t ldw, int dtype, int64_t N,
                                 int64_t H, int64_t V, const int64_t* t, int64_t ignore_index, const float* stats,
                                 const float* g, int64_t g_stride, void* dh, void* dW, void* ws, size_t ws_bytes,
-                                void* stream);
+                                int split_hint, void* stream);
 
 /* Static description of a status code. */
 VWS_API const char* vws_strerror(int status);

@@ -100,18 +100,14 @@ def f64_to_bf16_bits(x):
     return bits
 
 
-def check(x, y, c, kind, factor=None):
+def check(x, y, c, kind):
     """Compare device values x with oracle values y under the rule above.
 
-    kind is "f32", "bf16" or "f16". ``factor`` replaces 64 eps32 in the conditioned
-    bound where the computation rounds an operand more coarsely (the fused
-    linear-logp backward feeds dz to its contractions in bf16: each term then
-    carries up to 2^-9 relative error, so its rule uses factor 2^-8).
-    Returns a dict with the element count, the number of elements missing the
-    strict bound, the number failing both bounds, the NaN / inf placement
-    mismatches, and the worst ratio of error to allowance.
+    kind is "f32", "bf16" or "f16". Returns a dict with the element count, the
+    number of elements missing the strict bound, the number failing both bounds,
+    the NaN / inf placement mismatches, and the worst ratio of error to allowance.
     """
-    cfac = COND if factor is None else float(factor)
+    cfac = COND
     x = np.asarray(x, dtype=np.float64).ravel()
     y = np.asarray(y, dtype=np.float64).ravel()
     c = np.asarray(c, dtype=np.float64).ravel()

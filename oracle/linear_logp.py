@@ -18,8 +18,9 @@ import numpy as np
 
 from . import reductions
 
-__all__ = ["logits", "linear_logp_fwd", "linear_logp_bwd_dh", "linear_logp_bwd_dw", "cond_logits",
-           "cond_linear_fwd", "cond_linear_dh", "cond_linear_dw", "linear_logp_bwd_dw_cond"]
+__all__ = ["logits", "linear_logp_fwd", "linear_logp_bwd_dz", "linear_logp_bwd_dh", "linear_logp_bwd_dw",
+           "cond_logits", "cond_linear_fwd", "cond_linear_dz", "cond_linear_dh", "cond_linear_dw",
+           "linear_logp_bwd_dw_cond"]
 
 
 def _f64(x):
@@ -51,6 +52,16 @@ def linear_logp_fwd(h, W, t, ignore_index=-100, rows=None):
         t = t[np.asarray(rows)]
     z = logits(h, W, rows)
     return reductions.logprobs_fwd(z, t, ignore_index)
+
+
+def linear_logp_bwd_dz(h, W, t, g, ignore_index=-100, rows=None):
+    """dz = g (onehot(t) - p) of the selected rows: the gradient of g logp with respect to the logits."""
+    t = np.asarray(t, dtype=np.int64)
+    g = _f64(g).reshape(-1)
+    if rows is not None:
+        t = t[np.asarray(rows)]
+        g = g[np.asarray(rows)]
+    return reductions.logprobs_bwd(logits(h, W, rows), t, g, ignore_index)
 
 
 def linear_logp_bwd_dh(h, W, t, g, ignore_index=-100, rows=None):
@@ -106,6 +117,23 @@ def cond_linear_fwd(h, W, t, ignore_index=-100, rows=None):
     r = np.nonzero(ok)[0]
     c[r] += np.abs(z[r, t[r]] - m[r]) + cz[r, t[r]]
     return c
+
+
+def cond_linear_dz(h, W, t, g, ignore_index=-100, rows=None):
+    """Scale of dz_nv: the logits-op scale |g| (1[v = t] + p_v (1 + |z_v - m| + |log S|)) plus
+    |g| p_v (cz_v + sum_u p_u cz_u), the rounding of the logit itself and of log S behind it."""
+    t = np.asarray(t, dtype=np.int64)
+    g = _f64(g).reshape(-1)
+    if rows is not None:
+        t = t[np.asarray(rows)]
+        g = g[np.asarray(rows)]
+    z = logits(h, W, rows)
+    cz = cond_logits(h, W, rows)
+    p = np.exp(reductions.log_softmax_rows(z)[0])
+    c = reductions.cond_logprobs_bwd(z, t, g, ignore_index)
+    extra = np.abs(g)[:, None] * p * (cz + np.sum(p * cz, axis=1, keepdims=True))
+    live = (t != ignore_index)[:, None]
+    return c + np.where(live, extra, 0.0)
 
 
 def cond_linear_dh(h, W, t, g, ignore_index=-100, rows=None):

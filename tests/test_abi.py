@@ -125,17 +125,28 @@ def test_linear_validation(L):
     assert fwd(logp=0) == EINVAL
     assert fwd(nb=16) == EWORKSPACE
     assert fwd(N=0, h=0, W=0, t=0) == 0
-    assert B.linear_workspace_bytes(1, 8, 64, 100) == 8 * 104 * 2
+    # backward workspace: the dz pair (hi and lo planes of [N, chunk] bf16, 256-byte aligned), plus
+    # the fp32 sum of dh [N, H] when the vocabulary spans more than one chunk of 8192 columns
+    align = lambda x: (x + 255) // 256 * 256
+    assert B.linear_workspace_bytes(1, 8, 64, 100) == 2 * align(8 * 104 * 2)
+    assert B.linear_workspace_bytes(1, 8192, 4096, 151936) == 2 * 8192 * 8192 * 2 + 8192 * 4096 * 4
+    assert B.linear_workspace_bytes(1, 8192, 4096, 151936) < 0.41e9
+    assert B.linear_workspace_bytes(1, 300, 200, 3001, 3) == 2 * align(300 * 1024 * 2) + 300 * 200 * 4
+    assert B.linear_workspace_bytes(1, 300, 200, 3001, 1) == 2 * align(300 * 3008 * 2)
     assert B.linear_workspace_bytes(0, 8, 64, 100) > 8 * 4
     with pytest.raises(ValueError):
         B.linear_workspace_bytes(2, 8, 64, 100)
     bwd = L.vws_linear_logp_bwd
     assert bwd(0x1000, 64, 0x2000, 64, B.VWS_BF16, 4, 64, 100, 0x3000, -100, 0x5000, 0x7000, -1, 0x8000, None, 0x6000,
-               1 << 20, None) == EINVAL
-    assert bwd(0x1000, 64, 0x2000, 64, B.VWS_BF16, 4, 64, 100, 0x3000, -100, 0x5000, 0x7000, 1, None, None, 0x6000,
-               1 << 20, None) == 0  # no gradient requested
+               1 << 20, 0, None) == EINVAL
     assert bwd(0x1000, 64, 0x2000, 64, B.VWS_BF16, 4, 64, 100, 0x3000, -100, 0x5000, 0x7000, 1, 0x8000, None, 0x6000,
-               16, None) == EWORKSPACE
+               1 << 20, -2, None) == EINVAL
+    assert bwd(0x1000, 64, 0x2000, 64, B.VWS_BF16, 4, 64, 100, 0x3000, -100, 0x5000, 0x7000, 1, None, None, 0x6000,
+               1 << 20, 0, None) == 0  # no gradient requested
+    assert bwd(0x1000, 64, 0x2000, 64, B.VWS_BF16, 4, 64, 100, 0x3000, -100, 0x5000, 0x7000, 1, 0x8000, None, 0x6000,
+               16, 0, None) == EWORKSPACE
+    assert bwd(0x1000, 64, 0x2000, 64, B.VWS_BF16, 4, 64, 100, 0x3000, -100, 0x5000, 0x7000, 1, 0x8000, None, 0x6010,
+               1 << 20, 0, None) == ELAYOUT  # the workspace is 256-byte aligned
     # more tiles than a launch of 512-thread workgroups can hold (2^23): rejected before any launch
     assert fwd(N=1 << 31, V=(1 << 31) - 1, nb=1 << 62) == EINVAL
     assert fwd(N=1 << 24, V=1 << 15, nb=1 << 62) == EINVAL  # 2^16 token x 2^7 vocabulary tiles
@@ -149,7 +160,7 @@ def test_linear_validation(L):
     per_row = lambda sp, v: (B.linear_workspace_bytes(0, 512, 64, v, sp) - 512 * 4) / (512 * 8)
     assert per_row(B.SPLIT_INVARIANT, 151936) == 149  # 594 vocabulary tiles in chunks of 4
     assert per_row(5, 151936) == 5
-    assert B.linear_workspace_bytes(1, 8, 64, 100, B.SPLIT_INVARIANT) == 8 * 104 * 2
+    assert B.linear_workspace_bytes(1, 8, 64, 100, B.SPLIT_INVARIANT) == 2 * align(8 * 104 * 2)
 
 
 def test_topk_validation(L):

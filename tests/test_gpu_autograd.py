@@ -61,11 +61,11 @@ def test_logprobs_shift_view(device):
     tt, ww = t.cpu().reshape(-1).numpy(), w.cpu().double().reshape(-1).numpy()
     ref, _, _ = R.logprobs_fwd(z, tt, -100)
     rep = compare.check(out.detach().double().cpu().reshape(-1).numpy(), ref, R.cond_logprobs_fwd(z, tt, -100), "f32")
-    assert rep["fail"] == 0 and rep["nan_mismatch"] == 0, rep
+    assert rep["fail"] == 0 and rep["nan_mismatch"] == 0 and rep["inf_mismatch"] == 0, rep
     gref = R.logprobs_bwd(z, tt, ww, -100)
     rep = compare.check(x.grad[:, :-1].double().cpu().reshape(-1, base.shape[-1]).numpy(), gref,
                         R.cond_logprobs_bwd(z, tt, ww, -100), "bf16")
-    assert rep["fail"] == 0 and rep["nan_mismatch"] == 0, rep
+    assert rep["fail"] == 0 and rep["nan_mismatch"] == 0 and rep["inf_mismatch"] == 0, rep
 
 
 def test_entropy_plain_sum_broadcast_gradient(device):
@@ -104,7 +104,7 @@ def test_kl_partial_gradients(device, need):
         zb = base2[:, :-1].float().cpu().double().reshape(-1, base.shape[-1]).numpy()
         ref = R.kl_fwd(za, zb)[0]
         rep = compare.check(out.detach().double().cpu().reshape(-1).numpy(), ref, R.cond_kl_fwd(za, zb), "f32")
-        assert rep["fail"] == 0 and rep["nan_mismatch"] == 0, rep
+        assert rep["fail"] == 0 and rep["nan_mismatch"] == 0 and rep["inf_mismatch"] == 0, rep
 
 
 def test_jsd_student_only(device):

@@ -192,3 +192,56 @@ def test_split_matches_unsplit(device):
     k1, _ = B.kl_fwd(da, db, split_hint=1)
     k8, _ = B.kl_fwd(da, db, split_hint=8)
     torch.testing.assert_close(k1, k8, rtol=1e-4, atol=1e-6)
+
+
+def _gap_rows(n, v, seed, lo=86.0, hi=104.0):
+    """Rows with one maximum at 0 and the rest spread over log-probability gaps of lo..hi nats,
+    so that p lies in [e^-104, e^-86]: below the smallest normal fp32 (2^-126 = e^-87.3) for most
+    columns, where the gradient is a subnormal that bf16 still holds (down to 2^-133 = e^-92.2)."""
+    gen = torch.Generator().manual_seed(seed)
+    a = -(lo + (hi - lo) * torch.rand(n, v, generator=gen))
+    a[:, 0] = 0.0
+    b = a + 0.5 * torch.randn(n, v, generator=gen)
+    b[:, 0] = 0.0
+    t = torch.randint(1, v, (n,), generator=gen)
+    g = torch.randn(n, generator=gen) * 1000.0  # large enough that g p is a normal number on some columns
+    return a, b, t, g
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_subnormal_probabilities_in_gradients(device, dtype):
+    """Gradients built on probabilities between 2^-149 and 2^-126: the hardware exponential flushes
+    results there to 0, so the backward passes rescale such arguments; every gradient element
+    (logprobs, entropy, both KL directions) must still pass the rule, including the bf16
+    subnormals and the normal-range products g p (log p - ...)."""
+    a, b, t, g = _gap_rows(6, 1500, seed=41)
+    a, b = a.to(dtype), b.to(dtype)
+    print("subnormal p", dtype, flush=True)
+    _check_all_ops(a, b, t, g, device)
+    # the top-k backward and the JSD backward recompute p the same way
+    from oracle import compare, jsd as J, topk as TK
+
+    ids = torch.stack([t, (t + 7) % 1500, t], dim=1)
+    gk = torch.randn(6, 3, generator=torch.Generator().manual_seed(3)) * 1000.0
+    da_, db_ = a.to(device), b.to(device)
+    lp, st = B.logprobs_topk_fwd(da_, ids.to(device), -100)
+    dz = B.logprobs_topk_bwd(da_, ids.to(device), st, gk.to(device), -100)
+    ha, hb, hi, hg = f64(a), f64(b), ids.numpy(), gk.double().numpy()
+    kind = "bf16" if dtype == torch.bfloat16 else "f32"
+    rep = compare.check(f64(dz), TK.logprobs_topk_bwd(ha, hi, hg), TK.cond_logprobs_topk_bwd(ha, hi, hg), kind)
+    assert rep["fail"] == 0 and rep["nan_mismatch"] == 0 and rep["inf_mismatch"] == 0, rep
+    out, st = B.jsd_fwd(da_, db_, 0.4)
+    ds, dt = B.jsd_bwd(da_, db_, 0.4, st, out, g.to(device))
+    rs, rt = J.jsd_bwd(ha, hb, g.double().numpy(), 0.4)
+    cs, ct = J.cond_jsd_bwd(ha, hb, g.double().numpy(), 0.4)
+    for x, y, c in ((ds, rs, cs), (dt, rt, ct)):
+        rep = compare.check(f64(x), y, c, kind)
+        assert rep["fail"] == 0 and rep["nan_mismatch"] == 0 and rep["inf_mismatch"] == 0, rep
+    if dtype == torch.bfloat16:
+        # the case is not vacuous: the oracle's entropy gradient has normal-range entries below
+        # e^-87.3 probability, which a flushed exponential would zero
+        from oracle import reductions as R
+
+        ge = R.entropy_bwd(ha, g.double().numpy())
+        p = np.exp(ha - np.log(np.exp(ha).sum(axis=1, keepdims=True)))
+        assert np.count_nonzero((p < 2.0 ** -126) & (compare.bf16_rne(ge) != 0)) > 1000

@@ -97,20 +97,20 @@ def test_fp16_topk_and_jsd(device):
     dz = B.logprobs_topk_bwd(s.to(device), ids.to(device), st, gk.to(device), -100)
     hs, hi, hg = f64(s), ids.numpy(), gk.double().numpy()
     rep = compare.check(f64(logp), TK.logprobs_topk_fwd(hs, hi)[0], TK.cond_logprobs_topk_fwd(hs, hi), "f32")
-    assert rep["fail"] == 0 and rep["nan_mismatch"] == 0, rep
+    assert rep["fail"] == 0 and rep["nan_mismatch"] == 0 and rep["inf_mismatch"] == 0, rep
     rep = compare.check(f64(dz), TK.logprobs_topk_bwd(hs, hi, hg), TK.cond_logprobs_topk_bwd(hs, hi, hg), "f16")
-    assert rep["fail"] == 0 and rep["nan_mismatch"] == 0, rep
+    assert rep["fail"] == 0 and rep["nan_mismatch"] == 0 and rep["inf_mismatch"] == 0, rep
     g = torch.randn(20, generator=gen)
     out, st = B.jsd_fwd(s.to(device), t.to(device), 0.4)
     ds, dt = B.jsd_bwd(s.to(device), t.to(device), 0.4, st, out, g.to(device))
     ht, hgj = f64(t), g.double().numpy()
     rep = compare.check(f64(out), J.jsd_fwd(hs, ht, 0.4)[0], J.cond_jsd_fwd(hs, ht, 0.4), "f32")
-    assert rep["fail"] == 0 and rep["nan_mismatch"] == 0, rep
+    assert rep["fail"] == 0 and rep["nan_mismatch"] == 0 and rep["inf_mismatch"] == 0, rep
     rs, rt = J.jsd_bwd(hs, ht, hgj, 0.4)
     cs, ct = J.cond_jsd_bwd(hs, ht, hgj, 0.4)
     for x, y, c in ((ds, rs, cs), (dt, rt, ct)):
         rep = compare.check(f64(x), y, c, "f16")
-        assert rep["fail"] == 0 and rep["nan_mismatch"] == 0, rep
+        assert rep["fail"] == 0 and rep["nan_mismatch"] == 0 and rep["inf_mismatch"] == 0, rep
 
 
 def _bits(x):

@@ -131,5 +131,5 @@ def test_topk_single_slot_matches_single_id_op(device):
     dk = B.logprobs_topk_bwd(zd, ids.to(device), stk, g.to(device), IGN)
     # same statistics; the one-hot term is formed as fma(-g, p, g) here and g (1 - p) there
     rep = compare.check(f64(dk), f64(d1).astype(np.float64), np.abs(f64(d1)) + 1e-30, "bf16")
-    assert rep["nan_mismatch"] == 0 and rep["fail"] == 0, rep
+    assert rep["nan_mismatch"] == 0 and rep["inf_mismatch"] == 0 and rep["fail"] == 0, rep
     assert torch.allclose(lpk[:, 0], lp1, rtol=2e-6, atol=2e-6, equal_nan=True)

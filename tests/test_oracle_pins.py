@@ -538,6 +538,15 @@ def test_condition_scales_of_topk_jsd_and_linear():
     cdh = linear_logp.cond_linear_dh(h, W, tl, gl)[:, 0]
     np.testing.assert_allclose(cdh[:3], 2 * np.abs(gl[:3]) * (1 - 1 / Vl), rtol=1e-13)
     assert cdh[3] == 0.0
+    # dz scale: the logits-op scale |g| (1[v = t] + (1 + log V) / V) plus |g| (cz + sum p cz) / V
+    cdz = linear_logp.cond_linear_dz(h, W, tl, gl)
+    one = np.zeros((n, Vl))
+    one[np.arange(3), tl[:3]] = 1.0
+    want_dz = np.abs(gl)[:, None] * (one + (1 + np.log(Vl) + 2 * np.abs(h)) / Vl)
+    np.testing.assert_allclose(cdz[:3], want_dz[:3], rtol=1e-13)
+    np.testing.assert_allclose(cdz[3], np.abs(gl[3]) * (1 + np.log(Vl)) / Vl, rtol=1e-13)  # ignored: no logit term
+    dz = linear_logp.linear_logp_bwd_dz(h, W, tl, gl)
+    np.testing.assert_allclose(dz[:3], gl[:3, None] * (one[:3] - 1.0 / Vl), rtol=1e-13)
     cdw = linear_logp.cond_linear_dw(h, W, tl, gl)[:, 0]
     want = np.zeros(Vl)
     for i in range(3):

@@ -86,7 +86,7 @@ def lib():
             "vws_linear_workspace_bytes": (SZ, [I32, I64, I64, I64, I32]),
             "vws_linear_logp_fwd": (I32, [VP, I64, VP, I64, I32, I64, I64, I64, VP, I64, FP, FP, VP, SZ, I32, VP]),
             "vws_linear_logp_bwd": (I32, [VP, I64, VP, I64, I32, I64, I64, I64, VP, I64, FP, FP, I64, VP, VP, VP,
-                                          SZ, VP]),
+                                          SZ, I32, VP]),
             "vws_strerror": (ctypes.c_char_p, [I32]),
             "vws_version": (I32, []),
         }
@@ -419,9 +419,12 @@ def linear_logp_fwd(h, W, t, ignore_index=-100, split_hint=0):
     return logp, stats
 
 
-def linear_logp_bwd(h, W, t, stats, g, ignore_index=-100, need_h=True, need_w=True):
-    """(dh bf16 [N, H] or None, dW bf16 [V, H] or None) -- vws_linear_logp_bwd."""
-    dev = _device(h, W, t, stats, g)
+def linear_logp_bwd(h, W, t, stats, g, ignore_index=-100, need_h=True, need_w=True, split_hint=0, ws=None):
+    """(dh bf16 [N, H] or None, dW bf16 [V, H] or None) -- vws_linear_logp_bwd.
+    split_hint: 0 vocabulary chunks of 8192 columns, k >= 1 k chunks. ws: optional uint8 device
+    tensor of at least linear_workspace_bytes(1, ...) bytes to use as the workspace (after the
+    call it holds the last chunk's dz pair; allocated here when None)."""
+    dev = _device(h, W, t, stats, g, ws)
     L = lib()
     _lin_check(h, W, t)
     n, hidden = h.shape
@@ -429,11 +432,14 @@ def linear_logp_bwd(h, W, t, stats, g, ignore_index=-100, need_h=True, need_w=Tr
     g, gs = _g_arg(g, h)
     dh = torch.empty((n, hidden), dtype=torch.bfloat16, device=h.device) if need_h else None
     dW = torch.empty((v, hidden), dtype=torch.bfloat16, device=h.device) if need_w else None
-    nb = linear_workspace_bytes(1, n, hidden, v)
-    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=h.device)
+    nb = linear_workspace_bytes(1, n, hidden, v, split_hint)
+    if ws is None:
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=h.device)
+    elif ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.numel() < nb:
+        raise ValueError("workspace must be a contiguous uint8 tensor of at least %d bytes" % nb)
     with torch.cuda.device(dev):
         _check("vws_linear_logp_bwd", L.vws_linear_logp_bwd(h.data_ptr(), h.stride(0), W.data_ptr(), W.stride(0),
                                                             VWS_BF16, n, hidden, v, t.data_ptr(), ignore_index,
-                                                            _ptr(stats), _ptr(g), gs, _ptr(dh), _ptr(dW), _ptr(ws), nb,
-                                                            _stream(dev)))
+                                                            _ptr(stats), _ptr(g), gs, _ptr(dh), _ptr(dW), _ptr(ws),
+                                                            ws.numel(), split_hint, _stream(dev)))
     return dh, dW

@@ -283,15 +283,27 @@ int64_t round_up8(int64_t x) { return (x + 7) / 8 * 8; }
 
 constexpr int64_t kLinMaxBlocks = (int64_t)1 << 23;  // 512-thread workgroups per linear-logp launch
 
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Backward vocabulary chunk: width in columns and pitch of the dz planes.
+int64_t lin_bwd_chunk(int64_t V, int split_hint) { return (int64_t)vws::lin_bwd_tiles_per_chunk(V, split_hint) * 256; }
+int64_t lin_bwd_ldc(int64_t V, int split_hint) {
+  const int64_t c = lin_bwd_chunk(V, split_hint);
+  return c < round_up8(V) ? c : round_up8(V);
+}
+
 // Workspace layout of the fused linear-logp.
 //   forward:  part [N, chunks, 2] fp32, then zt [N] fp32
-//   backward: dz [N, round_up8(V)] bf16
-size_t lin_ws_bytes(int pass, int64_t N, int64_t V, int split_hint) {
+//   backward: the chunk's dz as a bf16 pair, hi [N, ldc] then lo [N, ldc] (each 256-byte
+//             aligned), then, with more than one chunk, the fp32 running sum of dh [N, H]
+size_t lin_ws_bytes(int pass, int64_t N, int64_t H, int64_t V, int split_hint) {
   if (pass == 0) {
     const size_t part = (size_t)N * (size_t)vws::lin_chunks(N, V, split_hint) * 2 * sizeof(float);
-    return (part + 255) / 256 * 256 + (size_t)N * sizeof(float);
+    return align256(part) + (size_t)N * sizeof(float);
   }
-  return (size_t)N * (size_t)round_up8(V) * 2;
+  const size_t plane = align256((size_t)N * (size_t)lin_bwd_ldc(V, split_hint) * 2);
+  const bool multi = lin_bwd_chunk(V, split_hint) < V;
+  return 2 * plane + (multi ? (size_t)N * (size_t)H * sizeof(float) : 0);
 }
 
 int lin_check(const void* h, int64_t ldh, const void* W, int64_t ldw, int dtype, int64_t N, int64_t H, int64_t V,
@@ -320,7 +332,7 @@ extern "C" {
 VWS_API size_t vws_linear_workspace_bytes(int pass, int64_t N, int64_t H, int64_t V, int split_hint) {
   if ((pass != 0 && pass != 1) || N < 0 || H < 1 || V < 1 || split_hint < VWS_SPLIT_INVARIANT) return (size_t)-1;
   if (N == 0) return 0;
-  return lin_ws_bytes(pass, N, V, split_hint);
+  return lin_ws_bytes(pass, N, H, V, split_hint);
 }
 
 VWS_API int vws_linear_logp_fwd(const void* h, int64_t ldh, const void* W, int64_t ldw, int dtype, int64_t N,
@@ -332,7 +344,7 @@ VWS_API int vws_linear_logp_fwd(const void* h, int64_t ldh, const void* W, int64
   if (N == 0) return VWS_OK;
   if (!logp || !stats) return VWS_EINVAL;
   if (!aligned(logp, 4) || !aligned(stats, 4)) return VWS_ELAYOUT;
-  const size_t need = lin_ws_bytes(0, N, V, split_hint);
+  const size_t need = lin_ws_bytes(0, N, H, V, split_hint);
   if (!ws || ws_bytes < need) return VWS_EWORKSPACE;
   if (!aligned(ws, 16)) return VWS_ELAYOUT;
   vws::LinArgs p{};
@@ -349,7 +361,7 @@ VWS_API int vws_linear_logp_fwd(const void* h, int64_t ldh, const void* W, int64
   p.stats = stats;
   const size_t part = (size_t)N * (size_t)vws::lin_chunks(N, V, split_hint) * 2 * sizeof(float);
   p.part = static_cast<float*>(ws);
-  p.zt = reinterpret_cast<float*>(static_cast<char*>(ws) + (part + 255) / 256 * 256);
+  p.zt = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(part));
   hipError_t e = vws::launch_lin_fwd(p, split_hint, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? VWS_OK : VWS_EHIP;
 }
@@ -357,16 +369,16 @@ VWS_API int vws_linear_logp_fwd(const void* h, int64_t ldh, const void* W, int64
 VWS_API int vws_linear_logp_bwd(const void* h, int64_t ldh, const void* W, int64_t ldw, int dtype, int64_t N,
                                 int64_t H, int64_t V, const int64_t* t, int64_t ignore_index, const float* stats,
                                 const float* g, int64_t g_stride, void* dh, void* dW, void* ws, size_t ws_bytes,
-                                void* stream) {
+                                int split_hint, void* stream) {
   int rc = lin_check(h, ldh, W, ldw, dtype, N, H, V, t);
   if (rc) return rc;
-  if (g_stride < 0) return VWS_EINVAL;
+  if (g_stride < 0 || split_hint < VWS_SPLIT_INVARIANT) return VWS_EINVAL;
   if (N == 0 || (!dh && !dW)) return VWS_OK;
   if (!stats || !g) return VWS_EINVAL;
   if (!aligned(stats, 4) || !aligned(g, 4) || !aligned(dh, 16) || !aligned(dW, 16)) return VWS_ELAYOUT;
-  const size_t need = lin_ws_bytes(1, N, V, 0);
+  const size_t need = lin_ws_bytes(1, N, H, V, split_hint);
   if (!ws || ws_bytes < need) return VWS_EWORKSPACE;
-  if (!aligned(ws, 16)) return VWS_ELAYOUT;
+  if (!aligned(ws, 256)) return VWS_ELAYOUT;
   vws::LinArgs p{};
   p.h = static_cast<const uint16_t*>(h);
   p.W = static_cast<const uint16_t*>(W);
@@ -380,10 +392,13 @@ VWS_API int vws_linear_logp_bwd(const void* h, int64_t ldh, const void* W, int64
   p.stats = const_cast<float*>(stats);
   p.g = g;
   p.g_stride = g_stride;
-  p.dz = static_cast<uint16_t*>(ws);
-  p.ldz = round_up8(V);
-  p.ldw_out = H;
-  hipError_t e = vws::launch_lin_bwd(p, static_cast<uint16_t*>(dh), static_cast<uint16_t*>(dW),
+  const int64_t ldc = lin_bwd_ldc(V, split_hint);
+  const size_t plane = align256((size_t)N * (size_t)ldc * 2);
+  p.dzh = static_cast<uint16_t*>(ws);
+  p.dzl = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + plane);
+  p.ldc = ldc;
+  p.dh_acc = lin_bwd_chunk(V, split_hint) < V ? reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * plane) : nullptr;
+  hipError_t e = vws::launch_lin_bwd(p, split_hint, static_cast<uint16_t*>(dh), static_cast<uint16_t*>(dW),
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? VWS_OK : VWS_EHIP;
 }

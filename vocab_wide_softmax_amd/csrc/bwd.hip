@@ -105,10 +105,10 @@ __device__ __forceinline__ void bwd_store(const RowBwd& r, const float (&xa)[UB]
       for (int j = 0; j < 8; ++j) {
         const float ua = (xa[u][j] - r.m) - r.ls;
         const float ub = (xb[u][j] - r.mb) - r.lsb;
-        const float pa = expf_fast(ua);
-        const float pb = expf_fast(ub);
-        ya[j] = r.nan_a ? qnan : mul0(pa, (ua - ub) - r.res) * r.gv;
-        yb[j] = r.nan_b ? qnan : (pb - pa) * r.gv;
+        const PScaled pa = exp_split(ua);
+        const PScaled pb = exp_split(ub);
+        ya[j] = r.nan_a ? qnan : (mul0(pa.p, (ua - ub) - r.res) * r.gv) * pa.f;
+        yb[j] = r.nan_b ? qnan : ((pb.p - pa.p) * r.gv) * pa.f;  // pa and pb share the scale
       }
       if (FULL) {
         if (oa) store_group_vec<DT>(oa, g, ya);
@@ -123,15 +123,16 @@ __device__ __forceinline__ void bwd_store(const RowBwd& r, const float (&xa)[UB]
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float lp = (xa[u][j] - r.m) - r.ls;  // log p_j
-          const float pj = expf_fast(lp);
-          y[j] = r.nan_a ? qnan : mul0(pj, lp + r.res) * (-r.gv);
+          const PScaled pj = exp_split(lp);
+          y[j] = r.nan_a ? qnan : (mul0(pj.p, lp + r.res) * (-r.gv)) * pj.f;
         }
       } else {
         float pr[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          pr[j] = expf_fast((xa[u][j] - r.m) - r.ls);
-          y[j] = r.zero ? 0.0f : (r.nan_a ? qnan : -r.gv * pr[j]);
+          const PScaled pj = exp_split((xa[u][j] - r.m) - r.ls);
+          pr[j] = pj.p * pj.f;
+          y[j] = r.zero ? 0.0f : (r.nan_a ? qnan : (-r.gv * pj.p) * pj.f);
         }
         if (g == r.tg) {
 #pragma unroll

@@ -21,6 +21,14 @@
 //   -inf has been seen.
 // - S and W are centred on ref = m, or on 0 while m = -inf (then S = 0 and
 //   W = 0 unless a NaN was seen).
+// - The logits ops keep S and W multiplied by 2^64: a term e^(z - m) below
+//   2^-126 (a column 87.3 to 131.7 nats below the max) is then still a normal
+//   number. v_exp_f32 returns 0 for results below 2^-126, and such terms are
+//   what H and KL are made of on a row that is one-hot up to a far tail. The
+//   scale rides on the exponent argument (exp_scaled: one fma where the
+//   unscaled form has one multiply); merges and rescales multiply by the
+//   scaled exponential and by 2^-64, which leaves an unscaled state unscaled
+//   too; finalization divides the scale out in double precision.
 // - A NaN input always reaches S (e^(NaN) = NaN, and 0 * NaN = NaN in the
 //   plain products used for S), so S carries "row undefined" to the end.
 #pragma once
@@ -76,8 +84,35 @@ extern "C" __device__ float vws_llvm_fmul_legacy(float, float) __asm("llvm.amdgc
 // a * b, but exactly 0 when a or b is 0 (even if the other is inf or NaN).
 __device__ __forceinline__ float mul0(float a, float b) { return vws_llvm_fmul_legacy(a, b); }
 
-// e^x through the hardware base-2 exponential (v_exp_f32).
+// e^x through the hardware base-2 exponential (v_exp_f32). Results below 2^-126 come out as 0:
+// used where such a term is negligible against the sum it joins (the forward statistics).
 __device__ __forceinline__ float expf_fast(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+constexpr float kSumScaleLog2 = 64.0f;  // the running sums' scale 2^64, as an exponent
+constexpr float kSumUnscale = 0x1p-64f;
+
+// 2^64 e^d for d <= 0: exact for d = 0, a normal number down to d = -131.7 nats.
+__device__ __forceinline__ float exp_scaled(float d) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(d, kLog2e, kSumScaleLog2));
+}
+
+// log of a running sum S kept at the 2^64 scale: the scale is divided out exactly in double.
+__device__ __forceinline__ double log_unscaled(float S) { return log((double)S * 0x1p-64); }
+
+// e^x for gradients as a pair (p, f) with e^x = p f, p = 2^64 e^x and f = 2^-64: a probability
+// below 2^-126, where v_exp_f32 returns 0 but bf16 still holds the gradient (down to 2^-133, and
+// far above that once multiplied by g and a log-probability), is a normal number at that scale.
+// A caller forms its whole product with p and multiplies by f last, so the result is rounded once
+// at its own magnitude. The scale rides on the exponent argument (one fma where the unscaled
+// form has one multiply): rounding that argument near 64 costs up to 2^-18 ln 2 relative in p,
+// far inside the fp32 2e-5 bound, and one multiply by f per gradient. Choosing the scale per
+// element instead cost the KL backward 5% and the top-k backward 13%.
+struct PScaled {
+  float p, f;
+};
+__device__ __forceinline__ PScaled exp_split(float x) {
+  return PScaled{__builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, kSumScaleLog2)), kSumUnscale};
+}
 
 template <int DT>
 struct ElemSize {
@@ -264,11 +299,11 @@ __device__ __forceinline__ State1 merge1(const State1& x, const State1& y) {
   const float M = fmaxf(x.m, y.m);
   const float R = ref_of(M);
   const float dx = x.m - R, dy = y.m - R;  // -inf for an empty part, or on overflow
-  const float sx = expf_fast(dx), sy = expf_fast(dy);
+  const float sx = exp_scaled(dx), sy = exp_scaled(dy);
   State1 r;
   r.m = M;
-  r.S = sx * x.S + sy * y.S;
-  r.W = WITH_W ? mul0(sx, x.W + dx * x.S) + mul0(sy, y.W + dy * y.S) : 0.0f;
+  r.S = sx * (x.S * kSumUnscale) + sy * (y.S * kSumUnscale);
+  r.W = WITH_W ? mul0(sx, (x.W + dx * x.S) * kSumUnscale) + mul0(sy, (y.W + dy * y.S) * kSumUnscale) : 0.0f;
   return r;
 }
 
@@ -277,17 +312,17 @@ __device__ __forceinline__ StateKL merge_kl(const StateKL& x, const StateKL& y) 
   const float Ma = fmaxf(x.ma, y.ma), Mb = fmaxf(x.mb, y.mb);
   const float Ra = ref_of(Ma), Rb = ref_of(Mb);
   const float dax = x.ma - Ra, day = y.ma - Ra;
-  const float sax = expf_fast(dax), say = expf_fast(day);
-  const float sbx = expf_fast(x.mb - Rb), sby = expf_fast(y.mb - Rb);
+  const float sax = exp_scaled(dax), say = exp_scaled(day);
+  const float sbx = exp_scaled(x.mb - Rb), sby = exp_scaled(y.mb - Rb);
   // W_i is centred on (ref(m_a,i), ref(m_b,i)); shifting both references:
   // W' = s_a,i (W_i + ((m_a,i - Ra) - (ref(m_b,i) - Rb)) S_A,i)
   const float shx = dax - (ref_of(x.mb) - Rb), shy = day - (ref_of(y.mb) - Rb);
   StateKL r;
   r.ma = Ma;
   r.mb = Mb;
-  r.Sa = sax * x.Sa + say * y.Sa;
-  r.Sb = sbx * x.Sb + sby * y.Sb;
-  r.W = mul0(sax, x.W + shx * x.Sa) + mul0(say, y.W + shy * y.Sa);
+  r.Sa = sax * (x.Sa * kSumUnscale) + say * (y.Sa * kSumUnscale);
+  r.Sb = sbx * (x.Sb * kSumUnscale) + sby * (y.Sb * kSumUnscale);
+  r.W = mul0(sax, (x.W + shx * x.Sa) * kSumUnscale) + mul0(say, (y.W + shy * y.Sa) * kSumUnscale);
   r.F = x.F | y.F;
   return r;
 }

@@ -11,7 +11,8 @@
 // Per batch the lane takes the batch max first and rescales its state once
 // (second commit message of PR #8838: when the max grows, the weighted sum is
 // rescaled like the sum-exp), then accumulates e = exp(z - m),
-// S += e, W += e (z - m) with the zero-weight product. Lanes are merged by a
+// S += e, W += e (z - m) with the zero-weight product (S and W at the 2^64
+// scale of device.h). Lanes are merged by a
 // butterfly over the wave, waves through LDS in wave order ("lane
 // re-centring", fix commit of the 0 x inf thread).
 //
@@ -35,9 +36,9 @@ __device__ __forceinline__ void update1(State1& st, const float (&x)[U][8]) {
     for (int j = 0; j < 8; ++j) bm = fmaxf(bm, x[k][j]);
   if (bm > st.m) {
     const float d = st.m - bm;  // -inf when the state is empty
-    const float s = expf_fast(d);
-    if (WITH_W) st.W = mul0(s, st.W + d * st.S);
-    st.S = s * st.S;
+    const float s = exp_scaled(d);
+    if (WITH_W) st.W = mul0(s, (st.W + d * st.S) * kSumUnscale);
+    st.S = s * (st.S * kSumUnscale);
     st.m = bm;
   }
   const float ref = ref_of(st.m);
@@ -46,7 +47,7 @@ __device__ __forceinline__ void update1(State1& st, const float (&x)[U][8]) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float d = x[k][j] - ref;
-      const float e = expf_fast(d);
+      const float e = exp_scaled(d);  // 2^64 e^d
       st.S += e;
       if (WITH_W) st.W += mul0(e, d);
     }
@@ -70,10 +71,14 @@ __device__ __forceinline__ void update_kl(StateKL& st, const float (&xa)[U][8], 
     // both shifts are applied as one difference, so identical inputs (A = B) keep W exactly 0.
     const float nma = ga ? bma : st.ma, nmb = gb ? bmb : st.mb;
     const float sh = (ref_of(st.ma) - ref_of(nma)) - (ref_of(st.mb) - ref_of(nmb));
-    const float s = ga ? expf_fast(st.ma - nma) : 1.0f;  // 0 when the state was empty
-    st.W = mul0(s, st.W + sh * st.Sa);
-    st.Sa = s * st.Sa;
-    if (gb) st.Sb = expf_fast(st.mb - nmb) * st.Sb;
+    if (ga) {
+      const float s = exp_scaled(st.ma - nma);  // 0 when the state was empty
+      st.W = mul0(s, (st.W + sh * st.Sa) * kSumUnscale);
+      st.Sa = s * (st.Sa * kSumUnscale);
+    } else {
+      st.W += sh * st.Sa;
+    }
+    if (gb) st.Sb = exp_scaled(st.mb - nmb) * (st.Sb * kSumUnscale);
     st.ma = nma;
     st.mb = nmb;
   }
@@ -92,8 +97,8 @@ __device__ __forceinline__ void update_kl(StateKL& st, const float (&xa)[U][8], 
     for (int j = 0; j < 8; ++j) {
       const float da = xa[k][j] - ra;
       const float db = xb[k][j] - rb;
-      const float ea = expf_fast(da);
-      const float eb = expf_fast(db);
+      const float ea = exp_scaled(da);
+      const float eb = exp_scaled(db);
       st.Sa += ea;
       st.Sb += eb;
       st.W += mul0(ea, da - db);
@@ -102,7 +107,7 @@ __device__ __forceinline__ void update_kl(StateKL& st, const float (&xa)[U][8], 
 
 // ---- finalization of a row from its merged state ----------------------------------
 
-__device__ __forceinline__ double log_d(float S) { return log((double)S); }
+__device__ __forceinline__ double log_d(float S) { return log_unscaled(S); }
 
 template <int DT>
 __device__ void finalize1_logprobs(const FwdArgs& p, int64_t row, const State1& st) {

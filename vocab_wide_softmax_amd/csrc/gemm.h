@@ -17,6 +17,11 @@
 // are not padded; 16-byte chunks are XOR-swizzled by row instead, which keeps
 // the fragment reads free of bank conflicts.
 //
+// Split A (SA = 2): A is a pair of bf16 planes, hi and lo, whose sum carries an fp32 operand to
+// about 2^-17 relative; both planes are staged and contracted with the same B tile into the same
+// fp32 accumulators (all hi MFMAs of a k-slice, then all lo MFMAs, so that the two products
+// feeding one accumulator are never back to back).
+//
 // MFMA 32x32x16 bf16 lane layout (checked on the device): lane l supplies
 // A[l % 32][8 (l / 32) + e] and B[8 (l / 32) + e][l % 32], e = 0..7, and holds
 // accumulator v = C[8 (v / 4) + 4 (l / 32) + (v % 4)][l % 32].
@@ -42,20 +47,27 @@ typedef __attribute__((address_space(3))) void lds_void;
 // Source of the 16-byte chunks that lie past the reduction length: they must add nothing.
 extern __device__ const uint32_t kZeroChunk[4];
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int LA_, int LB_, int NSTAGE_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int LA_, int LB_, int NSTAGE_, int SA_ = 1, int PIECES_ = 2>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, LA = LA_, LB = LB_, NSTAGE = NSTAGE_;
+  static constexpr int SA = SA_;  // planes of A: 1, or 2 for a bf16 (hi, lo) pair
+  static constexpr int PIECES = PIECES_;  // buffer-path refill pieces per stage (see mainloop_t)
   static constexpr int NW = WM * WN, NT = NW * 64;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
-  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int A_PLANE = BM * BK * 2;  // LDS bytes of one A plane of a stage
+  static constexpr int A_BYTES = SA * A_PLANE, B_BYTES = BN * BK * 2, STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
-  static constexpr int A_INSTR = A_BYTES / 1024 / NW, B_INSTR = B_BYTES / 1024 / NW;  // DMA loads per wave
+  static constexpr int AP_INSTR = A_PLANE / 1024 / NW;  // DMA loads per wave of one A plane
+  static constexpr int A_INSTR = SA * AP_INSTR, B_INSTR = B_BYTES / 1024 / NW;  // DMA loads per wave
   static constexpr int LOADS_PER_STAGE = A_INSTR + B_INSTR;
+  static constexpr int MFMAS = SA * FM * FN;  // MFMAs per wave per 16-wide k-slice
+  static_assert(SA == 1 || SA == 2, "planes");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(BK == 32 || BK == 64, "ROWK swizzles exist for 4 and 8 chunks per row");
   static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "tile");
   static_assert((LA != KROW || BM % 128 == 0) && (LB != KROW || BN % 128 == 0), "KROW swizzle needs 16 chunks per k-row");
-  static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole DMA instructions per wave");
+  static_assert(A_PLANE % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole DMA instructions per wave");
 };
 
 // Global operand view.
@@ -64,7 +76,12 @@ struct Operand {
   int64_t ld;    // elements between consecutive rows (ROWK) or consecutive k (KROW); multiple of 8
   int64_t rows;  // valid rows (>= 8 for KROW); rows beyond are clamped on load and masked by the caller
   int64_t K;     // valid reduction length, multiple of 8 for ROWK; chunks past it read zeros
+  int64_t plane = 0;  // split A: elements from the hi plane to the lo plane (same layout)
 };
+
+__device__ __forceinline__ Operand lo_plane(const Operand& a) {
+  return Operand{a.base + a.plane, a.ld, a.rows, a.K, 0};
+}
 
 // Swizzled chunk of a ROWK row (BK / 8 chunks of 16 B per row; the pattern keeps 8 and
 // 16 consecutive rows at one chunk on distinct banks) and of a KROW k-row (R / 8 chunks).
@@ -199,23 +216,32 @@ __device__ __forceinline__ void read_frag(u32x4& f, const char* lds, int r0, int
 
 template <class C>
 struct Frags {
-  u32x4 a[C::FM], b[C::FN];
+  u32x4 a[C::SA][C::FM], b[C::FN];
 };
 
 template <class C>
 __device__ __forceinline__ void read_frags(Frags<C>& F, const char* sa, const char* sb, int wm, int wn, int kk, int lane) {
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) read_frag<C::LA, C::BM, C::BK>(F.a[i], sa, wm * C::TM + i * 32, kk, lane);
+  for (int pl = 0; pl < C::SA; ++pl)
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+      read_frag<C::LA, C::BM, C::BK>(F.a[pl][i], sa + pl * C::A_PLANE, wm * C::TM + i * 32, kk, lane);
 #pragma unroll
   for (int j = 0; j < C::FN; ++j) read_frag<C::LB, C::BN, C::BK>(F.b[j], sb, wn * C::TN + j * 32, kk, lane);
 }
 
-// Wait for every outstanding LDS read and make the fragments depend on that wait.
+// Wait for every outstanding LDS read and make the fragments depend on that wait. The
+// scheduling barrier keeps the wait below the previous slice's MFMAs: the compiler may
+// otherwise hoist it above them (they touch no memory), and the fragment reads issued at
+// the start of that slice would then stall its MFMAs instead of overlapping them.
 template <class C>
 __device__ __forceinline__ void settle(Frags<C>& F) {
+  __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) asm volatile("" : "+v"(F.a[i]));
+  for (int pl = 0; pl < C::SA; ++pl)
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) asm volatile("" : "+v"(F.a[pl][i]));
 #pragma unroll
   for (int j = 0; j < C::FN; ++j) asm volatile("" : "+v"(F.b[j]));
 }
@@ -232,14 +258,20 @@ struct Acc {
   }
 };
 
-template <class C>
+// MFMA n of a slice: plane n / (FM FN), block ((n mod FM FN) / FN, n mod FN).
+template <class C, int N>
+__device__ __forceinline__ void mfma_n(Acc<C>& acc, const Frags<C>& F) {
+  constexpr int pl = N / (C::FM * C::FN), r = N % (C::FM * C::FN), i = r / C::FN, j = r % C::FN;
+  acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, F.a[pl][i]),
+                                                        __builtin_bit_cast(bf16x8, F.b[j]), acc.c[i][j], 0, 0, 0);
+}
+
+template <class C, int N = 0>
 __device__ __forceinline__ void mfmas(Acc<C>& acc, const Frags<C>& F) {
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-      acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, F.a[i]),
-                                                            __builtin_bit_cast(bf16x8, F.b[j]), acc.c[i][j], 0, 0, 0);
+  if constexpr (N < C::MFMAS) {
+    mfma_n<C, N>(acc, F);
+    mfmas<C, N + 1>(acc, F);
+  }
 }
 
 // Wait until at most n of this wave's DMA loads are outstanding (loads complete in order).
@@ -261,11 +293,11 @@ __device__ __forceinline__ void stage_ready(int s, int nk) {
   asm volatile("" ::: "memory");  // keep LDS reads and DMA issues on their side of the barrier
 }
 
-// Buffer-path refills go out in this many pieces per stage (see mainloop_t). Two pieces, each
-// interleaved one load per MFMA, ran the four GEMMs 1.2-1.9% faster than one burst of a stage's
-// loads after the barrier (bit-identical results); four pieces were slower (the last piece then
-// has under two slices of lead time).
-constexpr int kRefillPieces = 2;
+// Buffer-path refills go out in Cfg::PIECES pieces per stage (see mainloop_t). For the plain
+// GEMMs (BK = 64, four slices per stage) two pieces, each interleaved one load per MFMA, ran 1.2-1.9%
+// faster than one burst of a stage's loads after the barrier (bit-identical results); four pieces
+// were slower (the last piece then has under two slices of lead time). The split-A GEMMs (BK = 32,
+// two slices per stage, twice the MFMAs per slice) run 5-7% faster with one burst.
 
 // Loads [J0, J1) of one stage's refill, counted over the A loads then the B loads (buffer path).
 template <class C, int J0, int J1>
@@ -273,9 +305,15 @@ __device__ __forceinline__ void issue_buf_range(const Operand& A, const Operand&
                                                 char* lds, int wave, int lane) {
   char* st = lds + (s % C::NSTAGE) * C::STAGE_BYTES;
   const int64_t k0 = (int64_t)s * C::BK;
-  dma_tile_buf<C::LA, C::BM, C::BK, C::NW, C::A_INSTR, J0, J1>(A, m0, k0, st, wave, lane);
-  dma_tile_buf<C::LB, C::BN, C::BK, C::NW, C::B_INSTR, J0 - C::A_INSTR, J1 - C::A_INSTR>(B, n0, k0, st + C::A_BYTES,
-                                                                                           wave, lane);
+  constexpr int P = C::AP_INSTR;
+  if constexpr (J0 < P)
+    dma_tile_buf<C::LA, C::BM, C::BK, C::NW, P, J0, J1>(A, m0, k0, st, wave, lane);
+  if constexpr (C::SA == 2 && J0 < 2 * P && J1 > P)
+    dma_tile_buf<C::LA, C::BM, C::BK, C::NW, P, J0 - P, J1 - P>(lo_plane(A), m0, k0, st + C::A_PLANE, wave, lane);
+  if constexpr (J1 > C::A_INSTR)
+    dma_tile_buf<C::LB, C::BN, C::BK, C::NW, C::B_INSTR, J0 - C::A_INSTR, J1 - C::A_INSTR>(B, n0, k0,
+                                                                                             st + C::A_BYTES, wave,
+                                                                                             lane);
 }
 
 // MFMA n of the slice (block n / FN, n % FN), then refill load J0 + n of stage s while n < J1 - J0.
@@ -285,10 +323,8 @@ template <class C, int J0, int J1, int N>
 __device__ __forceinline__ void mfmas_loads(Acc<C>& acc, const Frags<C>& F, const Operand& A, const Operand& B,
                                             int64_t m0, int64_t n0, int s, bool live, char* lds, int wave,
                                             int lane) {
-  if constexpr (N < C::FM * C::FN) {
-    constexpr int i = N / C::FN, j = N % C::FN;
-    acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, F.a[i]),
-                                                          __builtin_bit_cast(bf16x8, F.b[j]), acc.c[i][j], 0, 0, 0);
+  if constexpr (N < C::MFMAS) {
+    mfma_n<C, N>(acc, F);
     if constexpr (N < J1 - J0) {
       __builtin_amdgcn_sched_barrier(0);
       if (live) issue_buf_range<C, J0 + N, J0 + N + 1>(A, B, m0, n0, s, lds, wave, lane);
@@ -315,7 +351,7 @@ __device__ __forceinline__ void mfmas_piece(Acc<C>& acc, const Frags<C>& F, int 
 //
 // Schedule: the fragments of the next k-slice are read while the MFMAs of the current
 // one run; at the last slice of stage s the workgroup waits for stage s + 1, refills the
-// stage-s buffer with stage s + NSTAGE (on the buffer path in kRefillPieces pieces spread over
+// stage-s buffer with stage s + NSTAGE (on the buffer path in Cfg::PIECES pieces spread over
 // the following slices), and reads stage s + 1's first fragments before stage s's last MFMAs.
 template <class C, bool EDGE, bool BUF>
 __device__ __forceinline__ void mainloop_t(const Operand& A, const Operand& B, int64_t m0, int64_t n0, int64_t K,
@@ -332,10 +368,14 @@ __device__ __forceinline__ void mainloop_t(const Operand& A, const Operand& B, i
     char* st = lds + (s % C::NSTAGE) * C::STAGE_BYTES;
     const int64_t k0 = (int64_t)s * C::BK;
     if constexpr (BUF) {
-      dma_tile_buf<C::LA, C::BM, C::BK, C::NW, C::A_INSTR>(A, m0, k0, st, wave, lane);
+      dma_tile_buf<C::LA, C::BM, C::BK, C::NW, C::AP_INSTR>(A, m0, k0, st, wave, lane);
+      if constexpr (C::SA == 2)
+        dma_tile_buf<C::LA, C::BM, C::BK, C::NW, C::AP_INSTR>(lo_plane(A), m0, k0, st + C::A_PLANE, wave, lane);
       dma_tile_buf<C::LB, C::BN, C::BK, C::NW, C::B_INSTR>(B, n0, k0, st + C::A_BYTES, wave, lane);
     } else {
-      dma_tile<C::LA, C::BM, C::BK, C::NW, C::A_INSTR, EDGE>(A, m0, k0, st, wave, lane);
+      dma_tile<C::LA, C::BM, C::BK, C::NW, C::AP_INSTR, EDGE>(A, m0, k0, st, wave, lane);
+      if constexpr (C::SA == 2)
+        dma_tile<C::LA, C::BM, C::BK, C::NW, C::AP_INSTR, EDGE>(lo_plane(A), m0, k0, st + C::A_PLANE, wave, lane);
       dma_tile<C::LB, C::BN, C::BK, C::NW, C::B_INSTR, EDGE>(B, n0, k0, st + C::A_BYTES, wave, lane);
     }
   };
@@ -353,9 +393,9 @@ __device__ __forceinline__ void mainloop_t(const Operand& A, const Operand& B, i
   // Refill pieces: with SP > 1 (buffer path), stage s + NSTAGE's loads go out in SP pieces of PL
   // loads, piece 0 right after the barrier that frees its buffer, piece p during slice p - 1 of the
   // next stage, each interleaved with a slice's MFMAs.
-  constexpr int SP = BUF ? kRefillPieces : 1;
+  constexpr int SP = BUF ? C::PIECES : 1;
   constexpr int PL = C::LOADS_PER_STAGE / SP;
-  static_assert(SP >= 1 && SP <= KQ && C::LOADS_PER_STAGE % SP == 0 && PL <= C::FM * C::FN, "refill pieces");
+  static_assert(SP >= 1 && SP <= KQ && C::LOADS_PER_STAGE % SP == 0 && PL <= C::MFMAS, "refill pieces");
   int cur = 0;
   for (int s = 0; s < nk; ++s) {
 #pragma unroll
@@ -398,6 +438,7 @@ __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int
                                          char* lds, Acc<C>& acc) {
   const bool interior = m0 + C::BM <= A.rows && n0 + C::BN <= B.rows && K % C::BK == 0 && A.K >= K && B.K >= K;
   const bool fits = stage_span_fits<C::LA, C::BM, C::BK>(A) && stage_span_fits<C::LB, C::BN, C::BK>(B);
+  // (the lo plane of a split A has the hi plane's layout, so its stages span the same bytes)
   if (interior && fits) mainloop_t<C, false, true>(A, B, m0, n0, K, lds, acc);
   else if (interior) mainloop_t<C, false, false>(A, B, m0, n0, K, lds, acc);
   else mainloop_t<C, true, false>(A, B, m0, n0, K, lds, acc);

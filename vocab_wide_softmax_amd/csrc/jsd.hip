@@ -65,10 +65,14 @@ __device__ __forceinline__ JsdRow jsd_row(const float* st4, float beta) {
 // entries masked) recomputes it as mx + log2((1-b) 2^(us-mx) + b 2^(ut-mx)) with
 // mx = max(us, ut), whose argument lies in [min(b, 1-b), 1] (NaN when both are masked,
 // where both weights are 0).
+// FULL (the backward): ps and pt are kept at the 2^64 scale of exp_split, p = ps fs and p = pt ft,
+// so that a gradient whose probability lies below 2^-126 is formed at scale and rounded once
+// (device.h); the divergence pass sums its terms against ones near 1 and keeps fs = ft = 1.
 struct JsdGroup {
-  float us[8], ut[8], ps[8], pt[8], lm[8];
+  float us[8], ut[8], ps[8], pt[8], fs[8], ft[8], lm[8];
 };
 
+template <bool FULL>
 __device__ __forceinline__ void jsd_group(const JsdRow& r, const float (&xs)[8], const float (&xt)[8], JsdGroup& q) {
   bool small = false;
 #pragma unroll
@@ -77,9 +81,16 @@ __device__ __forceinline__ void jsd_group(const JsdRow& r, const float (&xs)[8],
     // and the fma rounds once
     q.us[j] = __builtin_fmaf(xs[j] - r.ms, kLog2e, -r.lss2);
     q.ut[j] = __builtin_fmaf(xt[j] - r.mt, kLog2e, -r.lst2);
-    q.ps[j] = __builtin_amdgcn_exp2f(q.us[j]);
-    q.pt[j] = __builtin_amdgcn_exp2f(q.ut[j]);
-    const float mix = __builtin_fmaf(r.wt, q.pt[j], r.ws * q.ps[j]);
+    if constexpr (FULL) {
+      q.ps[j] = __builtin_amdgcn_exp2f(q.us[j] + kSumScaleLog2);
+      q.pt[j] = __builtin_amdgcn_exp2f(q.ut[j] + kSumScaleLog2);
+      q.fs[j] = q.ft[j] = kSumUnscale;
+    } else {
+      q.ps[j] = __builtin_amdgcn_exp2f(q.us[j]);
+      q.pt[j] = __builtin_amdgcn_exp2f(q.ut[j]);
+      q.fs[j] = q.ft[j] = 1.0f;
+    }
+    const float mix = __builtin_fmaf(r.wt, q.pt[j] * q.ft[j], r.ws * (q.ps[j] * q.fs[j]));
     q.lm[j] = __builtin_amdgcn_logf(mix);
     small |= !(mix >= kFltMin);
   }
@@ -89,7 +100,7 @@ __device__ __forceinline__ void jsd_group(const JsdRow& r, const float (&xs)[8],
       const float mx = fmaxf(q.us[j], q.ut[j]);
       const float inner =
           __builtin_fmaf(r.wt, __builtin_amdgcn_exp2f(q.ut[j] - mx), r.ws * __builtin_amdgcn_exp2f(q.us[j] - mx));
-      const float mix = __builtin_fmaf(r.wt, q.pt[j], r.ws * q.ps[j]);
+      const float mix = __builtin_fmaf(r.wt, q.pt[j] * q.ft[j], r.ws * (q.ps[j] * q.fs[j]));
       if (!(mix >= kFltMin)) q.lm[j] = mx + __builtin_amdgcn_logf(inner);
     }
   }
@@ -137,7 +148,7 @@ __global__ __launch_bounds__(kJsdBlock) void jsd_div_kernel(JsdArgs p) {
     float Ks = 0.0f, Kt = 0.0f;  // base-2 sums; scaled by ln 2 once per row
     auto accumulate = [&](const float (&xs)[8], const float (&xt)[8]) {
       JsdGroup q;
-      jsd_group(r, xs, xt, q);
+      jsd_group<false>(r, xs, xt, q);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         Ks += mul0(q.ps[j], q.us[j] - q.lm[j]);
@@ -235,12 +246,12 @@ __device__ __forceinline__ void jsd_bwd_groups(const JsdRow& r, float Ks, float 
       load_group<DT, true>(rt, g, V, g_full, xt);
     }
     JsdGroup q;
-    jsd_group(r, xs, xt, q);
+    jsd_group<true>(r, xs, xt, q);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       // (log p - log M) - K in natural units: ln 2 (u - l) - K
-      ys[j] = r.bad ? qnan : mul0(q.ps[j], __builtin_fmaf(kLn2, q.us[j] - q.lm[j], -Ks)) * gs;
-      yt[j] = r.bad ? qnan : mul0(q.pt[j], __builtin_fmaf(kLn2, q.ut[j] - q.lm[j], -Kt)) * gt;
+      ys[j] = r.bad ? qnan : (mul0(q.ps[j], __builtin_fmaf(kLn2, q.us[j] - q.lm[j], -Ks)) * gs) * q.fs[j];
+      yt[j] = r.bad ? qnan : (mul0(q.pt[j], __builtin_fmaf(kLn2, q.ut[j] - q.lm[j], -Kt)) * gt) * q.ft[j];
     }
     if (FULL) {
       if (os) store_group_vec<DT>(os, g, ys);

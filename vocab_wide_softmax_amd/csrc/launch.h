@@ -102,18 +102,25 @@ struct LinArgs {
   float* part;   // workspace [N, chunks, 2]
   float* zt;     // workspace [N]
   int32_t chunks, tiles_per_chunk;
-  // backward
+  // backward, one vocabulary chunk [v0, v0 + cw) at a time
   const float* g;
   int64_t g_stride;
-  uint16_t* dz;  // workspace [N, ldz] bf16
-  int64_t ldz;
-  int64_t ldw_out;  // row stride of dW
+  uint16_t* dzh;  // workspace [N, ldc] bf16: hi part of the chunk's dz
+  uint16_t* dzl;  // workspace [N, ldc] bf16: lo part, dz - hi rounded
+  int64_t ldc;    // row pitch of the dz planes (columns [cw, ldc) hold zeros)
+  int64_t v0, cw;
+  float* dh_acc;  // workspace [N, H] fp32: dh summed over the chunks so far (more than one chunk)
 };
+
+// Epilogue of the dh contraction of one chunk.
+enum DhMode : int { kDhStore = 0, kDhFirst = 1, kDhAdd = 2, kDhLast = 3 };
 
 struct GemmArgs {
   gemm::Operand A, B;
-  uint16_t* C;
+  uint16_t* C;     // bf16 output, row pitch ldc
+  float* acc;      // fp32 running sum (dh over chunks), row pitch ldc
   int64_t ldc, M, Nc, K;
+  int32_t mode;    // DhMode for dh; kDhStore for dW
 };
 
 // Forward vocabulary chunking; split_hint as for the logits ops (0 automatic, >= 1 that many
@@ -121,7 +128,10 @@ struct GemmArgs {
 int32_t lin_tiles_per_chunk(int64_t N, int64_t V, int split_hint);
 int lin_chunks(int64_t N, int64_t V, int split_hint);
 hipError_t launch_lin_fwd(LinArgs p, int split_hint, hipStream_t stream);
-hipError_t launch_lin_bwd(LinArgs p, uint16_t* dh, uint16_t* dW, hipStream_t stream);
+// Backward vocabulary chunking: tiles of 256 columns per chunk (split_hint 0 or -1: 32 tiles, a
+// function of nothing; k >= 1: k chunks), and the workspace layout built on it.
+int32_t lin_bwd_tiles_per_chunk(int64_t V, int split_hint);
+hipError_t launch_lin_bwd(LinArgs p, int split_hint, uint16_t* dh, uint16_t* dW, hipStream_t stream);
 
 // Workgroups per launch: kernels loop over virtual blocks beyond this, which
 // keeps grid size x workgroup size below the 2^32 work-item limit.

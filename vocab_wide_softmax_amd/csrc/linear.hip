@@ -12,11 +12,13 @@
 // shards, inside one GPU) and forms logp = z_t - lse, with z_t from
 // lin_target_kernel (one wave per token, fp32 dot product).
 //
-// Backward: dz = g (onehot(t) - p) with p = exp((z - m) - log S) recomputed
-// from a second MFMA pass (lin_dz_kernel, A = h rows, B = W rows, so a lane's
-// 32 consecutive vocabulary columns make coalesced bf16 stores of dz [N, V]);
-// then dh = dz W and dW = dz^T h by gemm_store_kernel, reading the transposed
-// operands through gfx950's transposing LDS reads (gemm.h).
+// Backward, one vocabulary chunk of 8192 columns at a time (the chunked backward of the review
+// nitpick): dz = g (onehot(t) - p) with p = exp((z - m) - log S) recomputed from a second MFMA
+// pass (lin_dz_kernel, A = h rows, B = W rows, so a lane's 32 consecutive vocabulary columns
+// make coalesced stores of dz [N, chunk]), kept as a bf16 (hi, lo) pair; then dW of the chunk's
+// vocabulary rows = dz^T h, and dh += dz W_chunk summed in fp32 over the chunks, by
+// gemm_pair_kernel (both planes of dz contracted into one fp32 accumulator), reading the
+// transposed operands through gfx950's transposing LDS reads (gemm.h).
 #include "device.h"
 #include "gemm.h"
 #include "launch.h"
@@ -30,8 +32,11 @@ using gemm::Operand;
 using gemm::ROWK;
 
 typedef Cfg<256, 256, 64, 2, 4, ROWK, ROWK, 2> CfgNT;  // A, B both reduction-contiguous
-typedef Cfg<256, 256, 64, 2, 4, ROWK, KROW, 2> CfgNN;  // dh = dz W
-typedef Cfg<256, 256, 64, 2, 4, KROW, KROW, 2> CfgTN;  // dW = dz^T h
+// dh = dz W and dW = dz^T h with dz a bf16 (hi, lo) pair: 3 stages of BK = 32 (48 KB each), wave
+// tiles of 64 x 128 so that a k-slice reads 2 + 2 A fragments and 4 B fragments for 16 MFMAs
+// (128 x 64 wave tiles: 7-13% slower), each stage's refill in one burst.
+typedef Cfg<256, 256, 32, 4, 2, ROWK, KROW, 3, 2, 1> CfgNN2;  // dh = dz W
+typedef Cfg<256, 256, 32, 4, 2, KROW, KROW, 3, 2, 1> CfgTN2;  // dW = dz^T h
 
 namespace gemm {
 __device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
@@ -179,44 +184,48 @@ __global__ __launch_bounds__(256) void lin_combine_kernel(LinArgs p) {
 
 // ---- backward ------------------------------------------------------------------------
 
-// Block -> (token tile, vocabulary tile) for the dz pass. Block b runs on XCD b % 8, and an
-// XCD runs 32 blocks at a time; those 32 form a patch of 4 token tiles x 8 vocabulary tiles,
-// so its L2 streams 4 h panels and 8 W tiles per k-step (one vocabulary tile at a time would
-// stream 32 h panels for 1 W tile). The 8 XCDs' patches lie side by side along the
-// vocabulary (a super-tile of 4 x 64 tiles), and super-tiles go token group fastest, so a
-// group of 64 W tiles is reused from the MALL by every token group in turn. Tiles outside
-// the whole super-tiles follow in plain order.
+// Block -> (token tile, vocabulary tile of the chunk) for the dz pass. Block b runs on XCD b % 8,
+// and an XCD runs 32 blocks at a time; those 32 form a patch of 4 token tiles x 8 vocabulary
+// tiles, so its L2 streams 4 h panels and 8 W tiles per k-step (one vocabulary tile at a time
+// would stream 32 h panels for 1 W tile). The 8 XCDs' patches make a super-tile of 8 token tiles
+// x 32 vocabulary tiles (2 x 4 patches), and super-tiles go token fastest, so the chunk's W tiles
+// are reused from the MALL by every token group in turn. Tiles outside the whole super-tiles
+// follow in plain order.
 __device__ __forceinline__ void dz_tile(int64_t b, int64_t ntt, int64_t nvt, int64_t& tt, int64_t& vt) {
-  const int64_t ntt4 = (ntt / 4) * 4, nvt64 = (nvt / 64) * 64;
-  const int64_t nfull = ntt4 * nvt64;
+  const int64_t ntt8 = (ntt / 8) * 8, nvt32 = (nvt / 32) * 32;
+  const int64_t nfull = ntt8 * nvt32;
   if (b < nfull) {
-    const int64_t x = b % 8, q = b / 8, s = q / 32, ngt = ntt4 / 4;
-    tt = (s % ngt) * 4 + q % 4;
-    vt = (s / ngt) * 64 + x * 8 + (q / 4) % 8;
+    const int64_t x = b % 8, q = b / 8, s = q / 32, w = q % 32, nst = ntt8 / 8;
+    tt = (s % nst) * 8 + (x / 4) * 4 + w % 4;
+    vt = (s / nst) * 32 + (x % 4) * 8 + w / 4;
     return;
   }
-  const int64_t r = b - nfull, r1 = ntt4 * (nvt - nvt64);
+  const int64_t r = b - nfull, r1 = ntt8 * (nvt - nvt32);
   if (r < r1) {  // whole token groups, vocabulary tiles past the last super-tile
-    tt = r % ntt4;
-    vt = nvt64 + r / ntt4;
-  } else {  // the last ntt - ntt4 token tiles, every vocabulary tile
-    const int64_t r2 = r - r1, nt2 = ntt - ntt4;
-    tt = ntt4 + r2 % nt2;
+    tt = r % ntt8;
+    vt = nvt32 + r / ntt8;
+  } else {  // the last ntt - ntt8 token tiles, every vocabulary tile
+    const int64_t r2 = r - r1, nt2 = ntt - ntt8;
+    tt = ntt8 + r2 % nt2;
     vt = r2 / nt2;
   }
 }
 
+// dz of one vocabulary chunk: recompute the logits tile z = h W^T (fp32 accumulation), form
+// dz = g (1[v = t] - p) with p = exp((z - m) - log S) in fp32, and store it as the bf16 pair
+// hi = rne(dz), lo = rne(dz - hi), which carries dz to about 2^-17 relative into the two
+// contractions (a single bf16 dz would cost up to 2^-9 per term of dh and dW).
 template <class C>
 __global__ __launch_bounds__(C::NT) void lin_dz_kernel(LinArgs p) {
   extern __shared__ __align__(16) char lds[];
-  const int64_t ntt = (p.N + C::BM - 1) / C::BM, nvt = (p.V + C::BN - 1) / C::BN;
+  const int64_t ntt = (p.N + C::BM - 1) / C::BM, nvt = (p.cw + C::BN - 1) / C::BN;
   int64_t tt, vt;
   dz_tile((int64_t)blockIdx.x, ntt, nvt, tt, vt);
-  const int64_t m0 = tt * C::BM, n0 = vt * C::BN;
+  const int64_t m0 = tt * C::BM, n0 = vt * C::BN;  // n0: column inside the chunk
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
   const Operand A{p.h, p.ldh, p.N, p.H};
-  const Operand B{p.W, p.ldw, p.V, p.H};
+  const Operand B{p.W + p.v0 * p.ldw, p.ldw, p.cw, p.H};
   // This tile's per-token constants, read before the main loop so that their latency is
   // hidden behind it: m, log S, the upstream gradient (NaN when the target is out of range,
   // which makes the whole row NaN) and the target's column inside the tile (-1 when it lies
@@ -227,7 +236,8 @@ __global__ __launch_bounds__(C::NT) void lin_dz_kernel(LinArgs p) {
     const int64_t t = p.t[n];
     const float m = p.stats[2 * n], ls = p.stats[2 * n + 1], gv = p.g[n * p.g_stride];
     const bool ignored = t == p.ignore_index, bad = !ignored && (t < 0 || t >= p.V);
-    const int32_t tc = ignored ? -2 : (t >= n0 && t < n0 + C::BN ? (int32_t)(t - n0) : -1);
+    const int64_t c0 = p.v0 + n0;
+    const int32_t tc = ignored ? -2 : (t >= c0 && t < c0 + C::BN ? (int32_t)(t - c0) : -1);
     rowc = (f32x4){m, ls, bad ? __builtin_nanf("") : gv, __int_as_float(tc)};
   }
   Acc<C> acc;
@@ -236,8 +246,9 @@ __global__ __launch_bounds__(C::NT) void lin_dz_kernel(LinArgs p) {
   if (threadIdx.x < C::BM) cst[threadIdx.x] = rowc;
   __syncthreads();
   // dz = g (1[v = t] - p) = fma(-g, p, g 1[v = t]); interior tiles store without guards.
-  const bool interior = m0 + C::BM <= p.N && n0 + C::BN <= p.V;
-  uint16_t* tile = p.dz + m0 * p.ldz + n0;
+  const bool interior = m0 + C::BM <= p.N && n0 + C::BN <= p.cw;
+  uint16_t* th = p.dzh + m0 * p.ldc + n0;
+  uint16_t* tl = p.dzl + m0 * p.ldc + n0;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -246,40 +257,47 @@ __global__ __launch_bounds__(C::NT) void lin_dz_kernel(LinArgs p) {
       const f32x4 c = cst[r];
       const float m = c.x, ls = c.y, gv = c.z;
       const int32_t tc = __float_as_int(c.w);
-      uint16_t* rowp = tile + (int64_t)r * p.ldz;
+      const int64_t ro = (int64_t)r * p.ldc;
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
         const int lc = wn * C::TN + gemm::acc_col(j, lane);
-        const float pz = expf_fast((acc.c[i][j][v] - m) - ls);
-        float d = __builtin_fmaf(-gv, pz, lc == tc ? gv : 0.0f);
+        const PScaled pz = exp_split((acc.c[i][j][v] - m) - ls);
+        float d = lc == tc ? __builtin_fmaf(-gv, pz.p * pz.f, gv) : (-gv * pz.p) * pz.f;
         d = tc == -2 ? 0.0f : d;
         const bf16x2 hb = __builtin_convertvector((f32x2){d, 0.0f}, bf16x2);
-        const uint16_t bits = (uint16_t)(__builtin_bit_cast(uint32_t, hb) & 0xffffu);
+        const uint32_t hbits = __builtin_bit_cast(uint32_t, hb) & 0xffffu;
+        const float lo = d - __uint_as_float(hbits << 16);  // exact (Sterbenz), 0 for 0 and NaN
+        const bf16x2 lb = __builtin_convertvector((f32x2){lo, 0.0f}, bf16x2);
+        const uint16_t lbits = (uint16_t)(__builtin_bit_cast(uint32_t, lb) & 0xffffu);
         if (interior) {
-          rowp[lc] = bits;
+          th[ro + lc] = (uint16_t)hbits;
+          tl[ro + lc] = lbits;
         } else {
-          // columns [V, ldz) pad the rows with zeros for the dh contraction
+          // columns [cw, ldc) pad the rows with zeros for the dh contraction
           const int64_t col = n0 + lc;
-          if (m0 + r < p.N && col < p.ldz) rowp[lc] = col < p.V ? bits : (uint16_t)0;
+          if (m0 + r < p.N && col < p.ldc) {
+            th[ro + lc] = col < p.cw ? (uint16_t)hbits : (uint16_t)0;
+            tl[ro + lc] = col < p.cw ? lbits : (uint16_t)0;
+          }
         }
       }
     }
 }
 
-// C = A B^T over K with bf16 (RNE) stores; used for dh (A = dz rows, B = W^T via KROW) and
-// dW (A = dz^T via KROW, B = h^T via KROW).
+// C = A B^T over K, A a split (hi, lo) pair; dW rows of a chunk (bf16 stores) and dh of a chunk
+// (stored, or added to the fp32 running sum over the chunks; the last chunk rounds the sum to bf16).
 template <class C>
-__global__ __launch_bounds__(C::NT) void gemm_store_kernel(GemmArgs g) {
+__global__ __launch_bounds__(C::NT) void gemm_pair_kernel(GemmArgs g) {
   extern __shared__ __align__(16) char lds[];
-  const int64_t ntm = (g.M + C::BM - 1) / C::BM, ntn = (g.Nc + C::BN - 1) / C::BN;
+  const int64_t ntn = (g.Nc + C::BN - 1) / C::BN;
   // consecutive blocks share the A tile (on different XCDs they still share it in the MALL)
   const int64_t tm = blockIdx.x / ntn, tn = blockIdx.x - (blockIdx.x / ntn) * ntn;
-  (void)ntm;
   const int64_t m0 = tm * C::BM, n0 = tn * C::BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
   Acc<C> acc;
   gemm::mainloop<C>(g.A, g.B, m0, n0, g.K, lds, acc);
+  const int mode = g.mode;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -289,8 +307,19 @@ __global__ __launch_bounds__(C::NT) void gemm_store_kernel(GemmArgs g) {
       for (int j = 0; j < C::FN; ++j) {
         const int64_t col = n0 + wn * C::TN + gemm::acc_col(j, lane);
         if (r < g.M && col < g.Nc) {
-          const bf16x2 hb = __builtin_convertvector((f32x2){acc.c[i][j][v], 0.0f}, bf16x2);
-          g.C[r * g.ldc + col] = (uint16_t)(__builtin_bit_cast(uint32_t, hb) & 0xffffu);
+          float x = acc.c[i][j][v];
+          const int64_t o = r * g.ldc + col;
+          if (mode == kDhFirst) {
+            g.acc[o] = x;
+            continue;
+          }
+          if (mode != kDhStore) x = g.acc[o] + x;  // the running sum first: chunk order
+          if (mode == kDhAdd) {
+            g.acc[o] = x;
+            continue;
+          }
+          const bf16x2 hb = __builtin_convertvector((f32x2){x, 0.0f}, bf16x2);
+          g.C[o] = (uint16_t)(__builtin_bit_cast(uint32_t, hb) & 0xffffu);
         }
       }
     }
@@ -348,24 +377,51 @@ hipError_t launch_lin_fwd(LinArgs p, int split_hint, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_lin_bwd(LinArgs p, uint16_t* dh, uint16_t* dW, hipStream_t stream) {
-  const int64_t ntt = (p.N + CfgNT::BM - 1) / CfgNT::BM, nvt = (p.V + CfgNT::BN - 1) / CfgNT::BN;
-  hipLaunchKernelGGL((lin_dz_kernel<CfgNT>), dim3((uint32_t)(ntt * nvt)), dim3(CfgNT::NT), lds_bytes<CfgNT>(), stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (dh) {
-    // dh[n, k] = sum_v dz[n, v] W[v, k]: A = dz (ROWK, reduction v), B(k, v) = W[v, k] (KROW)
-    GemmArgs g{Operand{p.dz, p.ldz, p.N, p.ldz}, Operand{p.W, p.ldw, p.H, p.V}, dh, p.H, p.N, p.H, p.ldz};
-    const int64_t blocks = ((p.N + CfgNN::BM - 1) / CfgNN::BM) * ((p.H + CfgNN::BN - 1) / CfgNN::BN);
-    hipLaunchKernelGGL((gemm_store_kernel<CfgNN>), dim3((uint32_t)blocks), dim3(CfgNN::NT), lds_bytes<CfgNN>(), stream, g);
+// Vocabulary tiles per backward chunk: 32 (8192 columns) unless split_hint >= 1 asks for that
+// many chunks. The chunking depends on V alone, so dh is batch invariant.
+int32_t lin_bwd_tiles_per_chunk(int64_t V, int split_hint) {
+  const int64_t nvt = (V + CfgNT::BN - 1) / CfgNT::BN;
+  int64_t tpc = 32;
+  if (split_hint >= 1) tpc = (nvt + split_hint - 1) / split_hint;
+  tpc = tpc < 1 ? 1 : (tpc > nvt ? nvt : tpc);
+  return (int32_t)tpc;
+}
+
+hipError_t launch_lin_bwd(LinArgs p, int split_hint, uint16_t* dh, uint16_t* dW, hipStream_t stream) {
+  const int64_t C = (int64_t)lin_bwd_tiles_per_chunk(p.V, split_hint) * CfgNT::BN;
+  const int64_t nchunks = (p.V + C - 1) / C;
+  const int64_t ntt = (p.N + CfgNT::BM - 1) / CfgNT::BM, nht = (p.H + CfgNN2::BN - 1) / CfgNN2::BN;
+  hipError_t e;
+  for (int64_t c = 0; c < nchunks; ++c) {
+    p.v0 = c * C;
+    p.cw = p.V - p.v0 < C ? p.V - p.v0 : C;
+    const int64_t nvt = (p.cw + CfgNT::BN - 1) / CfgNT::BN;
+    const int64_t kz = (p.cw + 7) / 8 * 8;  // reduction length of dh: the zero-padded chunk width
+    hipLaunchKernelGGL((lin_dz_kernel<CfgNT>), dim3((uint32_t)(ntt * nvt)), dim3(CfgNT::NT), lds_bytes<CfgNT>(),
+                       stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  if (dW) {
-    // dW[v, k] = sum_n dz[n, v] h[n, k]: A(v, n) = dz[n, v] (KROW), B(k, n) = h[n, k] (KROW)
-    GemmArgs g{Operand{p.dz, p.ldz, p.ldz, p.N}, Operand{p.h, p.ldh, p.H, p.N}, dW, p.ldw_out, p.V, p.H, p.N};
-    const int64_t blocks = ((p.V + CfgTN::BM - 1) / CfgTN::BM) * ((p.H + CfgTN::BN - 1) / CfgTN::BN);
-    hipLaunchKernelGGL((gemm_store_kernel<CfgTN>), dim3((uint32_t)blocks), dim3(CfgTN::NT), lds_bytes<CfgTN>(), stream, g);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t plane = p.dzl - p.dzh;
+    if (dW) {
+      // dW[v0 + v, k] = sum_n dz[n, v] h[n, k]: A(v, n) = dz[n, v] (KROW pair; its rows are the
+      // zero-padded width kz, so that every 8-row load stays inside the planes), B(k, n) = h[n, k] (KROW)
+      GemmArgs g{Operand{p.dzh, p.ldc, kz, p.N, plane}, Operand{p.h, p.ldh, p.H, p.N}, dW + p.v0 * p.H, nullptr,
+                 p.H, p.cw, p.H, p.N, kDhStore};
+      const int64_t blocks = nvt * nht;
+      hipLaunchKernelGGL((gemm_pair_kernel<CfgTN2>), dim3((uint32_t)blocks), dim3(CfgTN2::NT), lds_bytes<CfgTN2>(),
+                         stream, g);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (dh) {
+      // dh[n, k] += sum_v dz[n, v] W[v0 + v, k]: A = dz (ROWK pair), B(k, v) = W[v0 + v, k] (KROW)
+      const int32_t mode = nchunks == 1 ? kDhStore : (c == 0 ? kDhFirst : (c + 1 < nchunks ? kDhAdd : kDhLast));
+      GemmArgs g{Operand{p.dzh, p.ldc, p.N, kz, plane}, Operand{p.W + p.v0 * p.ldw, p.ldw, p.H, p.cw}, dh, p.dh_acc,
+                 p.H, p.N, p.H, kz, mode};
+      if (mode == kDhFirst || mode == kDhAdd) g.ldc = p.H;
+      const int64_t blocks = ntt * nht;
+      hipLaunchKernelGGL((gemm_pair_kernel<CfgNN2>), dim3((uint32_t)blocks), dim3(CfgNN2::NT), lds_bytes<CfgNN2>(),
+                         stream, g);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }

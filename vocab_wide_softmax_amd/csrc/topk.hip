@@ -98,8 +98,9 @@ __device__ __forceinline__ void topk_groups(const float (&x)[UB][8], char* oa, i
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float pj = expf_fast((x[u][j] - m) - ls);
-      y[j] = zero_row ? 0.0f : (nan_row ? qnan : __builtin_fmaf(-Gs, pj, h[j]));
+      const PScaled pj = exp_split((x[u][j] - m) - ls);
+      const float d = __builtin_fmaf(-Gs * pj.p, pj.f, h[j]);
+      y[j] = zero_row ? 0.0f : (nan_row ? qnan : d);
     }
     if (FULL) store_group_vec<DT>(oa, g, y);
     else store_group<DT, true>(oa, g, V, g_full, y);
@@ -275,8 +276,9 @@ __device__ __forceinline__ void topk_small_tile(const TopkArgs& p, int64_t row, 
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float pj = expf_fast((x[u][j] - m) - ls);
-      y[j] = zero_row ? 0.0f : (nan_row ? qnan : __builtin_fmaf(-Gs, pj, hu[j]));
+      const PScaled pj = exp_split((x[u][j] - m) - ls);
+      const float d = __builtin_fmaf(-Gs * pj.p, pj.f, hu[j]);
+      y[j] = zero_row ? 0.0f : (nan_row ? qnan : d);
     }
     if constexpr (FULL) store_group_vec<DT>(oa, gu, y);
     else store_group<DT, true>(oa, gu, V, g_full, y);
