@@ -771,6 +771,74 @@ def counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
         f.write("\n")
 
 
+def _raw_counter_sums(d):
+    """{kernel: {counter: mean per dispatch}} from a rocprofv3 counter_collection.csv holding
+    several raw counters (instances summed per dispatch)."""
+    path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+    acc = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            k = acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], {})
+            k[r["Dispatch_Id"]] = k.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return {kern: {c: sum(v.values()) / len(v) for c, v in cs.items()} for kern, cs in acc.items()}
+
+
+def _read_bytes(c):
+    """Read bytes from the request counts by size: 32-, 64- and 128-byte requests."""
+    rd, r32, r128 = c.get("TCC_EA0_RDREQ", 0.0), c.get("TCC_EA0_RDREQ_32B", 0.0), c.get("TCC_EA0_RDREQ_128B", 0.0)
+    return r32 * 32 + r128 * 128 + (rd - r32 - r128) * 64
+
+
+def _fetch_size_formula_bytes(c):
+    """The stock FETCH_SIZE expression (in bytes): 128-byte requests counted through TCC_BUBBLE."""
+    rd, r32, bub = c.get("TCC_EA0_RDREQ", 0.0), c.get("TCC_EA0_RDREQ_32B", 0.0), c.get("TCC_BUBBLE", 0.0)
+    return bub * 128 + (rd - bub - r32) * 64 + r32 * 32
+
+
+def _write_bytes(c):
+    wr, w64 = c.get("TCC_EA0_WRREQ", 0.0), c.get("TCC_EA0_WRREQ_64B", 0.0)
+    return (wr - w64) * 32 + w64 * 64
+
+
+def counters_raw(rd_dir, wr_dir, cal_rd_dir, cal_wr_dir):
+    """HBM bytes per kernel from the L2-to-memory request counts by request size (no fitted factor):
+    reads = 32 B x RDREQ_32B + 128 B x RDREQ_128B + 64 B x the rest of RDREQ, writes =
+    32 B x (WRREQ - WRREQ_64B) + 64 B x WRREQ_64B. The plain device copy of T bytes each way checks
+    the derivation against known traffic; the stock FETCH_SIZE expression, which counts 128-byte
+    requests through TCC_BUBBLE, is shown beside it. Writes the dominant kernel's bytes per launch
+    to profiles/kl_bwd_pair8192_counters.json."""
+    rd, wr, crd, cwr = (_raw_counter_sums(x) for x in (rd_dir, wr_dir, cal_rd_dir, cal_wr_dir))
+    copy = [k for k in crd if "copyBuffer" in k or "copy" in k.lower()][0]
+    cr, cw = _read_bytes(crd[copy]), _write_bytes(cwr[copy])
+    print("Calibration copy (%d bytes each way): request-size reads %.0f bytes (ratio %.5f), writes %.0f bytes "
+          "(ratio %.5f); the stock FETCH_SIZE expression gives %.0f bytes (ratio %.5f): RDREQ %.0f, 32B %.0f, "
+          "128B %.0f, BUBBLE %.0f." % (T_BYTES, cr, cr / T_BYTES, cw, cw / T_BYTES, _fetch_size_formula_bytes(crd[copy]),
+                                      _fetch_size_formula_bytes(crd[copy]) / T_BYTES, crd[copy].get("TCC_EA0_RDREQ", 0),
+                                      crd[copy].get("TCC_EA0_RDREQ_32B", 0), crd[copy].get("TCC_EA0_RDREQ_128B", 0),
+                                      crd[copy].get("TCC_BUBBLE", 0)))
+    print()
+    print("| kernel | RDREQ | RDREQ_32B | RDREQ_128B | BUBBLE | WRREQ | WRREQ_64B | read bytes | write bytes | "
+          "total / T | FETCH_SIZE expression bytes |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    dom = None
+    for k in sorted(rd):
+        c, w = rd[k], wr.get(k, {})
+        rb, wb = _read_bytes(c), _write_bytes(w)
+        print("| %s | %.0f | %.0f | %.0f | %.0f | %.0f | %.0f | %.0f | %.0f | %.4f | %.0f |" % (
+            k, c.get("TCC_EA0_RDREQ", 0), c.get("TCC_EA0_RDREQ_32B", 0), c.get("TCC_EA0_RDREQ_128B", 0),
+            c.get("TCC_BUBBLE", 0), w.get("TCC_EA0_WRREQ", 0), w.get("TCC_EA0_WRREQ_64B", 0), rb, wb,
+            (rb + wb) / T_BYTES, _fetch_size_formula_bytes(c)))
+        if k.startswith("void vws::bwd_kernel<2, 1, true"):
+            dom = rb + wb
+    out = {"kernel": "bwd_kernel<KL,bf16,vec> on the 8192x75968 bf16 pair", "hbm_bytes_per_launch": round(dom),
+           "method": "L2-to-memory request counts by size (TCC_EA0_RDREQ, _32B, _128B; TCC_EA0_WRREQ, _64B), "
+                     "no fitted factor", "calibration_copy_ratio": {"read": cr / T_BYTES, "write": cw / T_BYTES},
+           "kernel_source_hash": kernel_source_hash(), "sources": KERNEL_SOURCES}
+    with open(os.path.join(PROFILE_DIR, "kl_bwd_pair8192_counters.json"), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+
+
 # --------------------------------------------------------------------------------- main
 
 def main():
@@ -791,6 +859,9 @@ def main():
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--summarize", nargs=2, metavar=("DIR", "MODE"))
     ap.add_argument("--counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"))
+    ap.add_argument("--counters-raw", nargs=4, metavar=("RD_DIR", "WR_DIR", "CAL_RD_DIR", "CAL_WR_DIR"),
+                    help="HBM bytes from request counts by size (TCC_EA0_RDREQ/_32B/_128B, TCC_BUBBLE; "
+                         "TCC_EA0_WRREQ/_64B)")
     args = ap.parse_args()
 
     if args.summarize:
@@ -798,6 +869,9 @@ def main():
         return
     if args.counters:
         counters(*args.counters)
+        return
+    if args.counters_raw:
+        counters_raw(*args.counters_raw)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only; --gpus %d is not supported (rows would shard across GPUs with "
