@@ -256,3 +256,22 @@ def test_linear_strided_rows_broadcast_g_and_partial_stage(device):
                              "bf16"), "strided dh")
     _assert_ok(compare.check(f64(dW), OL.linear_logp_bwd_dw(hh, hw, ht, hg), OL.cond_linear_dw(hh, hw, ht, hg),
                              "bf16"), "strided dW")
+
+
+@pytest.mark.slow
+def test_linear_xcd_patch_orders_all_elements(device):
+    """Hidden width 4096 (16 hidden tiles) with 17 token tiles and 17 vocabulary tiles: the dh and
+    dW contractions map their first 16 x 16 tiles through the XCD patch order and the last row of
+    tiles in row-major order; a tile visited twice or never would leave a wrong dh or dW element."""
+    wl = W.linear_logp(n=4352, hidden=4096, v=4200, seed=23, w_std=0.02)
+    wl.t[::89] = -100
+    logp, stats, dh, dW = _run(wl.h, wl.W, wl.t, wl.g, device)
+    hh, hw, ht, hg = f64(wl.h), f64(wl.W), wl.t.numpy(), wl.g.double().numpy()
+    lp, m, ls = OL.linear_logp_fwd(hh, hw, ht)
+    _assert_ok(compare.check(f64(logp), lp, OL.cond_linear_fwd(hh, hw, ht), "f32"), "patch logp")
+    for r0 in range(0, hh.shape[0], 1088):
+        rows = np.arange(r0, min(r0 + 1088, hh.shape[0]))
+        _assert_ok(compare.check(f64(dh[r0:rows[-1] + 1]), OL.linear_logp_bwd_dh(hh, hw, ht, hg, rows=rows),
+                                 OL.cond_linear_dh(hh, hw, ht, hg, rows=rows), "bf16"), "patch dh %d" % r0)
+    dw_ref, dw_c = OL.linear_logp_bwd_dw_cond(hh, hw, ht, hg)
+    _assert_ok(compare.check(f64(dW), dw_ref, dw_c, "bf16"), "patch dW")

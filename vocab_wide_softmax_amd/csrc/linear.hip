@@ -284,14 +284,39 @@ __global__ __launch_bounds__(C::NT) void lin_dz_kernel(LinArgs p) {
     }
 }
 
+// Block -> (M tile, N tile) of a contraction with a long reduction (K = 8192 for dh and dW).
+// Block b runs on XCD b % 8, and an XCD runs 32 blocks at a time; those form a patch of 4 M tiles
+// x 8 N tiles, so per k-step its L2 takes 4 A and 8 B tile slices for 32 tiles (row-major order
+// gave an XCD 16 M tiles x 2 N tiles: 18 slices, an L2 hit rate of 61-64%). The 8 XCDs' patches
+// cover a super-tile of (32 / ntn) 4 M tiles x ntn N tiles (ntn in {8, 16, 32, 64}), super-tiles
+// go along M; other shapes and the M tiles past the last whole super-tile run in row-major order.
+__device__ __forceinline__ void pair_tile(int64_t b, int64_t ntm, int64_t ntn, int64_t& tm, int64_t& tn) {
+  if (ntn == 8 || ntn == 16 || ntn == 32 || ntn == 64) {
+    const int64_t ng = ntn / 8, mg = 8 / ng, sm = mg * 4;  // XCD groups along N and M; super-tile rows
+    const int64_t nfull = (ntm / sm) * sm * ntn;
+    if (b < nfull) {
+      const int64_t x = b % 8, q = b / 8, st = q / 32, w = q % 32;
+      tm = st * sm + (x % mg) * 4 + w % 4;
+      tn = (x / mg) * 8 + w / 4;
+      return;
+    }
+    const int64_t r = b - nfull;
+    tm = ntm / sm * sm + r / ntn;
+    tn = r % ntn;
+    return;
+  }
+  tm = b / ntn;
+  tn = b - tm * ntn;
+}
+
 // C = A B^T over K, A a split (hi, lo) pair; dW rows of a chunk (bf16 stores) and dh of a chunk
 // (stored, or added to the fp32 running sum over the chunks; the last chunk rounds the sum to bf16).
 template <class C>
 __global__ __launch_bounds__(C::NT) void gemm_pair_kernel(GemmArgs g) {
   extern __shared__ __align__(16) char lds[];
-  const int64_t ntn = (g.Nc + C::BN - 1) / C::BN;
-  // consecutive blocks share the A tile (on different XCDs they still share it in the MALL)
-  const int64_t tm = blockIdx.x / ntn, tn = blockIdx.x - (blockIdx.x / ntn) * ntn;
+  const int64_t ntm = (g.M + C::BM - 1) / C::BM, ntn = (g.Nc + C::BN - 1) / C::BN;
+  int64_t tm, tn;
+  pair_tile((int64_t)blockIdx.x, ntm, ntn, tm, tn);
   const int64_t m0 = tm * C::BM, n0 = tn * C::BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
