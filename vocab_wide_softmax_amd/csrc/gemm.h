@@ -148,11 +148,19 @@ __device__ __forceinline__ bool stage_span_fits(const Operand& op) {
   return (int64_t)(L == ROWK ? R : BK) * op.ld * 2 <= (int64_t)0xFFFFFFFF;
 }
 
+// The base and size are the same in every lane; passing them through readfirstlane lets the
+// compiler see that, so the descriptor stays in scalar registers. Without it the compiler may
+// keep the base in vector registers and wrap every load in a loop over the distinct descriptors
+// of the wave (four lane reads, two compares and an exec-mask loop per load).
 template <int L, int R, int BK>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t stage_rsrc(const Operand& op, int64_t r0, int64_t k0) {
   const uint16_t* base = L == ROWK ? op.base + r0 * op.ld + k0 : op.base + k0 * op.ld + r0;
-  const int64_t span = (int64_t)(L == ROWK ? R : BK) * op.ld * 2;
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(uint32_t)span, 0x00020000);
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t span = __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)(L == ROWK ? R : BK) * op.ld * 2));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, (int)span,
+                                           0x00020000);
 }
 
 template <int L, int R, int BK, int NW, int NINSTR, int J0 = 0, int J1 = NINSTR>
