@@ -91,7 +91,7 @@ __global__ __launch_bounds__(C::NT) void lin_fwd_kernel(LinArgs p) {
   Acc<C> acc;
   for (int64_t vt = vt0; vt < vt1; ++vt) {
     const int64_t m0 = vt * C::BM;
-    gemm::mainloop<C>(A, B, m0, n0, p.H, lds, acc);
+    gemm::mainloop_pp<C>(A, B, m0, n0, p.H, lds, acc);  // ping-pong: 3% faster here, not for dz
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
       float bm = -kInf;
