@@ -454,23 +454,23 @@ __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int
   else mainloop_t<C, true, false>(A, B, m0, n0, K, lds, acc);
 }
 
-// Ping-pong schedule of the same product for interior tiles on the buffer path (8 waves, 2
-// stages, whole half-stages of slices). Waves 0-3 and 4-7 form two groups with one wave of each
-// on every SIMD (waves go to SIMDs in turn). Every wave runs the same loop over half-stages:
-// read the half's fragments (and issue or await its share of a stage refill), barrier, multiply
-// the half from registers, barrier. Group 1 passes one extra barrier before the loop and group 0
-// one after it, so the groups run one phase apart: while one group multiplies, the other reads
-// and waits, on every SIMD one wave feeds the MFMA pipe while the other waits on memory, and the
-// waits of a SIMD's two waves no longer coincide. Counting phases from the first read of group 0
-// (phase -1), group g reads half k in phase 2k - 1 + g and multiplies it in phase 2k + g; it
-// issues its loads of stage s + 1 while reading half 2s (phase 4s - 1 + g), after the last read of
-// stage s - 1, whose buffer they fill (phase 4s - 2), and awaits them while reading half 2s + 1
-// (phase 4s + 1 + g), before the first read of stage s + 1 (phase 4s + 3). Every accumulator sees
+// Ping-pong schedule of the same product for interior tiles on the buffer path (8 waves, whole
+// half-stages of slices). Waves 0-3 and 4-7 form two groups with one wave of each on every SIMD
+// (waves go to SIMDs in turn). Every wave runs the same loop over half-stages: read the half's
+// fragments (and issue or await its share of a stage refill), barrier, multiply the half from
+// registers, barrier. Group 1 passes one extra barrier before the loop and group 0 one after it,
+// so the groups run one phase apart: while one group multiplies, the other reads and waits, on
+// every SIMD one wave feeds the MFMA pipe while the other waits on memory, and the waits of a
+// SIMD's two waves no longer coincide. Counting phases from the first read of group 0 (phase
+// -1), group g reads half k in phase 2k - 1 + g and multiplies it in phase 2k + g. While reading
+// half 2s it issues its loads of stage s + NSTAGE - 1 (phase 4s - 1 + g), after the last read of
+// stage s - 1, whose buffer they fill (phase 4s - 2); while reading half 2s + 1 it awaits stage
+// s + 1 (phase 4s + 1 + g), before that stage's first read (phase 4s + 3). Every accumulator sees
 // the same MFMA sequence as in mainloop_t, so the results are the same bits.
 template <class C>
 __device__ __forceinline__ void mainloop_pp_t(const Operand& A, const Operand& B, int64_t m0, int64_t n0, int64_t K,
                                               char* lds, Acc<C>& acc) {
-  static_assert(C::NW == 8 && C::NSTAGE == 2 && (C::BK / 16) % 2 == 0, "ping-pong layout");
+  static_assert(C::NW == 8 && (C::NSTAGE == 2 || C::NSTAGE == 3) && (C::BK / 16) % 2 == 0, "ping-pong layout");
   constexpr int HQ = C::BK / 32;  // slices per half-stage
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -484,26 +484,29 @@ __device__ __forceinline__ void mainloop_pp_t(const Operand& A, const Operand& B
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  issue_buf_range<C, 0, C::LOADS_PER_STAGE>(A, B, m0, n0, 0, lds, wave, lane);
-  if (nk > 1) {
-    issue_buf_range<C, 0, C::LOADS_PER_STAGE>(A, B, m0, n0, 1, lds, wave, lane);
-    wait_vm<C::LOADS_PER_STAGE>();
-  } else {
-    wait_vm<0>();
-  }
+#pragma unroll
+  for (int s = 0; s < C::NSTAGE; ++s)
+    if (s < nk) issue_buf_range<C, 0, C::LOADS_PER_STAGE>(A, B, m0, n0, s, lds, wave, lane);
+  // stage 0 landed: the stages issued after it may stay in flight (loads complete in order)
+  if (C::NSTAGE == 3 && nk > 2) wait_vm<2 * C::LOADS_PER_STAGE>();
+  else if (nk > 1) wait_vm<C::LOADS_PER_STAGE>();
+  else wait_vm<0>();
   barrier();
   if (second) barrier();
   Frags<C> F[HQ];
+  int buf = 0;  // s mod NSTAGE
   for (int s = 0; s < nk; ++s) {
-    const char* sa = lds + (s & 1) * C::STAGE_BYTES;
+    const char* sa = lds + buf * C::STAGE_BYTES;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
       for (int h = 0; h < HQ; ++h) read_frags<C>(F[h], sa, sa + C::A_BYTES, wm, wn, (half * HQ + h) * 16, lane);
       if (half == 0) {
-        if (s >= 1 && s + 1 < nk) issue_buf_range<C, 0, C::LOADS_PER_STAGE>(A, B, m0, n0, s + 1, lds, wave, lane);
-      } else {
-        if (s + 1 < nk) wait_vm<0>();
+        const int st = s + C::NSTAGE - 1;
+        if (s >= 1 && st < nk) issue_buf_range<C, 0, C::LOADS_PER_STAGE>(A, B, m0, n0, st, lds, wave, lane);
+      } else if (s + 1 < nk) {
+        if (C::NSTAGE == 3 && s + 2 < nk) wait_vm<C::LOADS_PER_STAGE>();  // stage s + 2 stays in flight
+        else wait_vm<0>();
       }
 #pragma unroll
       for (int h = 0; h < HQ; ++h) settle<C>(F[h]);
@@ -512,6 +515,7 @@ __device__ __forceinline__ void mainloop_pp_t(const Operand& A, const Operand& B
       for (int h = 0; h < HQ; ++h) mfmas<C>(acc, F[h]);
       barrier();
     }
+    buf = buf + 1 == C::NSTAGE ? 0 : buf + 1;
   }
   if (!second) barrier();
   __syncthreads();

@@ -38,7 +38,8 @@ typedef Cfg<256, 256, 64, 2, 4, ROWK, ROWK, 2, 1, 1> CfgNT;   // dz
 typedef Cfg<256, 256, 64, 2, 4, ROWK, ROWK, 2, 1, 2> CfgFwd;  // forward
 // dh = dz W and dW = dz^T h with dz a bf16 (hi, lo) pair: 3 stages of BK = 32 (48 KB each), wave
 // tiles of 64 x 128 so that a k-slice reads 2 + 2 A fragments and 4 B fragments for 16 MFMAs
-// (128 x 64 wave tiles: 7-13% slower), each stage's refill in one burst.
+// (128 x 64 wave tiles: 7-13% slower), run by the ping-pong main loop (a phase is one slice;
+// 5% faster than the shared loop, whose refill went out in one burst).
 typedef Cfg<256, 256, 32, 4, 2, ROWK, KROW, 3, 2, 1> CfgNN2;  // dh = dz W
 typedef Cfg<256, 256, 32, 4, 2, KROW, KROW, 3, 2, 1> CfgTN2;  // dW = dz^T h
 
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(C::NT) void gemm_pair_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
   Acc<C> acc;
-  gemm::mainloop<C>(g.A, g.B, m0, n0, g.K, lds, acc);
+  gemm::mainloop_pp<C>(g.A, g.B, m0, n0, g.K, lds, acc);
   const int mode = g.mode;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
