@@ -51,7 +51,7 @@ template <int BM_, int BN_, int BK_, int WM_, int WN_, int LA_, int LB_, int NST
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, LA = LA_, LB = LB_, NSTAGE = NSTAGE_;
   static constexpr int SA = SA_;  // planes of A: 1, or 2 for a bf16 (hi, lo) pair
-  static constexpr int PIECES = PIECES_;  // buffer-path refill pieces per stage (see mainloop_t)
+  static constexpr int PIECES = PIECES_;  // buffer-path refill pieces per stage (mainloop_t, mainloop_pp_t)
   static constexpr int NW = WM * WN, NT = NW * 64;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
@@ -465,8 +465,11 @@ __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int
 // -1), group g reads half k in phase 2k - 1 + g and multiplies it in phase 2k + g. While reading
 // half 2s it issues its loads of stage s + NSTAGE - 1 (phase 4s - 1 + g), after the last read of
 // stage s - 1, whose buffer they fill (phase 4s - 2); while reading half 2s + 1 it awaits stage
-// s + 1 (phase 4s + 1 + g), before that stage's first read (phase 4s + 3). Every accumulator sees
-// the same MFMA sequence as in mainloop_t, so the results are the same bits.
+// s + 1 (phase 4s + 1 + g), before that stage's first read (phase 4s + 3). With three stages and
+// Cfg::PIECES = 2 the refill goes out in two pieces, the second while reading half 2s + 1, which
+// spreads the loads of a stage over both read phases (they queue on the CU's load path when
+// issued at once). Every accumulator sees the same MFMA sequence as in mainloop_t, so the results
+// are the same bits.
 template <class C>
 __device__ __forceinline__ void mainloop_pp_t(const Operand& A, const Operand& B, int64_t m0, int64_t n0, int64_t K,
                                               char* lds, Acc<C>& acc) {
@@ -501,12 +504,17 @@ __device__ __forceinline__ void mainloop_pp_t(const Operand& A, const Operand& B
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
       for (int h = 0; h < HQ; ++h) read_frags<C>(F[h], sa, sa + C::A_BYTES, wm, wn, (half * HQ + h) * 16, lane);
+      constexpr bool SPLIT = C::NSTAGE == 3 && C::PIECES == 2;
+      constexpr int L0 = SPLIT ? C::LOADS_PER_STAGE / 2 : C::LOADS_PER_STAGE;
+      const int st = s + C::NSTAGE - 1;
       if (half == 0) {
-        const int st = s + C::NSTAGE - 1;
-        if (s >= 1 && st < nk) issue_buf_range<C, 0, C::LOADS_PER_STAGE>(A, B, m0, n0, st, lds, wave, lane);
-      } else if (s + 1 < nk) {
-        if (C::NSTAGE == 3 && s + 2 < nk) wait_vm<C::LOADS_PER_STAGE>();  // stage s + 2 stays in flight
-        else wait_vm<0>();
+        if (s >= 1 && st < nk) issue_buf_range<C, 0, L0>(A, B, m0, n0, st, lds, wave, lane);
+      } else {
+        if (SPLIT && s >= 1 && st < nk) issue_buf_range<C, L0, C::LOADS_PER_STAGE>(A, B, m0, n0, st, lds, wave, lane);
+        if (s + 1 < nk) {
+          if (C::NSTAGE == 3 && s + 2 < nk) wait_vm<C::LOADS_PER_STAGE>();  // stage s + 2 stays in flight
+          else wait_vm<0>();
+        }
       }
 #pragma unroll
       for (int h = 0; h < HQ; ++h) settle<C>(F[h]);

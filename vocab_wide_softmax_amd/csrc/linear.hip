@@ -38,10 +38,10 @@ typedef Cfg<256, 256, 64, 2, 4, ROWK, ROWK, 2, 1, 1> CfgNT;   // dz
 typedef Cfg<256, 256, 64, 2, 4, ROWK, ROWK, 2, 1, 2> CfgFwd;  // forward
 // dh = dz W and dW = dz^T h with dz a bf16 (hi, lo) pair: 3 stages of BK = 32 (48 KB each), wave
 // tiles of 64 x 128 so that a k-slice reads 2 + 2 A fragments and 4 B fragments for 16 MFMAs
-// (128 x 64 wave tiles: 7-13% slower), run by the ping-pong main loop (a phase is one slice;
-// 5% faster than the shared loop, whose refill went out in one burst).
-typedef Cfg<256, 256, 32, 4, 2, ROWK, KROW, 3, 2, 1> CfgNN2;  // dh = dz W
-typedef Cfg<256, 256, 32, 4, 2, KROW, KROW, 3, 2, 1> CfgTN2;  // dW = dz^T h
+// (128 x 64 wave tiles: 7-13% slower), run by the ping-pong main loop (a phase is one slice),
+// each refill in two pieces, one per half-stage read: 8% faster than the shared loop.
+typedef Cfg<256, 256, 32, 4, 2, ROWK, KROW, 3, 2, 2> CfgNN2;  // dh = dz W
+typedef Cfg<256, 256, 32, 4, 2, KROW, KROW, 3, 2, 2> CfgTN2;  // dW = dz^T h
 
 namespace gemm {
 __device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
