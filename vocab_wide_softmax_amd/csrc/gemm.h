@@ -454,6 +454,15 @@ __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int
   else mainloop_t<C, true, false>(A, B, m0, n0, K, lds, acc);
 }
 
+// Wait until at most n whole stages of this wave's refill loads (n < NSTAGE) are outstanding.
+template <class C>
+__device__ __forceinline__ void wait_stages(int n) {
+  if (C::NSTAGE > 3 && n >= 3) wait_vm<3 * C::LOADS_PER_STAGE>();
+  else if (C::NSTAGE > 2 && n == 2) wait_vm<2 * C::LOADS_PER_STAGE>();
+  else if (n == 1) wait_vm<C::LOADS_PER_STAGE>();
+  else wait_vm<0>();
+}
+
 // Ping-pong schedule of the same product for interior tiles on the buffer path (8 waves, whole
 // half-stages of slices). Waves 0-3 and 4-7 form two groups with one wave of each on every SIMD
 // (waves go to SIMDs in turn). Every wave runs the same loop over half-stages: read the half's
@@ -473,7 +482,7 @@ __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int
 template <class C>
 __device__ __forceinline__ void mainloop_pp_t(const Operand& A, const Operand& B, int64_t m0, int64_t n0, int64_t K,
                                               char* lds, Acc<C>& acc) {
-  static_assert(C::NW == 8 && (C::NSTAGE == 2 || C::NSTAGE == 3) && (C::BK / 16) % 2 == 0, "ping-pong layout");
+  static_assert(C::NW == 8 && C::NSTAGE >= 2 && C::NSTAGE <= 4 && (C::BK / 16) % 2 == 0, "ping-pong layout");
   constexpr int HQ = C::BK / 32;  // slices per half-stage
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -491,9 +500,7 @@ __device__ __forceinline__ void mainloop_pp_t(const Operand& A, const Operand& B
   for (int s = 0; s < C::NSTAGE; ++s)
     if (s < nk) issue_buf_range<C, 0, C::LOADS_PER_STAGE>(A, B, m0, n0, s, lds, wave, lane);
   // stage 0 landed: the stages issued after it may stay in flight (loads complete in order)
-  if (C::NSTAGE == 3 && nk > 2) wait_vm<2 * C::LOADS_PER_STAGE>();
-  else if (nk > 1) wait_vm<C::LOADS_PER_STAGE>();
-  else wait_vm<0>();
+  wait_stages<C>(min(C::NSTAGE - 1, nk - 1));
   barrier();
   if (second) barrier();
   Frags<C> F[HQ];
@@ -504,17 +511,15 @@ __device__ __forceinline__ void mainloop_pp_t(const Operand& A, const Operand& B
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
       for (int h = 0; h < HQ; ++h) read_frags<C>(F[h], sa, sa + C::A_BYTES, wm, wn, (half * HQ + h) * 16, lane);
-      constexpr bool SPLIT = C::NSTAGE == 3 && C::PIECES == 2;
+      constexpr bool SPLIT = C::NSTAGE >= 3 && C::PIECES == 2;
       constexpr int L0 = SPLIT ? C::LOADS_PER_STAGE / 2 : C::LOADS_PER_STAGE;
       const int st = s + C::NSTAGE - 1;
       if (half == 0) {
         if (s >= 1 && st < nk) issue_buf_range<C, 0, L0>(A, B, m0, n0, st, lds, wave, lane);
       } else {
         if (SPLIT && s >= 1 && st < nk) issue_buf_range<C, L0, C::LOADS_PER_STAGE>(A, B, m0, n0, st, lds, wave, lane);
-        if (s + 1 < nk) {
-          if (C::NSTAGE == 3 && s + 2 < nk) wait_vm<C::LOADS_PER_STAGE>();  // stage s + 2 stays in flight
-          else wait_vm<0>();
-        }
+        // stage s + 1 landed; stages s + 2 .. s + NSTAGE - 1 (those issued) stay in flight
+        if (s + 1 < nk) wait_stages<C>(min(s + C::NSTAGE - 1, nk - 1) - (s + 1));
       }
 #pragma unroll
       for (int h = 0; h < HQ; ++h) settle<C>(F[h]);
