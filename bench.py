@@ -459,6 +459,46 @@ def linear_bench(steps, warmup, device, wl=None):
     }
 
 
+def library_gemm(device, wl=None, reps=5):
+    """Context for the fused linear-logp's roofline, not part of the path: torch's own bf16 GEMM
+    (hipBLASLt) on the products the path computes, at the same shapes and on the same h and W (dz
+    random, N(0, 1e-8)), timed with HIP events on torch's stream: the full logits h W^T, one
+    8192-column chunk of them, and the chunk's dW = dz^T h and dh = dz W_chunk with a single bf16
+    dz (the path contracts a hi + lo pair, twice that work)."""
+    import torch
+
+    from vocab_wide_softmax_amd import workloads as W
+
+    wl = wl or W.linear_logp(LIN_N, LIN_H, LIN_V)
+    h, Wm = wl.h.to(device), wl.W.to(device)
+    n, hidden = h.shape
+    v, c = Wm.shape[0], 8192
+    wc = Wm[:c].contiguous()
+    gen = torch.Generator().manual_seed(11)
+    dz = (torch.randn(n, c, generator=gen) * 1e-4).to(torch.bfloat16).to(device)
+    cases = (("logits_h_Wt_8192x151936x4096", lambda: h @ Wm.t(), 2.0 * n * v * hidden),
+             ("chunk_logits_h_Wct_8192x8192x4096", lambda: h @ wc.t(), 2.0 * n * c * hidden),
+             ("chunk_dW_dzt_h_8192x4096x8192", lambda: dz.t() @ h, 2.0 * c * hidden * n),
+             ("chunk_dh_dz_Wc_8192x4096x8192", lambda: dz @ wc, 2.0 * n * hidden * c))
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name, f, flop in cases:
+        for _ in range(2):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 3), "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1)}
+    del h, Wm, wc, dz
+    torch.cuda.empty_cache()
+    return out
+
+
 def linear_cpu_baseline(wl, rows=512, vocab_rows=512):
     """The fp64 oracle of the fused linear-logp on a sub-batch of `rows` evenly spaced tokens of
     the same workload: logp (forward over the full vocabulary), dh of those tokens, and the rows of
@@ -700,7 +740,8 @@ def summarize(outdir, mode):
     """Condense rocprofv3 output (its SQLite database) in `outdir` into a text table.
 
     mode "stats": calls and average / total duration per kernel;
-    mode "counters": mean value per dispatch of every collected counter, per kernel.
+    mode "counters": mean value per dispatch of every collected counter, per kernel;
+    mode "gemm": clock, MFMA-busy and wait fractions of the MFMA kernels (see _summarize_gemm).
     """
     con = _rocpd(outdir)
     if mode == "stats":
@@ -712,6 +753,9 @@ def summarize(outdir, mode):
         for name, calls, avg, mn, mx, tot in rows:
             print("| %s | %d | %.1f | %.1f | %.1f | %.1f | %.2f |" % (name, calls, avg / 1e3, mn / 1e3, mx / 1e3,
                                                                       tot / 1e3, 100.0 * tot / total))
+        return
+    if mode == "gemm":
+        _summarize_gemm(con)
         return
     rows = con.execute("select * from counters_collection").fetchall()
     cols = [d[0] for d in con.execute("select * from counters_collection limit 1").description]
@@ -727,6 +771,40 @@ def summarize(outdir, mode):
     for (name, ctr), per in sorted(acc.items()):
         vals = list(per.values())
         print("| %s | %s | %d | %.1f |" % (name, ctr, len(vals), sum(vals) / len(vals)))
+
+
+def _summarize_gemm(con, cus=256, xcds=8):
+    """Per MFMA kernel (the linear-logp GEMMs and torch's Cijk GEMMs), from one counter run of
+    GRBM_GUI_ACTIVE, SQ_WAVE_CYCLES, SQ_WAIT_ANY, SQ_WAIT_INST_ANY, SQ_VALU_MFMA_BUSY_CYCLES,
+    SQ_LDS_IDX_ACTIVE, SQ_LDS_BANK_CONFLICT and SQ_BUSY_CYCLES: GRBM_GUI_ACTIVE sums the XCDs, so
+    cycles = value / xcds; clock = cycles / kernel duration; MFMA busy = MFMA busy cycles / (4 cus
+    SIMDs x cycles); waves per SIMD = SQ_WAVE_CYCLES (quad-cycles) x 4 / (4 cus x cycles); wait and
+    issue-wait fractions = SQ_WAIT_ANY and SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES (all quad-cycles);
+    LDS index active = SQ_LDS_IDX_ACTIVE / (cus x cycles)."""
+    rows = con.execute("select dispatch_id, kernel_name, counter_name, sum(value), avg(duration) "
+                       "from counters_collection group by dispatch_id, counter_name").fetchall()
+    per = {}
+    for did, kn, cn, v, dur in rows:
+        e = per.setdefault(did, {"name": kn, "dur": dur})
+        e[cn] = v
+    groups = {}
+    for e in per.values():
+        n = e["name"]
+        if "lin_" in n and ("fwd_kernel" in n or "dz_kernel" in n) or "gemm_pair" in n or "Cijk" in n:
+            groups.setdefault(n, []).append(e)
+    print("| kernel | dispatches | mean us | clock GHz | MFMA busy | waves / SIMD | wait | issue wait "
+          "| LDS index active | LDS bank conflicts / dispatch |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for n, es in sorted(groups.items(), key=lambda kv: -sum(e["dur"] for e in kv[1])):
+        m = {k: sum(e.get(k, 0.0) for e in es) / len(es) for k in es[0] if k != "name"}
+        cyc = m["GRBM_GUI_ACTIVE"] / xcds
+        wc = max(m.get("SQ_WAVE_CYCLES", 0.0), 1.0)
+        label = n if len(n) < 110 else n[:60] + "..." + n[-40:]
+        print("| %s | %d | %.1f | %.2f | %.1f%% | %.2f | %.2f | %.2f | %.1f%% | %.0f |" % (
+            label, len(es), m["dur"] / 1e3, cyc / m["dur"],
+            100 * m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (4 * cus * cyc), 4 * wc / (4 * cus * cyc),
+            m.get("SQ_WAIT_ANY", 0.0) / wc, m.get("SQ_WAIT_INST_ANY", 0.0) / wc,
+            100 * m.get("SQ_LDS_IDX_ACTIVE", 0.0) / (cus * cyc), m.get("SQ_LDS_BANK_CONFLICT", 0.0)))
 
 
 def _counter_means(path):
@@ -856,6 +934,8 @@ def main():
                     help="in the oracle comparison, skip the dW rows of the fused linear-logp (full-batch fp64 logits)")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--cpu-linear-rows", type=int, default=512)
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time torch's bf16 GEMM (hipBLASLt) on the linear-logp products, as context")
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--summarize", nargs=2, metavar=("DIR", "MODE"))
     ap.add_argument("--counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"))
@@ -951,6 +1031,9 @@ def main():
         lin_wl = W.linear_logp(LIN_N, LIN_H, LIN_V)
         out["linear_logp"] = linear_bench(max(3, args.steps // 4), 2, device, lin_wl)
         log("linear-logp: %.2f ms fwd, %.2f ms bwd" % (out["linear_logp"]["fwd_ms"], out["linear_logp"]["bwd_ms"]))
+        if args.library_gemm:
+            out["linear_logp"]["library_gemm"] = library_gemm(device, lin_wl)
+            log("library GEMM reference: %s" % json.dumps(out["linear_logp"]["library_gemm"]))
         if not args.no_cpu_baseline:
             out["linear_logp"]["cpu_baseline"] = linear_cpu_baseline(lin_wl, args.cpu_linear_rows)
             log("linear-logp cpu baseline: %s TFLOP/s" % out["linear_logp"]["cpu_baseline"]["value"])
