@@ -216,6 +216,16 @@ __device__ __forceinline__ void dz_tile(int64_t b, int64_t ntt, int64_t nvt, int
   }
 }
 
+// dz = g (1[v = t] - p) of one logit x, the product formed at the 2^64 scale of exp_split so that
+// probabilities below 2^-126 keep their bits; c = (m, log S, -g, target column or -1) of its
+// token. -g = 0 (ignored token) gives 0 even where p is not finite (v_mul_legacy_f32); the
+// target's entry is fma(-g, p, g), rounded once.
+__device__ __forceinline__ float dz_of(float x, const f32x4& c, int lc) {
+  const PScaled pz = exp_split((x - c.x) - c.y);
+  const float gn = c.z;
+  return lc == __float_as_int(c.w) ? __builtin_fmaf(gn, pz.p * pz.f, -gn) : mul0(gn, pz.p) * pz.f;
+}
+
 // dz of one vocabulary chunk: recompute the logits tile z = h W^T (fp32 accumulation), form
 // dz = g (1[v = t] - p) with p = exp((z - m) - log S) in fp32, and store it as the bf16 pair
 // hi = rne(dz), lo = rne(dz - hi), which carries dz to about 2^-17 relative into the two
@@ -232,9 +242,9 @@ __global__ __launch_bounds__(C::NT) void lin_dz_kernel(LinArgs p) {
   const Operand A{p.h, p.ldh, p.N, p.H};
   const Operand B{p.W + p.v0 * p.ldw, p.ldw, p.cw, p.H};
   // This tile's per-token constants, read before the main loop so that their latency is
-  // hidden behind it: m, log S, the upstream gradient (NaN when the target is out of range,
-  // which makes the whole row NaN) and the target's column inside the tile (-1 when it lies
-  // in another tile, -2 for an ignored token, whose row is zero).
+  // hidden behind it: m, log S, -g (NaN when the target is out of range, which makes the whole
+  // row NaN; 0 for an ignored token, whose row is zero) and the target's column inside the tile
+  // (-1 when it lies in another tile or the token is ignored).
   f32x4 rowc = {0.0f, 0.0f, 0.0f, 0.0f};
   if (threadIdx.x < C::BM) {
     const int64_t n = m0 + threadIdx.x < p.N ? m0 + threadIdx.x : p.N - 1;
@@ -242,51 +252,71 @@ __global__ __launch_bounds__(C::NT) void lin_dz_kernel(LinArgs p) {
     const float m = p.stats[2 * n], ls = p.stats[2 * n + 1], gv = p.g[n * p.g_stride];
     const bool ignored = t == p.ignore_index, bad = !ignored && (t < 0 || t >= p.V);
     const int64_t c0 = p.v0 + n0;
-    const int32_t tc = ignored ? -2 : (t >= c0 && t < c0 + C::BN ? (int32_t)(t - c0) : -1);
-    rowc = (f32x4){m, ls, bad ? __builtin_nanf("") : gv, __int_as_float(tc)};
+    const int32_t tc = !ignored && t >= c0 && t < c0 + C::BN ? (int32_t)(t - c0) : -1;
+    const float gneg = ignored ? 0.0f : (bad ? __builtin_nanf("") : -gv);
+    rowc = (f32x4){m, ls, gneg, __int_as_float(tc)};
   }
   Acc<C> acc;
   gemm::mainloop<C>(A, B, m0, n0, p.H, lds, acc);  // ends with a barrier: LDS is free again
   f32x4* cst = reinterpret_cast<f32x4*>(lds);
   if (threadIdx.x < C::BM) cst[threadIdx.x] = rowc;
   __syncthreads();
-  // dz = g (1[v = t] - p) = fma(-g, p, g 1[v = t]); interior tiles store without guards.
-  const bool interior = m0 + C::BM <= p.N && n0 + C::BN <= p.cw;
   uint16_t* th = p.dzh + m0 * p.ldc + n0;
   uint16_t* tl = p.dzl + m0 * p.ldc + n0;
+  if (m0 + C::BM <= p.N && n0 + C::BN <= p.cw && p.ldc < (1 << 23)) {
+    // Interior tile: no guards, 32-bit byte offsets from the tile's base (below 2^32 for rows of
+    // fewer than 2^23 columns, so the stores take a scalar base and a 32-bit offset), and the
+    // two rows v, v + 1 of an accumulator pair rounded by one conversion per plane.
+    const uint32_t ldb = (uint32_t)p.ldc * 2u;  // row pitch in bytes
+    char* thb = reinterpret_cast<char*>(th);
+    char* tlb = reinterpret_cast<char*>(tl);
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i)
+    for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = wm * C::TM + gemm::acc_row(i, v, lane);
-      const f32x4 c = cst[r];
-      const float m = c.x, ls = c.y, gv = c.z;
-      const int32_t tc = __float_as_int(c.w);
-      const int64_t ro = (int64_t)r * p.ldc;
+      for (int v = 0; v < 16; v += 2) {
+        const int r = wm * C::TM + gemm::acc_row(i, v, lane);  // row r + 1 holds accumulator v + 1
+        const f32x4 c0 = cst[r], c1 = cst[r + 1];
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        const int lc = wn * C::TN + gemm::acc_col(j, lane);
-        const PScaled pz = exp_split((acc.c[i][j][v] - m) - ls);
-        float d = lc == tc ? __builtin_fmaf(-gv, pz.p * pz.f, gv) : (-gv * pz.p) * pz.f;
-        d = tc == -2 ? 0.0f : d;
-        const bf16x2 hb = __builtin_convertvector((f32x2){d, 0.0f}, bf16x2);
-        const uint32_t hbits = __builtin_bit_cast(uint32_t, hb) & 0xffffu;
-        const float lo = d - __uint_as_float(hbits << 16);  // exact (Sterbenz), 0 for 0 and NaN
-        const bf16x2 lb = __builtin_convertvector((f32x2){lo, 0.0f}, bf16x2);
-        const uint16_t lbits = (uint16_t)(__builtin_bit_cast(uint32_t, lb) & 0xffffu);
-        if (interior) {
-          th[ro + lc] = (uint16_t)hbits;
-          tl[ro + lc] = lbits;
-        } else {
-          // columns [cw, ldc) pad the rows with zeros for the dh contraction
+        for (int j = 0; j < C::FN; ++j) {
+          const int lc = wn * C::TN + gemm::acc_col(j, lane);
+          const float d0 = dz_of(acc.c[i][j][v], c0, lc), d1 = dz_of(acc.c[i][j][v + 1], c1, lc);
+          const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){d0, d1}, bf16x2));
+          // exact (Sterbenz), 0 for 0 and NaN
+          const float l0 = d0 - __uint_as_float(hb << 16), l1 = d1 - __uint_as_float(hb & 0xffff0000u);
+          const uint32_t lb = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){l0, l1}, bf16x2));
+          const uint32_t o = (uint32_t)r * ldb + (uint32_t)lc * 2u;
+          *reinterpret_cast<uint16_t*>(thb + o) = (uint16_t)hb;
+          *reinterpret_cast<uint16_t*>(thb + (o + ldb)) = (uint16_t)(hb >> 16);
+          *reinterpret_cast<uint16_t*>(tlb + o) = (uint16_t)lb;
+          *reinterpret_cast<uint16_t*>(tlb + (o + ldb)) = (uint16_t)(lb >> 16);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * C::TM + gemm::acc_row(i, v, lane);
+        const f32x4 c = cst[r];
+        const int64_t ro = (int64_t)r * p.ldc;
+        const bool row_ok = m0 + r < p.N;
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+          const int lc = wn * C::TN + gemm::acc_col(j, lane);
           const int64_t col = n0 + lc;
-          if (m0 + r < p.N && col < p.ldc) {
-            th[ro + lc] = col < p.cw ? (uint16_t)hbits : (uint16_t)0;
-            tl[ro + lc] = col < p.cw ? lbits : (uint16_t)0;
+          if (row_ok && col < p.ldc) {
+            // columns [cw, ldc) pad the rows with zeros for the dh contraction
+            const float d = col < p.cw ? dz_of(acc.c[i][j][v], c, lc) : 0.0f;
+            const bf16x2 hb = __builtin_convertvector((f32x2){d, 0.0f}, bf16x2);
+            const uint32_t hbits = __builtin_bit_cast(uint32_t, hb) & 0xffffu;
+            const float lo = d - __uint_as_float(hbits << 16);
+            const bf16x2 lb = __builtin_convertvector((f32x2){lo, 0.0f}, bf16x2);
+            th[ro + lc] = (uint16_t)hbits;
+            tl[ro + lc] = (uint16_t)(__builtin_bit_cast(uint32_t, lb) & 0xffffu);
           }
         }
       }
-    }
+  }
 }
 
 // Block -> (M tile, N tile) of a contraction with a long reduction (K = 8192 for dh and dW).
