@@ -353,11 +353,58 @@ __global__ __launch_bounds__(C::NT) void gemm_pair_kernel(GemmArgs g) {
   int64_t tm, tn;
   pair_tile((int64_t)blockIdx.x, ntm, ntn, tm, tn);
   const int64_t m0 = tm * C::BM, n0 = tn * C::BN;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
   Acc<C> acc;
   gemm::mainloop_pp<C>(g.A, g.B, m0, n0, g.K, lds, acc);
   const int mode = g.mode;
+  if (m0 + C::BM <= g.M && n0 + C::BN <= g.Nc && g.ldc < (1 << 22)) {
+    // Interior tile: the mode is tested once, addresses are the wave's scalar tile base plus a
+    // 32-bit byte offset (below 2^32: 64 rows of fewer than 2^22 fp32), bf16 results are rounded
+    // two rows (accumulators v, v + 1) per conversion, and the running sum is read one 32 x 32
+    // block (16 values a lane) at a time before any of it is added: one memory wait per block.
+    const int64_t wo = (m0 + wm * C::TM) * g.ldc + n0 + wn * C::TN;
+    const uint32_t ld = (uint32_t)g.ldc;
+    char* cb = reinterpret_cast<char*>(g.C + wo);
+    char* ab = reinterpret_cast<char*>(g.acc + wo);
+    auto off = [&](int i, int v, int j) { return (uint32_t)gemm::acc_row(i, v, lane) * ld + (uint32_t)gemm::acc_col(j, lane); };
+    auto store_pairs = [&](int i, int j, const float (&y)[16]) {
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){y[v], y[v + 1]}, bf16x2));
+        const uint32_t o = off(i, v, j) * 2u;  // row v + 1 is one pitch further
+        *reinterpret_cast<uint16_t*>(cb + o) = (uint16_t)hb;
+        *reinterpret_cast<uint16_t*>(cb + (o + ld * 2u)) = (uint16_t)(hb >> 16);
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        float y[16];
+        if (mode == kDhStore) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) y[v] = acc.c[i][j][v];
+          store_pairs(i, j, y);
+        } else if (mode == kDhFirst) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) *reinterpret_cast<float*>(ab + off(i, v, j) * 4u) = acc.c[i][j][v];
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) y[v] = *reinterpret_cast<const float*>(ab + off(i, v, j) * 4u);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) y[v] = y[v] + acc.c[i][j][v];  // the running sum first: chunk order
+          if (mode == kDhAdd) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) *reinterpret_cast<float*>(ab + off(i, v, j) * 4u) = y[v];
+          } else {
+            store_pairs(i, j, y);
+          }
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
