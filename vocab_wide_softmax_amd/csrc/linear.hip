@@ -93,18 +93,24 @@ __global__ __launch_bounds__(C::NT) void lin_fwd_kernel(LinArgs p) {
   for (int64_t vt = vt0; vt < vt1; ++vt) {
     const int64_t m0 = vt * C::BM;
     gemm::mainloop_pp<C>(A, B, m0, n0, p.H, lds, acc);  // ping-pong: 3% faster here, not for dz
+    if (m0 + C::BM > p.V) {  // the last vocabulary tile: rows past V take no part
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t row = m0 + wm * C::TM + gemm::acc_row(i, v, lane);
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+            if (row >= p.V) acc.c[i][j][v] = -kInf;
+        }
+    }
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
       float bm = -kInf;
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t row = m0 + wm * C::TM + gemm::acc_row(i, v, lane);
-          const float z = row < p.V ? acc.c[i][j][v] : -kInf;
-          acc.c[i][j][v] = z;
-          bm = fmaxf(bm, z);
-        }
+        for (int v = 0; v < 16; ++v) bm = fmaxf(bm, acc.c[i][j][v]);
       if (bm > st[j].m) {
         const float s = expf_fast(st[j].m - bm);
         st[j].S *= s;
