@@ -247,25 +247,30 @@ __global__ __launch_bounds__(C::NT) void lin_dz_kernel(LinArgs p) {
   const int wm = wave / C::WN, wn = wave % C::WN;
   const Operand A{p.h, p.ldh, p.N, p.H};
   const Operand B{p.W + p.v0 * p.ldw, p.ldw, p.cw, p.H};
-  // This tile's per-token constants, read before the main loop so that their latency is
-  // hidden behind it: m, log S, -g (NaN when the target is out of range, which makes the whole
-  // row NaN; 0 for an ignored token, whose row is zero) and the target's column inside the tile
-  // (-1 when it lies in another tile or the token is ignored).
-  f32x4 rowc = {0.0f, 0.0f, 0.0f, 0.0f};
+  // This tile's per-token inputs are loaded before the main loop and used only after it, so
+  // their latency hides behind it (deriving anything from them here would wait for them first).
+  int64_t t = 0;
+  float m = 0.0f, ls = 0.0f, gv = 0.0f;
   if (threadIdx.x < C::BM) {
     const int64_t n = m0 + threadIdx.x < p.N ? m0 + threadIdx.x : p.N - 1;
-    const int64_t t = p.t[n];
-    const float m = p.stats[2 * n], ls = p.stats[2 * n + 1], gv = p.g[n * p.g_stride];
+    t = p.t[n];
+    m = p.stats[2 * n];
+    ls = p.stats[2 * n + 1];
+    gv = p.g[n * p.g_stride];
+  }
+  Acc<C> acc;
+  gemm::mainloop<C>(A, B, m0, n0, p.H, lds, acc);  // ends with a barrier: LDS is free again
+  // Row constants in LDS: m, log S, -g (NaN when the target is out of range, which makes the
+  // whole row NaN; 0 for an ignored token, whose row is zero) and the target's column inside the
+  // tile (-1 when it lies in another tile or the token is ignored).
+  f32x4* cst = reinterpret_cast<f32x4*>(lds);
+  if (threadIdx.x < C::BM) {
     const bool ignored = t == p.ignore_index, bad = !ignored && (t < 0 || t >= p.V);
     const int64_t c0 = p.v0 + n0;
     const int32_t tc = !ignored && t >= c0 && t < c0 + C::BN ? (int32_t)(t - c0) : -1;
     const float gneg = ignored ? 0.0f : (bad ? __builtin_nanf("") : -gv);
-    rowc = (f32x4){m, ls, gneg, __int_as_float(tc)};
+    cst[threadIdx.x] = (f32x4){m, ls, gneg, __int_as_float(tc)};
   }
-  Acc<C> acc;
-  gemm::mainloop<C>(A, B, m0, n0, p.H, lds, acc);  // ends with a barrier: LDS is free again
-  f32x4* cst = reinterpret_cast<f32x4*>(lds);
-  if (threadIdx.x < C::BM) cst[threadIdx.x] = rowc;
   __syncthreads();
   uint16_t* th = p.dzh + m0 * p.ldc + n0;
   uint16_t* tl = p.dzl + m0 * p.ldc + n0;
