@@ -258,6 +258,23 @@ def test_linear_strided_rows_broadcast_g_and_partial_stage(device):
                              "bf16"), "strided dW")
 
 
+def test_linear_multichunk_interior_all_elements(device):
+    """512 tokens, hidden 512 and three vocabulary chunks of 8192: every dh tile is interior and
+    takes, chunk by chunk, the first / add / last epilogue of the fp32 running sum (batched reads,
+    paired bf16 rounding), every dW and dz tile the interior epilogue; all elements against the
+    oracle."""
+    wl = W.linear_logp(n=512, hidden=512, v=3 * 8192, seed=29, w_std=0.05)
+    wl.t[::41] = -100
+    logp, stats, dh, dW = _run(wl.h, wl.W, wl.t, wl.g, device)
+    hh, hw, ht, hg = f64(wl.h), f64(wl.W), wl.t.numpy(), wl.g.double().numpy()
+    lp, m, ls = OL.linear_logp_fwd(hh, hw, ht)
+    _assert_ok(compare.check(f64(logp), lp, OL.cond_linear_fwd(hh, hw, ht), "f32"), "multichunk logp")
+    _assert_ok(compare.check(f64(dh), OL.linear_logp_bwd_dh(hh, hw, ht, hg), OL.cond_linear_dh(hh, hw, ht, hg),
+                             "bf16"), "multichunk dh")
+    dw_ref, dw_c = OL.linear_logp_bwd_dw_cond(hh, hw, ht, hg)
+    _assert_ok(compare.check(f64(dW), dw_ref, dw_c, "bf16"), "multichunk dW")
+
+
 @pytest.mark.slow
 def test_linear_xcd_patch_orders_all_elements(device):
     """Hidden width 4096 (16 hidden tiles) with 17 token tiles and 17 vocabulary tiles: the dh and
