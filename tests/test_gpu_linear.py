@@ -258,6 +258,25 @@ def test_linear_strided_rows_broadcast_g_and_partial_stage(device):
                              "bf16"), "strided dW")
 
 
+@pytest.mark.parametrize("n,hidden,v", [(256, 64, 512), (256, 128, 512), (256, 192, 768),
+                                         (32, 256, 512), (64, 256, 512), (96, 256, 512)])
+def test_linear_short_reductions_all_elements(device, n, hidden, v):
+    """Interior tiles with one to three k-stages: the forward's ping-pong loop at hidden 64 / 128 /
+    192 (64-deep stages) and the dW pair's at 32 / 64 / 96 tokens (32-deep stages), where the
+    prologue issues fewer stages than the ring holds and the in-flight counts of the waits are
+    smallest; all elements against the oracle."""
+    wl = W.linear_logp(n=n, hidden=hidden, v=v, seed=31 + n + hidden, w_std=0.1)
+    wl.t[::7] = -100
+    logp, stats, dh, dW = _run(wl.h, wl.W, wl.t, wl.g, device)
+    hh, hw, ht, hg = f64(wl.h), f64(wl.W), wl.t.numpy(), wl.g.double().numpy()
+    lp, m, ls = OL.linear_logp_fwd(hh, hw, ht)
+    _assert_ok(compare.check(f64(logp), lp, OL.cond_linear_fwd(hh, hw, ht), "f32"), "short logp %d %d" % (n, hidden))
+    _assert_ok(compare.check(f64(dh), OL.linear_logp_bwd_dh(hh, hw, ht, hg), OL.cond_linear_dh(hh, hw, ht, hg),
+                             "bf16"), "short dh %d %d" % (n, hidden))
+    dw_ref, dw_c = OL.linear_logp_bwd_dw_cond(hh, hw, ht, hg)
+    _assert_ok(compare.check(f64(dW), dw_ref, dw_c, "bf16"), "short dW %d %d" % (n, hidden))
+
+
 def test_linear_multichunk_interior_all_elements(device):
     """512 tokens, hidden 512 and three vocabulary chunks of 8192: every dh tile is interior and
     takes, chunk by chunk, the first / add / last epilogue of the fp32 running sum (batched reads,
