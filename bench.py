@@ -268,11 +268,12 @@ def op_bwd(B, op, a, b, t, g, out, st):
     return B.kl_bwd(x, y, st, out, g)
 
 
-def op_times(ops, a, b, t, g, steps, warmup, flush=None):
+def op_times(ops, a, b, t, g, steps, warmup, flush=None, split=0):
     """Median fwd and bwd ms per op, the ops interleaved (the pages interleave their timed runs).
     With `flush`, a device buffer of 512 MB is overwritten before every op's forward, outside the
     event interval, so that the op starts with nothing of its inputs in the 256 MB Infinity Cache
-    or the L2 caches. All iterations are enqueued before one synchronisation."""
+    or the L2 caches. `split` is the forwards' split_hint. All iterations are enqueued before one
+    synchronisation."""
     import torch
 
     from vocab_wide_softmax_amd import binding as B
@@ -280,7 +281,7 @@ def op_times(ops, a, b, t, g, steps, warmup, flush=None):
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         for op in ops:
-            out, st = op_fwd(B, op, a, b, t)
+            out, st = op_fwd(B, op, a, b, t, split)
             op_bwd(B, op, a, b, t, g[op], out, st)
     evs = {op: [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)] for op in ops}
     torch.cuda.synchronize()
@@ -290,7 +291,7 @@ def op_times(ops, a, b, t, g, steps, warmup, flush=None):
                 flush.zero_()
             e = evs[op][i]
             e[0].record(stream)
-            out, st = op_fwd(B, op, a, b, t)
+            out, st = op_fwd(B, op, a, b, t, split)
             e[1].record(stream)
             grads = op_bwd(B, op, a, b, t, g[op], out, st)
             e[2].record(stream)
@@ -341,9 +342,11 @@ def memory_report(ops, a, b, t, g):
 
 def pair1024_leg(device, steps, warmup, wl=None):
     """The 1024 x 75968 bf16 pair (config 1: the shape of one tensor-parallel rank of a 151936-token
-    vocabulary, where the forward splits each row's vocabulary and an in-GPU combine merges the
-    parts): the four ops fwd+bwd, timed as they are (inputs of 156 MB each can sit in the 256 MB
-    Infinity Cache) and with the cache flushed before every op."""
+    vocabulary): the four ops fwd+bwd, timed as they are (inputs of 156 MB each can sit in the
+    256 MB Infinity Cache) and with the cache flushed before every op. The automatic launch does
+    not split the vocabulary at 1024 rows (one workgroup per row already fills the chip; split
+    forwards measured slower); `flushed_split8` times the forwards split into 8 parts merged by
+    the in-GPU combine, the pages' cross-shard path, for comparison."""
     import torch
 
     from vocab_wide_softmax_amd import binding as B
@@ -359,13 +362,15 @@ def pair1024_leg(device, steps, warmup, wl=None):
     torch.cuda.synchronize()
     warm = op_times(W.OPS, a, b, t, g, steps, warmup)
     cold = op_times(W.OPS, a, b, t, g, steps, warmup, flush=flush)
+    cold8 = op_times(W.OPS, a, b, t, g, steps, warmup, flush=flush, split=8)
     out = {"workload": "1024x75968 bf16 pair (A~N(0,3^2), B=A+N(0,0.5^2), 5% rows +1e4, 1% rows with 64 B "
                        "columns at -inf)", "vocab_parts": B.split_parts(B.OP_KL, n, v),
-           "unflushed": {}, "flushed": {}}
+           "unflushed": {}, "flushed": {}, "flushed_split8": {}}
     for op in W.OPS:
         out["unflushed"][op] = _op_entry(*warm[op], nbytes[op])
         out["flushed"][op] = _op_entry(*cold[op], nbytes[op])
-    for k, res in (("unflushed", warm), ("flushed", cold)):
+        out["flushed_split8"][op] = _op_entry(*cold8[op], nbytes[op])
+    for k, res in (("unflushed", warm), ("flushed", cold), ("flushed_split8", cold8)):
         tot = sum(sum(res[op]) for op in W.OPS)
         out[k]["all_four"] = _op_entry(tot, 0.0, sum(nbytes.values()))
     del flush

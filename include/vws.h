@@ -128,7 +128,8 @@ typedef struct vws_ids_k {
  * when N is small (the pages' cross-shard combine -- MAX of m, re-centring of
  * S and W on it, SUM -- done inside one GPU); the partial statistics go to
  * the workspace and a second kernel merges them. split_hint:
- *   0 = automatic (P grows as N shrinks; a row's rounding may then depend on N),
+ *   0 = automatic (P = ceil(768 / N): about three workgroups per CU, each part at
+ *       least 4096 columns; unsplit from 768 rows; a row's rounding may then depend on N),
  *   1 = never split, P > 1 = split into P parts (capped at ceil(V/8)),
  *   VWS_SPLIT_INVARIANT (-1) = fixed segments of 32768 columns, so P and every
  *       row's reduction order depend on V alone: a row's outputs are bitwise

@@ -44,15 +44,20 @@ def test_strerror(L):
 
 def test_split_parts_and_workspace(L):
     # long rows, few of them: split; many rows: no split
-    assert B.split_parts(B.OP_ENTROPY, 1024, 75968) == 8
+    assert B.split_parts(B.OP_ENTROPY, 1024, 75968) == 1  # 1024 rows fill the chip unsplit
+    assert B.split_parts(B.OP_ENTROPY, 256, 75968) == 3   # about 768 workgroups
+    assert B.split_parts(B.OP_ENTROPY, 64, 75968) == 12
+    assert B.split_parts(B.OP_ENTROPY, 1, 75968) == 18    # parts of at least 512 groups
     assert B.split_parts(B.OP_ENTROPY, 8192, 75968) == 1
     assert B.split_parts(B.OP_KL, 64, 1024, 4) == 4
     assert B.split_parts(B.OP_KL, 64, 1024, 16) == 16
     assert B.split_parts(B.OP_KL, 64, 1024, 1) == 1
     assert B.split_parts(B.OP_KL, 3, 20, 64) == 3  # capped at ceil(V/8) groups
     assert B.workspace_bytes(B.OP_ENTROPY, 8192, 75968) == 0
-    assert B.workspace_bytes(B.OP_ENTROPY, 1024, 75968) == 1024 * 8 * 3 * 4
-    assert B.workspace_bytes(B.OP_KL, 1024, 75968) == 1024 * 8 * 6 * 4
+    assert B.workspace_bytes(B.OP_ENTROPY, 1024, 75968) == 0
+    assert B.workspace_bytes(B.OP_ENTROPY, 256, 75968) == 256 * 3 * 3 * 4
+    assert B.workspace_bytes(B.OP_KL, 256, 75968) == 256 * 3 * 6 * 4
+    assert B.workspace_bytes(B.OP_KL, 1024, 75968, 8) == 1024 * 8 * 6 * 4
     assert B.workspace_bytes(B.OP_KL, 0, 75968) == 0
     with pytest.raises(ValueError):
         B.workspace_bytes(7, 10, 10)

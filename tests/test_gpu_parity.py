@@ -65,13 +65,18 @@ def pair1024(device):
 
 @pytest.mark.parametrize("op", OPS)
 def test_pair1024_all_elements(pair1024, op):
+    """Every element at 1024 x 75968, in the automatic launch (unsplit at this row count) and with
+    the vocabulary split into 8 parts merged by the in-GPU combine."""
     wl, (a, b, t), (ha, hb, ht) = pair1024
-    assert B.split_parts(B.OP_KL, a.shape[0], a.shape[1]) > 1  # the split-vocab path is what runs here
-    print("pair1024", op, flush=True)
-    dev = run_device(op, a, b, t, wl.g[op].to(a.device))
+    assert B.split_parts(B.OP_KL, a.shape[0], a.shape[1]) == 1
+    assert B.split_parts(B.OP_KL, a.shape[0], a.shape[1], 8) == 8
     ora = run_oracle(op, ha, hb, ht, wl.g[op].double().numpy())
-    reps = check_parity(dev, ora, "bf16", "pair1024 " + op)
-    print({k: (v["strict_miss"], round(v["worst"], 3)) for k, v in reps.items()}, flush=True)
+    for split in (0, 8):
+        print("pair1024", op, "split", split, flush=True)
+        dev = run_device(op, a, b, t, wl.g[op].to(a.device), split_hint=split)
+        reps = check_parity(dev, ora, "bf16", "pair1024 %s split %d" % (op, split))
+        print({k: (v["strict_miss"], round(v["worst"], 3)) for k, v in reps.items()}, flush=True)
+        del dev
 
 
 def _sample_rows(wl, n, k=24, seed=5):

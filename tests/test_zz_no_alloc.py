@@ -26,7 +26,7 @@ def _pair(n, v, seed):
     return a.to(torch.bfloat16), b.to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("calls", [((512, 20000, 0), (64, 3000, 7)), ((1024, 75968, 0), (96, 40000, B.SPLIT_INVARIANT))])
+@pytest.mark.parametrize("calls", [((512, 20000, 0), (64, 3000, 7)), ((1024, 75968, 8), (96, 40000, B.SPLIT_INVARIANT))])
 def test_noalloc_matches_workspace_entry(device, calls):
     for i, (n, v, split) in enumerate(calls):
         print("noalloc call", i, "n", n, "v", v, "split", split, flush=True)
