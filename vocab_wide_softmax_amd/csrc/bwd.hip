@@ -146,6 +146,64 @@ __device__ __forceinline__ void bwd_store(const RowBwd& r, const float (&xa)[UB]
   }
 }
 
+// Gradient of one element, the same arithmetic as bwd_store. For logprobs `tgt` marks the
+// target's column.
+template <int OP>
+__device__ __forceinline__ void elem_grad(const RowBwd& r, float xa, float xb, bool tgt, float& ya, float& yb) {
+  const float qnan = __builtin_nanf("");
+  if constexpr (OP == kKL) {
+    const float ua = (xa - r.m) - r.ls;
+    const float ub = (xb - r.mb) - r.lsb;
+    const PScaled pa = exp_split(ua);
+    const PScaled pb = exp_split(ub);
+    ya = r.nan_a ? qnan : (mul0(pa.p, (ua - ub) - r.res) * r.gv) * pa.f;
+    yb = r.nan_b ? qnan : ((pb.p - pa.p) * r.gv) * pa.f;
+  } else if constexpr (OP == kEntropy) {
+    const float lp = (xa - r.m) - r.ls;
+    const PScaled pj = exp_split(lp);
+    ya = r.nan_a ? qnan : (mul0(pj.p, lp + r.res) * (-r.gv)) * pj.f;
+  } else {
+    const PScaled pj = exp_split((xa - r.m) - r.ls);
+    ya = r.zero ? 0.0f : (r.nan_a ? qnan : (-r.gv * pj.p) * pj.f);
+    if (tgt) ya = r.gv * (1.0f - pj.p * pj.f);
+  }
+}
+
+// A whole fp32 tile (columns [8 g0, 8 (g0 + BLOCK UB))): the backward is elementwise, so instead of
+// a lane's group of 8 columns (32 bytes, two 16-byte accesses that each cover every other 16-byte
+// piece of the wave's span) lane l takes 16-byte pieces l, l + BLOCK, ...: every access of the
+// wave covers one contiguous 1 KB.
+template <int OP, int BLOCK, int UB>
+__device__ __forceinline__ void bwd_tile_f32(const BwdArgs& p, int64_t row, const char* ra, const char* rb, char* oa,
+                                             char* ob, int32_t g0, int32_t V) {
+  constexpr int NP = 2 * UB;
+  const int64_t q0 = 2 * (int64_t)g0 + threadIdx.x;  // this lane's first piece
+  f32x4 xa[NP], xb[OP == kKL ? NP : 1];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    xa[k] = stream_load(reinterpret_cast<const f32x4*>(ra) + q0 + k * BLOCK);
+    if constexpr (OP == kKL) xb[k] = stream_load(reinterpret_cast<const f32x4*>(rb) + q0 + k * BLOCK);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const RowBwd r = row_consts<OP>(p, row, V);
+  const int64_t tcol = r.tg >= 0 ? (int64_t)r.tg * 8 + r.tj : -1;
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const int64_t c0 = 4 * (q0 + k * BLOCK);
+    f32x4 ya, yb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float a, b = 0.0f;
+      elem_grad<OP>(r, xa[k][e], OP == kKL ? xb[k][e] : 0.0f, c0 + e == tcol, a, b);
+      ya[e] = a;
+      yb[e] = b;
+    }
+    if (oa) stream_store(ya, reinterpret_cast<f32x4*>(oa) + q0 + k * BLOCK);
+    if constexpr (OP == kKL)
+      if (ob) stream_store(yb, reinterpret_cast<f32x4*>(ob) + q0 + k * BLOCK);
+  }
+}
+
 template <int OP, int DT, bool VEC, int BLOCK, int UB>
 __global__ __launch_bounds__(BLOCK) void bwd_kernel(BwdArgs p) {
   constexpr int ES = ElemSize<DT>::value;
@@ -164,6 +222,12 @@ __global__ __launch_bounds__(BLOCK) void bwd_kernel(BwdArgs p) {
     char* ob = OP == kKL && p.db ? p.db + row * (int64_t)V * ES : nullptr;
     const int32_t g = g0 + threadIdx.x;
     float xa[UB][8], xb[OP == kKL ? UB : 1][8];
+    if constexpr (DT == kF32 && VEC) {
+      if (g0 + BLOCK * UB <= g_full) {
+        bwd_tile_f32<OP, BLOCK, UB>(p, row, ra, rb, oa, ob, g0, V);
+        continue;
+      }
+    }
     if (VEC && g0 + BLOCK * UB <= g_full) {
       // the whole tile's loads first, then the row constants: one memory latency per tile
       RawGroup<DT> wa[UB], wb[OP == kKL ? UB : 1];
