@@ -221,7 +221,7 @@ int bwd_common(int op, const vws_rows* a, const vws_rows* b, const vws_ids* t, i
   if (!aligned(da, es) || !aligned(db, es)) return VWS_ELAYOUT;
   int64_t nv, bytes;
   if (!mul_ok(N, a->V, &nv) || !mul_ok(nv, es, &bytes)) return VWS_EINVAL;
-  const int32_t tpr = vws::bwd_tiles_per_row(op, a->V);
+  const int32_t tpr = vws::bwd_tiles_per_row(op, a->dtype, a->V);
   if (N * (int64_t)tpr > (int64_t)INT32_MAX) return VWS_EINVAL;
 
   BwdArgs p{};

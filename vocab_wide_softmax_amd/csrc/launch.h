@@ -139,6 +139,6 @@ inline int64_t grid_cap(int64_t blocks) { return blocks < (1 << 20) ? (blocks > 
 
 hipError_t launch_fwd(int op, const FwdArgs& p, int dtype, bool vec, hipStream_t stream);
 hipError_t launch_bwd(int op, const BwdArgs& p, int dtype, bool vec, hipStream_t stream);
-int32_t bwd_tiles_per_row(int op, int64_t V);
+int32_t bwd_tiles_per_row(int op, int dtype, int64_t V);
 
 }  // namespace vws
