@@ -259,11 +259,14 @@ constexpr int kBwdBlock = 256;
 // on 16-bit data (4096-column tiles), 1 for KL, which reads two inputs, and for fp32 data
 // (2048-column tiles; on fp32 the single-input ops ran 11% slower with 2, KL 7% slower with 2).
 constexpr int bwd_ub(int op, int dt) { return op == kKL || dt == kF32 ? 1 : 2; }
+// Lanes per workgroup: 256, and 128 for fp32 KL (1024-column tiles, one 16-byte piece per input
+// and lane; 1.8% faster there than 256).
+constexpr int bwd_block(int op, int dt) { return op == kKL && dt == kF32 ? 128 : kBwdBlock; }
 
 template <int OP, int DT, bool VEC>
 hipError_t launch_bwd_t(const BwdArgs& p, hipStream_t stream) {
   const int64_t blocks = grid_cap(p.N * p.tiles_per_row);
-  hipLaunchKernelGGL((bwd_kernel<OP, DT, VEC, kBwdBlock, bwd_ub(OP, DT)>), dim3((uint32_t)blocks), dim3(kBwdBlock), 0,
+  hipLaunchKernelGGL((bwd_kernel<OP, DT, VEC, bwd_block(OP, DT), bwd_ub(OP, DT)>), dim3((uint32_t)blocks), dim3(bwd_block(OP, DT)), 0,
                      stream, p);
   return hipGetLastError();
 }
@@ -279,7 +282,7 @@ hipError_t launch_bwd_op(const BwdArgs& p, int dtype, bool vec, hipStream_t stre
 
 int32_t bwd_tiles_per_row(int op, int dtype, int64_t V) {
   const int64_t G = (V + 7) / 8;
-  const int64_t per = (int64_t)kBwdBlock * bwd_ub(op, dtype);
+  const int64_t per = (int64_t)bwd_block(op, dtype) * bwd_ub(op, dtype);
   return (int32_t)((G + per - 1) / per);
 }
 
