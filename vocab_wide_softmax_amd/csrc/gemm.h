@@ -303,11 +303,13 @@ __device__ __forceinline__ void stage_ready(int s, int nk) {
   asm volatile("" ::: "memory");  // keep LDS reads and DMA issues on their side of the barrier
 }
 
-// Buffer-path refills go out in Cfg::PIECES pieces per stage (see mainloop_t). For the plain
-// GEMMs (BK = 64, four slices per stage) two pieces, each interleaved one load per MFMA, ran 1.2-1.9%
-// faster than one burst of a stage's loads after the barrier (bit-identical results); four pieces
-// were slower (the last piece then has under two slices of lead time). The split-A GEMMs (BK = 32,
-// two slices per stage, twice the MFMAs per slice) run 5-7% faster with one burst.
+// In mainloop_t, buffer-path refills go out in Cfg::PIECES pieces per stage, each interleaved one
+// load per MFMA. When the plain GEMMs all ran this loop (BK = 64, four slices per stage), two
+// pieces were 1.2-1.9% faster than one burst of a stage's loads after the barrier (bit-identical
+// results) and four pieces slower (the last piece then has under two slices of lead time); the
+// split-A GEMMs (BK = 32, two slices per stage, twice the MFMAs per slice) were 5-7% faster with
+// one burst. In mainloop_pp_t, PIECES = 2 with three or more stages splits each refill over the
+// two read phases of a stage.
 
 // Loads [J0, J1) of one stage's refill, counted over the A loads then the B loads (buffer path).
 template <class C, int J0, int J1>

@@ -31,9 +31,10 @@ using gemm::KROW;
 using gemm::Operand;
 using gemm::ROWK;
 
-// Logits tiles, A and B both reduction-contiguous: the forward refills a stage in two pieces
-// spread over the stage's first slices, the dz pass in one burst after its barrier (each the
-// faster for that kernel, by 3% and 1%; bit-identical either way).
+// Logits tiles, A and B both reduction-contiguous, two stages of BK = 64. The forward runs the
+// ping-pong main loop, whose two-stage refill goes out whole in one read phase (PIECES plays no
+// part there, nor on the flat path of edge tiles); dz runs the shared loop and refills a stage in
+// one burst after its barrier (1% faster there than two pieces; bit-identical either way).
 typedef Cfg<256, 256, 64, 2, 4, ROWK, ROWK, 2, 1, 1> CfgNT;   // dz
 typedef Cfg<256, 256, 64, 2, 4, ROWK, ROWK, 2, 1, 2> CfgFwd;  // forward
 // dh = dz W and dW = dz^T h with dz a bf16 (hi, lo) pair: 3 stages of BK = 32 (48 KB each), wave
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(C::NT) void lin_fwd_kernel(LinArgs p) {
   Acc<C> acc;
   for (int64_t vt = vt0; vt < vt1; ++vt) {
     const int64_t m0 = vt * C::BM;
-    gemm::mainloop_pp<C>(A, B, m0, n0, p.H, lds, acc);  // ping-pong: 3% faster here, not for dz
+    gemm::mainloop_pp<C>(A, B, m0, n0, p.H, lds, acc);  // ping-pong: 3% faster here (dz: no gain)
     if (m0 + C::BM > p.V) {  // the last vocabulary tile: rows past V take no part
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
