@@ -115,6 +115,9 @@ int state_floats(int op) { return op == VWS_OP_KL ? 6 : 3; }
 // Segment length (in groups of 8 columns) of the batch-invariant split: 32768 columns.
 constexpr int64_t kInvariantGroups = 4096;
 
+// Most slots the unsplit forward writes itself (one per lane of its 256-lane workgroup).
+constexpr int64_t kFwdTopkMaxK = 256;
+
 // Vocabulary parts per row for the forward (see vws_split_parts in vws.h).
 int parts_for(int op, int64_t N, int64_t V, int hint) {
   const int64_t G = (V + 7) / 8;
@@ -150,9 +153,11 @@ int parts_for(int op, int64_t N, int64_t V, int hint) {
 // stats_only (logprobs): write the row statistics but no per-row output, for the multi-id forward.
 // static_ws: take the workspace from the library's static scratch (vws_kl_fwd_noalloc) instead of
 // ws / ws_bytes.
+// topk: multi-id logprobs written by the unsplit forward itself (out [N, K], 1 <= K <= kFwdTopkMaxK;
+// the caller checks that the launch is unsplit).
 int fwd_common(int op, const vws_rows* a, const vws_rows* b, const vws_ids* t, int64_t ignore_index, float* out,
                float* stats, void* ws, size_t ws_bytes, int split_hint, void* stream, bool stats_only = false,
-               bool static_ws = false) {
+               bool static_ws = false, const vws_ids_k* topk = nullptr) {
   int64_t N, Nb;
   int rc = check_rows(a, &N);
   if (rc) return rc;
@@ -163,7 +168,7 @@ int fwd_common(int op, const vws_rows* a, const vws_rows* b, const vws_ids* t, i
   }
   if (split_hint < VWS_SPLIT_INVARIANT) return VWS_EINVAL;
   if (N == 0) return VWS_OK;
-  if (op == VWS_OP_LOGPROBS && !stats_only && (rc = check_ids(t))) return rc;
+  if (op == VWS_OP_LOGPROBS && !stats_only && !topk && (rc = check_ids(t))) return rc;
   if ((!out && !stats_only) || !stats) return VWS_EINVAL;
   if (!aligned(out, 4) || !aligned(stats, 4)) return VWS_ELAYOUT;
   const int P = parts_for(op, N, a->V, split_hint);
@@ -185,6 +190,11 @@ int fwd_common(int op, const vws_rows* a, const vws_rows* b, const vws_ids* t, i
   p.a = rows_dev(a);
   if (op == VWS_OP_KL) p.b = rows_dev(b);
   p.ids = ids_dev(op == VWS_OP_LOGPROBS && !stats_only ? t : nullptr);
+  if (topk) {
+    p.ids = vws::IdsDev{topk->data, topk->s_outer, topk->s_inner};
+    p.ids_sk = topk->s_k;
+    p.K = (int32_t)topk->K;
+  }
   p.N = N;
   p.V = a->V;
   p.ignore_index = ignore_index;
@@ -468,9 +478,12 @@ VWS_API int vws_logprobs_topk_fwd(const vws_rows* z, const vws_ids_k* ids, int64
   if (!aligned(logp, 4)) return VWS_ELAYOUT;
   int64_t nk;
   if (!mul_ok(N, ids->K, &nk)) return VWS_EINVAL;
-  rc = fwd_common(VWS_OP_LOGPROBS, z, nullptr, nullptr, ignore_index, nullptr, stats, ws, ws_bytes, split_hint,
-                  stream, true);
-  if (rc) return rc;
+  // Unsplit rows with up to 256 slots: the forward writes the slots itself (their logits read
+  // before the row's stream); otherwise the statistics pass, then one gather launch.
+  const bool fused = parts_for(VWS_OP_LOGPROBS, N, z->V, split_hint) == 1 && ids->K <= kFwdTopkMaxK;
+  rc = fwd_common(VWS_OP_LOGPROBS, z, nullptr, nullptr, ignore_index, fused ? logp : nullptr, stats, ws, ws_bytes,
+                  split_hint, stream, !fused, false, fused ? ids : nullptr);
+  if (rc || fused) return rc;
   vws::TopkArgs p = topk_args(z, ids, N, ignore_index);
   p.stats = stats;
   p.out = logp;

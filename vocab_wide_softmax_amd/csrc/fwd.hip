@@ -109,23 +109,38 @@ __device__ __forceinline__ void update_kl(StateKL& st, const float (&xa)[U][8], 
 
 __device__ __forceinline__ double log_d(float S) { return log_unscaled(S); }
 
+// The target of a logprobs row, read before the row's stream and used after its merge: zt is the
+// target logit, NaN for an id outside [0, V); ign marks the ignored id.
+struct Target {
+  float zt;
+  bool ign;
+};
+
 template <int DT>
-__device__ void finalize1_logprobs(const FwdArgs& p, int64_t row, const State1& st) {
+__device__ __forceinline__ Target load_target(const FwdArgs& p, const char* ra, int64_t row, int32_t k) {
+  const int64_t ro = udiv(row, p.a.n_inner), ri = row - ro * p.a.n_inner;
+  const int64_t t = p.ids.data[ro * p.ids.s_outer + ri * p.ids.s_inner + (int64_t)k * p.ids_sk];
+  Target r{__builtin_nanf(""), t == p.ignore_index};
+  if (!r.ign && t >= 0 && t < p.V) r.zt = load_elem<DT>(ra, t);
+  return r;
+}
+
+__device__ __forceinline__ float logp_of(const Target& t, float m, double logS) {
+  return t.ign ? 0.0f : (float)(((double)t.zt - (double)m) - logS);
+}
+
+// Writes the row's statistics and, with one id per row, its log-probability (tgt: the target read
+// before the stream, or nullptr to read it here). Returns log S as stored.
+template <int DT>
+__device__ float finalize1_logprobs(const FwdArgs& p, int64_t row, const State1& st, const Target* tgt = nullptr) {
   const double logS = log_d(st.S);
   p.stats[2 * row + 0] = st.m;
   p.stats[2 * row + 1] = (float)logS;
-  if (p.out == nullptr) return;  // statistics only (the multi-id forward gathers its slots afterwards)
-  const int64_t t = load_id(p.ids, row, p.a.n_inner);
-  float out;
-  if (t == p.ignore_index) {
-    out = 0.0f;
-  } else if (t < 0 || t >= p.V) {
-    out = __builtin_nanf("");
-  } else {
-    const float zt = load_elem<DT>(row_ptr<DT>(p.a, row), t);
-    out = (float)(((double)zt - (double)st.m) - logS);
+  if (p.out != nullptr && p.K == 0) {  // else statistics only, or the K slots written after the merge
+    const Target t = tgt ? *tgt : load_target<DT>(p, row_ptr<DT>(p.a, row), row, 0);
+    p.out[row] = logp_of(t, st.m, logS);
   }
-  p.out[row] = out;
+  return (float)logS;
 }
 
 __device__ __forceinline__ void finalize1_entropy(const FwdArgs& p, int64_t row, const State1& st) {
@@ -228,6 +243,11 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs p) {
     }
   } else {
     constexpr bool WW = OP == kEntropy;
+    // logprobs, unsplit: the row's target logits (one, or K slots over the first K lanes) are
+    // loaded before the stream, so the row ends without a dependent load
+    const int32_t nslot = OP == kLogprobs && parts == 1 && p.out != nullptr ? (p.K > 0 ? p.K : 1) : 0;
+    Target tg{0.0f, true};
+    if (tid < nslot) tg = load_target<DT>(p, ra, row, tid);
     State1 st = state1_init();
     int32_t gb = g0 + tid;
     const int32_t nfull = VEC ? (min(g1, g_full) - g0) / (BLOCK * U) : 0;
@@ -253,6 +273,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs p) {
     }
     st = wave_reduce1<WW>(st);
     __shared__ State1 red[NW];
+    __shared__ float row_ml[2];  // (m, log S) of the row for the K-slot outputs
     if (lane == 0) red[wave] = st;
     __syncthreads();
     if (tid == 0) {
@@ -260,15 +281,23 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs p) {
 #pragma unroll
       for (int w = 1; w < NW; ++w) s = merge1<WW>(s, red[w]);
       if (parts == 1) {
-        if (OP == kEntropy) finalize1_entropy(p, row, s);
-        else finalize1_logprobs<DT>(p, row, s);
+        if (OP == kEntropy) {
+          finalize1_entropy(p, row, s);
+        } else {
+          row_ml[1] = finalize1_logprobs<DT>(p, row, s, &tg);
+          row_ml[0] = s.m;
+        }
       } else {
         float* o = p.ws + vb * 3;
         o[0] = s.m; o[1] = s.S; o[2] = s.W;
       }
     }
+    if (OP == kLogprobs && p.K > 0 && nslot > 0) {
+      __syncthreads();
+      if (tid < nslot) p.out[row * p.K + tid] = logp_of(tg, row_ml[0], (double)row_ml[1]);
+    }
   }
-  __syncthreads();  // red[] is reused by the next row
+  __syncthreads();  // red[] and row_ml[] are reused by the next row
   }
 }
 

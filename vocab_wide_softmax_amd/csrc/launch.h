@@ -32,6 +32,10 @@ struct FwdArgs {
   float* out;                      // [N]
   float* stats;                    // [N, 2] or [N, 4]
   float* ws;                       // [N, parts, 3 or 6] partial states when parts > 1
+  // multi-id logprobs in the unsplit forward: K ids per row (1 <= K <= 256) at
+  // ids[r_o * s_outer + r_i * s_inner + k * ids_sk], out [N, K]; K = 0 for one id (or none)
+  int64_t ids_sk;
+  int32_t K;
 };
 
 struct BwdArgs {

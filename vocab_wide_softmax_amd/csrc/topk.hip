@@ -11,9 +11,11 @@
 //              a row with every slot ignored gets a zero gradient, a row with
 //              any out-of-range live slot a NaN gradient.
 //
-// The forward reuses the single-read (m, S) pass of the logprobs forward, which
-// writes the row statistics; a gather kernel (one thread per slot) then forms
-// out[n, k]. The backward is one pass over the logits per (row, column tile),
+// The forward is the single-read (m, S) pass of the logprobs forward. When a row
+// is one workgroup (unsplit) and K <= 256 that pass writes out[n, k] itself:
+// lane k reads slot k's id and logit before the row's stream and forms its output
+// after the merge. Otherwise the pass writes the row statistics and the gather
+// kernel below (one thread per slot) forms out[n, k]. The backward is one pass over the logits per (row, column tile),
 // like the single-id backward. For K <= 64 each wave holds the row's slots one per
 // lane and works on them with ballots and lane reads; for larger K each workgroup
 // first collects, in slot order, the live ids that fall in its tile into LDS.
