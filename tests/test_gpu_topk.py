@@ -75,6 +75,15 @@ def test_topk_all_elements(device, dtype, v, K):
     _run_and_check(z.to(device), ids.to(device), g.to(device), z, ids, g, "v=%d K=%d" % (v, K))
 
 
+@pytest.mark.parametrize("K", [256, 257])
+def test_topk_slot_limit_of_the_fused_forward(device, K):
+    """Unsplit rows: K = 256 slots are written by the forward pass itself (one per lane), K = 257
+    by the statistics pass and the gather launch; every element against the oracle."""
+    z, ids, g = _case(40, 1024, K, seed=K, dtype=torch.bfloat16)
+    assert B.split_parts(B.OP_LOGPROBS, 40, 1024) == 1
+    _run_and_check(z.to(device), ids.to(device), g.to(device), z, ids, g, "K=%d" % K)
+
+
 @pytest.mark.parametrize("split", [3, 16])
 def test_topk_forced_split(device, split):
     z, ids, g = _case(12, 5000, 6, seed=5, dtype=torch.bfloat16)
