@@ -168,6 +168,34 @@ __device__ __forceinline__ void finalize_kl(const FwdArgs& p, int64_t row, const
   p.out[row] = out;
 }
 
+// fp32 groups of whole batches, loaded coalesced. A group is 32 bytes, so a lane loading its own
+// group's two 16-byte pieces makes each load of the wave cover every other piece of its 2 KB span.
+// Instead lane l loads pieces l and 64 + l of the span (one contiguous 1 KB per load), and two
+// exchanges give every lane its own group back: ds_permute sends piece s to lane s / 2 (even s)
+// or 32 + (s - 1) / 2 (odd s), then v_permlane32_swap trades lanes 32-63 of the first result
+// with lanes 0-31 of the second. Each lane ends up with the same 8 values as before, in order.
+// gw: the wave's first group (its lanes hold groups gw .. gw + 63).
+struct F32Span {
+  f32x4 a, b;
+};
+
+__device__ __forceinline__ F32Span load_span_f32(const char* row, int32_t gw, int lane) {
+  const f32x4* p = reinterpret_cast<const f32x4*>(row) + 2 * (int64_t)gw;
+  return F32Span{stream_load(p + lane), stream_load(p + 64 + lane)};
+}
+
+__device__ __forceinline__ void span_to_group(const F32Span& w, int lane, float (&x)[8]) {
+  const int dst = ((lane >> 1) + 32 * (lane & 1)) * 4;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int pa = __builtin_amdgcn_ds_permute(dst, __float_as_int(w.a[c]));
+    const int pb = __builtin_amdgcn_ds_permute(dst, __float_as_int(w.b[c]));
+    const auto r = __builtin_amdgcn_permlane32_swap(pa, pb, false, false);
+    x[c] = __int_as_float((int)r[0]);
+    x[4 + c] = __int_as_float((int)r[1]);
+  }
+}
+
 // ---- the streaming kernel -----------------------------------------------------------
 
 template <int OP, int DT, bool VEC, int BLOCK, int U>
@@ -195,18 +223,33 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs p) {
     const int32_t nfull = VEC ? (min(g1, g_full) - g0) / (BLOCK * U) : 0;
     for (int32_t it = 0; it < nfull; ++it, gb += BLOCK * U) {
       // all of the batch's loads in flight before any is used (one latency per batch)
-      RawGroup<DT> wa[U], wb[U];
-#pragma unroll
-      for (int k = 0; k < U; ++k) {
-        load_group_raw<DT>(ra, gb + k * BLOCK, wa[k]);
-        load_group_raw<DT>(rb, gb + k * BLOCK, wb[k]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
       float xa[U][8], xb[U][8];
+      if constexpr (DT == kF32) {
+        F32Span wa[U], wb[U];
 #pragma unroll
-      for (int k = 0; k < U; ++k) {
-        raw_to_float<DT>(wa[k], xa[k]);
-        raw_to_float<DT>(wb[k], xb[k]);
+        for (int k = 0; k < U; ++k) {
+          wa[k] = load_span_f32(ra, gb - lane + k * BLOCK, lane);
+          wb[k] = load_span_f32(rb, gb - lane + k * BLOCK, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          span_to_group(wa[k], lane, xa[k]);
+          span_to_group(wb[k], lane, xb[k]);
+        }
+      } else {
+        RawGroup<DT> wa[U], wb[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          load_group_raw<DT>(ra, gb + k * BLOCK, wa[k]);
+          load_group_raw<DT>(rb, gb + k * BLOCK, wb[k]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          raw_to_float<DT>(wa[k], xa[k]);
+          raw_to_float<DT>(wb[k], xb[k]);
+        }
       }
       update_kl<U>(st, xa, xb);
     }
@@ -253,8 +296,17 @@ __global__ __launch_bounds__(BLOCK) void fwd_kernel(FwdArgs p) {
     const int32_t nfull = VEC ? (min(g1, g_full) - g0) / (BLOCK * U) : 0;
     for (int32_t it = 0; it < nfull; ++it, gb += BLOCK * U) {
       float x[U][8];
+      if constexpr (DT == kF32) {
+        F32Span w[U];
 #pragma unroll
-      for (int k = 0; k < U; ++k) load_group_vec<DT>(ra, gb + k * BLOCK, x[k]);
+        for (int k = 0; k < U; ++k) w[k] = load_span_f32(ra, gb - lane + k * BLOCK, lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < U; ++k) span_to_group(w[k], lane, x[k]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < U; ++k) load_group_vec<DT>(ra, gb + k * BLOCK, x[k]);
+      }
       update1<WW, U>(st, x);
     }
     for (; gb < g1; gb += BLOCK * U) {
