@@ -23,6 +23,7 @@
 // product); rows where either input is undefined give NaN.
 #include "device.h"
 #include "launch.h"
+#include "span_f32.h"
 
 namespace vws {
 
@@ -160,19 +161,36 @@ __global__ __launch_bounds__(kJsdBlock) void jsd_div_kernel(JsdArgs p) {
     const int32_t nfull = VEC ? (min(g1, g_full) - g0) / (kJsdBlock * U) : 0;
     for (int32_t it = 0; it < nfull; ++it, gb += kJsdBlock * U) {
       // all of the batch's loads in flight before any is used
-      RawGroup<DT> ws_[U], wt_[U];
+      if constexpr (DT == kF32) {
+        F32Span ws_[U], wt_[U];
 #pragma unroll
-      for (int k = 0; k < U; ++k) {
-        load_group_raw<DT>(rs, gb + k * kJsdBlock, ws_[k]);
-        load_group_raw<DT>(rt, gb + k * kJsdBlock, wt_[k]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+        for (int k = 0; k < U; ++k) {
+          ws_[k] = load_span_f32(rs, gb - lane + k * kJsdBlock, lane);
+          wt_[k] = load_span_f32(rt, gb - lane + k * kJsdBlock, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int k = 0; k < U; ++k) {
-        float xs[8], xt[8];
-        raw_to_float<DT>(ws_[k], xs);
-        raw_to_float<DT>(wt_[k], xt);
-        accumulate(xs, xt);
+        for (int k = 0; k < U; ++k) {
+          float xs[8], xt[8];
+          span_to_group(ws_[k], lane, xs);
+          span_to_group(wt_[k], lane, xt);
+          accumulate(xs, xt);
+        }
+      } else {
+        RawGroup<DT> ws_[U], wt_[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          load_group_raw<DT>(rs, gb + k * kJsdBlock, ws_[k]);
+          load_group_raw<DT>(rt, gb + k * kJsdBlock, wt_[k]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          float xs[8], xt[8];
+          raw_to_float<DT>(ws_[k], xs);
+          raw_to_float<DT>(wt_[k], xt);
+          accumulate(xs, xt);
+        }
       }
     }
     for (; gb < g1; gb += kJsdBlock * U) {
