@@ -281,6 +281,47 @@ __device__ __forceinline__ void jsd_bwd_groups(const JsdRow& r, float Ks, float 
   }
 }
 
+// A whole fp32 tile: the gradients are elementwise (jsd_group decides its recomputed mixtures per
+// element), so lane l takes the tile's 16-byte pieces l, l + 256, ... instead of its groups of 8
+// columns, and every load and store of a wave covers one contiguous 1 KB. Two pieces form the 8
+// values one jsd_group call works on.
+__device__ __forceinline__ void jsd_bwd_tile_f32(const JsdRow& r, float Ks, float Kt, float gs, float gt,
+                                                 const char* rs, const char* rt, char* os, char* ot, int32_t g0) {
+  constexpr int NP = 2 * kJsdUB;  // pieces per lane
+  const int64_t q0 = 2 * (int64_t)g0 + threadIdx.x;
+  const float qnan = __builtin_nanf("");
+  f32x4 ps[NP], pt[NP];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    ps[k] = stream_load(reinterpret_cast<const f32x4*>(rs) + q0 + k * kJsdBlock);
+    pt[k] = stream_load(reinterpret_cast<const f32x4*>(rt) + q0 + k * kJsdBlock);
+  }
+#pragma unroll
+  for (int k = 0; k < NP; k += 2) {
+    float xs[8], xt[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xs[e] = ps[k][e];
+      xs[4 + e] = ps[k + 1][e];
+      xt[e] = pt[k][e];
+      xt[4 + e] = pt[k + 1][e];
+    }
+    JsdGroup q;
+    jsd_group<true>(r, xs, xt, q);
+    f32x4 ys[2], yt[2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ys[j >> 2][j & 3] = r.bad ? qnan : (mul0(q.ps[j], __builtin_fmaf(kLn2, q.us[j] - q.lm[j], -Ks)) * gs) * q.fs[j];
+      yt[j >> 2][j & 3] = r.bad ? qnan : (mul0(q.pt[j], __builtin_fmaf(kLn2, q.ut[j] - q.lm[j], -Kt)) * gt) * q.ft[j];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (os) stream_store(ys[h], reinterpret_cast<f32x4*>(os) + q0 + (k + h) * kJsdBlock);
+      if (ot) stream_store(yt[h], reinterpret_cast<f32x4*>(ot) + q0 + (k + h) * kJsdBlock);
+    }
+  }
+}
+
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kJsdBlock) void jsd_bwd_kernel(JsdArgs p) {
   constexpr int ES = ElemSize<DT>::value;
@@ -304,7 +345,9 @@ __global__ __launch_bounds__(kJsdBlock) void jsd_bwd_kernel(JsdArgs p) {
     char* os = p.ds ? p.ds + row * (int64_t)V * ES : nullptr;
     char* ot = p.dt ? p.dt + row * (int64_t)V * ES : nullptr;
     const int32_t g = g0 + threadIdx.x;
-    if (VEC && g0 + kJsdBlock * kJsdUB <= g_full)
+    if (DT == kF32 && VEC && g0 + kJsdBlock * kJsdUB <= g_full)
+      jsd_bwd_tile_f32(r, Ks, Kt, gs, gt, rs, rt, os, ot, g0);
+    else if (VEC && g0 + kJsdBlock * kJsdUB <= g_full)
       jsd_bwd_groups<DT, true>(r, Ks, Kt, gs, gt, rs, rt, os, ot, g, kJsdUB, G, V, g_full);
     else
       jsd_bwd_groups<DT, false>(r, Ks, Kt, gs, gt, rs, rt, os, ot, g, kJsdUB, G, V, g_full);
