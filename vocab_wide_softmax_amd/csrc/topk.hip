@@ -287,6 +287,72 @@ __device__ __forceinline__ void topk_small_tile(const TopkArgs& p, int64_t row, 
   }
 }
 
+// A whole fp32 tile of the small-K backward: the gradient is elementwise (a column adds the hits on
+// it in slot order), so lane l takes the tile's 16-byte pieces l, l + 256, ... instead of its
+// groups of 8 columns, and every load and store of a wave covers one contiguous 1 KB. Same slot
+// logic and arithmetic as topk_small_tile.
+template <int UB>
+__device__ __forceinline__ void topk_small_tile_f32(const TopkArgs& p, int64_t row, int32_t g0, int tid, int lane) {
+  constexpr int TG = kTopkBlock * UB;  // groups of 8 columns per tile
+  constexpr int NP = 2 * UB;           // 16-byte pieces per lane
+  const int32_t V = (int32_t)p.V;
+  const int32_t K = p.K;
+  const char* ra = row_ptr<kF32>(p.a, row);
+  const int64_t q0 = 2 * (int64_t)g0 + tid;  // this lane's first piece
+  int64_t tv = p.ignore_index;
+  float gl = 0.0f;
+  if (lane < K) {
+    tv = topk_id(p, row, lane);
+    gl = p.g[row * p.g_sr + (int64_t)lane * p.g_sk];
+  }
+  const float m = p.stats[2 * row], ls = p.stats[2 * row + 1];
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 x[NP];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) x[k] = stream_load(reinterpret_cast<const f32x4*>(ra) + q0 + k * kTopkBlock);
+  __builtin_amdgcn_sched_barrier(0);
+
+  const bool live = lane < K && tv != p.ignore_index;
+  const bool oor = live && (tv < 0 || tv >= V);
+  const bool in_tile = live && !oor && (tv >> 3) >= g0 && (tv >> 3) < g0 + TG;
+  const bool zero_row = __ballot(live) == 0ull, nan_row = __ballot(oor) != 0ull;
+  const uint64_t hits = __ballot(in_tile);
+  float Gs = live && !oor ? gl : 0.0f;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) Gs += __shfl_xor(Gs, off, 64);
+
+  float hu[NP][4];
+#pragma unroll
+  for (int k = 0; k < NP; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hu[k][e] = 0.0f;
+  for (uint64_t hm = hits; hm; hm &= hm - 1) {  // slot order
+    const int kk = __builtin_ctzll(hm);
+    const int32_t t = __builtin_amdgcn_readlane((int32_t)tv, kk);
+    const int32_t rel = (t >> 2) - 2 * g0;  // piece inside the tile
+    const float gk = lane_f(gl, kk);
+    const float add = (rel % kTopkBlock) == tid ? gk : 0.0f;
+#pragma unroll
+    for (int k = 0; k < NP; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (k == rel / kTopkBlock && e == (t & 3)) hu[k][e] += add;
+  }
+  char* oa = p.dz + row * (int64_t)V * 4;
+  const float qnan = __builtin_nanf("");
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    f32x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const PScaled pj = exp_split((x[k][e] - m) - ls);
+      const float d = __builtin_fmaf(-Gs * pj.p, pj.f, hu[k][e]);
+      y[e] = zero_row ? 0.0f : (nan_row ? qnan : d);
+    }
+    stream_store(y, reinterpret_cast<f32x4*>(oa) + q0 + k * kTopkBlock);
+  }
+}
+
 template <int DT, bool VEC, int UB>
 __global__ __launch_bounds__(kTopkBlock) void topk_bwd_small_kernel(TopkArgs p) {
   constexpr int TG = kTopkBlock * UB;  // groups of 8 columns per tile
@@ -298,7 +364,8 @@ __global__ __launch_bounds__(kTopkBlock) void topk_bwd_small_kernel(TopkArgs p) 
     const int64_t row = udiv(vb, tpr);
     const int32_t tile = (int32_t)(vb - row * tpr);
     const int32_t g0 = tile * TG;
-    if (VEC && g0 + TG <= g_full) topk_small_tile<DT, VEC, UB, true>(p, row, g0, tid, lane);
+    if (DT == kF32 && VEC && g0 + TG <= g_full) topk_small_tile_f32<UB>(p, row, g0, tid, lane);
+    else if (VEC && g0 + TG <= g_full) topk_small_tile<DT, VEC, UB, true>(p, row, g0, tid, lane);
     else topk_small_tile<DT, VEC, UB, false>(p, row, g0, tid, lane);
   }
 }
