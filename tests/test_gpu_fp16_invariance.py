@@ -73,8 +73,20 @@ def test_fp16_special_rows_and_splits(device, split):
 
 def test_fp16_forward_matches_fp32_bitwise(device):
     """The element -> lane map does not depend on the dtype: fp16 inputs and the same values
-    in fp32 give identical forward results, and the fp16 gradient is the RNE of the fp32 one."""
+    in fp32 give identical forward results, and the fp16 gradient is the RNE of the fp32 one.
+    At this width the fp32 forward loads its whole batches coalesced and regroups them across
+    lanes, so special values sit inside those batches too."""
     a, b, t, g = _pair(32, 75968, seed=5, scale=2.0)
+    a[0, 3000:3100] = NINF  # masked columns inside a whole batch
+    b[0, 3050:3200] = NINF  # some live A columns masked in B: KL = +inf
+    a[1, 9000] = float("nan")
+    b[2] = NINF  # B fully masked
+    a[3] = -60000.0  # one-hot row
+    a[3, 20001] = 60000.0
+    b[3] = a[3]
+    a[4] += 3e4  # large common offset
+    b[4] += 3e4
+    a[5, ::2] = NINF  # every other column masked
     a16, b16 = a.half(), b.half()
     for op in OPS:
         r16 = run_device(op, a16.to(device), b16.to(device), t.to(device), g.to(device))
