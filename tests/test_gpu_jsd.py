@@ -117,9 +117,12 @@ def test_jsd_near_endpoints(device):
         _check(s.to(device), t.to(device), g.to(device), s, t, g, beta, "beta=%g" % beta)
 
 
-def test_jsd_full_width(device):
-    s, t, g = _pair(48, 75968, seed=13, dtype=torch.bfloat16)
-    _check(s.to(device), t.to(device), g.to(device), s, t, g, 0.3, "full width", rows_chunk=8)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_jsd_full_width(device, dtype):
+    """Every element of 48 rows 75968 wide (special rows included): whole batches and tiles,
+    which on fp32 take the coalesced loads of the divergence pass and the backward."""
+    s, t, g = _pair(48, 75968, seed=13, dtype=dtype)
+    _check(s.to(device), t.to(device), g.to(device), s, t, g, 0.3, "full width %s" % dtype, rows_chunk=8)
 
 
 def test_jsd_endpoint_branches_equal_kl_calls(device):
