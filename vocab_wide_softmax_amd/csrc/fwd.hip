@@ -4,9 +4,13 @@
 // lane keeps the running state of device.h over the groups of 8 columns it
 // owns: group g of part [g0, g1) belongs to lane (g - g0) mod BLOCK, and a
 // lane takes its groups in increasing order, U groups per batch. The element
-// to lane map and the order of operations do not depend on the dtype, so bf16
-// and fp32 inputs holding the same values give bit-identical results (the
-// review comment on PR #8838 reports the same property for its patched kernels).
+// to lane map and the order of operations do not depend on the dtype (whole
+// fp32 batches are loaded coalesced and handed back to the same lanes,
+// span_f32.h), so bf16 and fp32 inputs holding the same values give
+// bit-identical results (the review comment on PR #8838 reports the same
+// property for its patched kernels). A logprobs row reads its target logits
+// (one id, or up to 256 top-k slots) before its stream and writes the
+// log-probabilities after the merge.
 //
 // Per batch the lane takes the batch max first and rescales its state once
 // (second commit message of PR #8838: when the max grows, the weighted sum is
