@@ -142,3 +142,40 @@ def test_topk_single_slot_matches_single_id_op(device):
     rep = compare.check(f64(dk), f64(d1).astype(np.float64), np.abs(f64(d1)) + 1e-30, "bf16")
     assert rep["nan_mismatch"] == 0 and rep["inf_mismatch"] == 0 and rep["fail"] == 0, rep
     assert torch.allclose(lpk[:, 0], lp1, rtol=2e-6, atol=2e-6, equal_nan=True)
+
+
+@pytest.mark.parametrize("split", [0, 4])
+def test_ignore_index_inside_the_vocabulary(device, split):
+    """ignore_index may name a real column: slots (and single targets) equal to it give 0 and no
+    gradient, other slots on that column's neighbours are ordinary. Unsplit rows take the forward's
+    own slot outputs, split rows the statistics pass and the gather launch."""
+    import oracle.reductions as R
+
+    ign = 7
+    n, v = 24, 9000
+    gen = torch.Generator().manual_seed(21)
+    z = 2.0 * torch.randn(n, v, generator=gen)
+    ids = torch.randint(0, v, (n, 5), generator=gen)
+    ids[0, 1] = ign
+    ids[1, :] = ign  # fully ignored row
+    ids[2, 3] = ign - 1
+    ids[3, 0] = ign + 1
+    g = torch.randn(n, 5, generator=gen)
+    zd, idd, gd = z.to(device), ids.to(device), g.to(device)
+    logp, stats = B.logprobs_topk_fwd(zd, idd, ign, split)
+    dz = B.logprobs_topk_bwd(zd, idd, stats, gd, ign)
+    torch.cuda.synchronize()
+    hz, hi, hg = f64(z), ids.numpy(), g.double().numpy()
+    out, _, _ = TK.logprobs_topk_fwd(hz, hi, ign)
+    _ok(compare.check(f64(logp), out, TK.cond_logprobs_topk_fwd(hz, hi, ign), "f32"), "top-k ign=7")
+    _ok(compare.check(f64(dz), TK.logprobs_topk_bwd(hz, hi, hg, ign), TK.cond_logprobs_topk_bwd(hz, hi, hg, ign),
+                      "f32"), "top-k ign=7 dz")
+    assert float(logp[0, 1]) == 0.0 and bool((logp[1] == 0).all())
+    # single target per row
+    t = ids[:, 0].contiguous()
+    lp1, st1 = B.logprobs_fwd(zd, t.to(device), ign, split)
+    d1 = B.logprobs_bwd(zd, t.to(device), st1, gd[:, 0].contiguous(), ign)
+    torch.cuda.synchronize()
+    o1, _, _ = R.logprobs_fwd(hz, t.numpy(), ignore_index=ign)
+    _ok(compare.check(f64(lp1), o1, R.cond_logprobs_fwd(hz, t.numpy(), ignore_index=ign), "f32"), "single ign=7")
+    assert float(lp1[1]) == 0.0 and bool((d1[1] == 0).all())
