@@ -198,14 +198,14 @@ def _timed(fwd, bwd, steps, warmup):
     return f[steps // 2], b[steps // 2]
 
 
-def extras_bench(wl, device, steps=15, warmup=30):
+def extras_bench(wl, device, steps=15, warmup=60):
     """The other ops on the same 8192 x 75968 pair, each fwd+bwd, with their algorithmic bytes:
     top-k logprobs (K = 16 ids per row), the generalized JSD (beta = 0.5: two reads of both
     inputs forward, one read of both and two writes backward), the four-op step on fp16 copies
     of the logits, and the four-op step in the batch-invariant split mode. These legs start right
     after their inputs' host-to-device copies, when the card runs its first few dozen sub-ms
     kernels slower (top-k backward 0.47 ms there, 0.39 ms afterwards); each leg therefore warms
-    up with 30 untimed calls before its 15 timed ones."""
+    up with 60 untimed calls before its 15 timed ones."""
     import torch
 
     from vocab_wide_softmax_amd import binding as B
