@@ -157,7 +157,7 @@ VWS_API int vws_logprobs_fwd(const vws_rows* z, const vws_ids* t, int64_t ignore
 
 /*
  * dz_j = g (1[j = t] - p_j) (RL-Kernel PR #208, review nitpick on the chunked
- * backward, which prints dz = -exp(logits - lse); dz[target] += 1; dz *= g).
+ * backward: the negated probabilities, one added at the target, scaled by g).
  *   stats   the [N, 2] stats written by vws_logprobs_fwd on the same z
  *   dz      out [N, V] contiguous, dtype of z
  */

@@ -109,8 +109,9 @@ def logprobs_fwd(z, t, ignore_index=-100):
 def logprobs_bwd(z, t, g, ignore_index=-100):
     """d logp_t / d z_j times g: g (1[j = t] - p_j).
 
-    This is the gradient printed in RL-Kernel PR #208 (review nitpick on the
-    chunked backward: dz = -exp(logits - lse); dz[target] += 1; dz *= g).
+    This is the gradient of RL-Kernel PR #208 (review nitpick on the chunked
+    backward: the negated probabilities, one added at the target column, all
+    scaled by the upstream gradient).
     Ignored rows are all zero; out-of-range targets and undefined rows NaN.
     """
     z = _f64(z)
