@@ -37,7 +37,7 @@
  *   exactly the stats its forward wrote (max-centred: m and log S are kept as
  *   two numbers, never folded into one log-sum-exp).
  * - Gradients are written contiguous [N, V] in the input dtype; a bf16 gradient
- *   is the round-to-nearest-even of the fp32 value (review comment on
+ *   is its fp32 value rounded to nearest, ties to even (review comment on
  *   PR #8838). `g` is the fp32 upstream gradient, element r at g[r * g_stride]
  *   (g_stride = 0 broadcasts one value, as an expanded scalar does).
  * - Outputs must not alias inputs.
@@ -86,9 +86,9 @@ enum { VWS_SPLIT_INVARIANT = -1 };
 typedef enum vws_op { VWS_OP_LOGPROBS = 0, VWS_OP_ENTROPY = 1, VWS_OP_KL = 2, VWS_OP_JSD = 3 } vws_op;
 
 /*
- * A logical [N, V] matrix of logits whose rows are addressed with up to two
- * strides, so that a slice such as logits[:, :-1, :] is read in place (second
- * commit message of PR #8838). Row r = r_o * n_inner + r_i (0 <= r_i < n_inner)
+ * A logical [N, V] matrix of logits. Row addresses take an outer and an inner
+ * stride, which lets a causal-shift view like logits[:, :-1, :] be read where it
+ * lies, without a copy (second commit message of PR #8838). Row r = r_o * n_inner + r_i (0 <= r_i < n_inner)
  * starts at element  r_o * s_outer + r_i * s_inner  of `data`; columns are
  * contiguous (col_stride must be 1; other layouts are copied by the caller).
  * Strides are in elements and must be >= 0. `data` must be aligned to the
@@ -165,9 +165,9 @@ VWS_API int vws_logprobs_bwd(const vws_rows* z, const vws_ids* t, int64_t ignore
                              const float* g, int64_t g_stride, void* dz, void* stream);
 
 /*
- * Multi-id (top-k) log-probabilities: K target ids per row (PR #8838 lists
- * duplicate and ignored top-k ids and a fully ignored row among its logprobs
- * test cases).
+ * Multi-id (top-k) log-probabilities: K target ids per row (the logprobs test
+ * cases of PR #8838 include repeated ids, ignored ids and rows whose ids are all
+ * ignored).
  *   ids     K ids per row (vws_ids_k); a slot equal to ignore_index gives 0,
  *           any other slot outside [0, V) gives NaN
  *   logp    out fp32 [N, K] contiguous: logp[r, k] = (z_id - m) - log S

@@ -1,8 +1,8 @@
 """fp64 definition of multi-id (top-k) log-probabilities (test infrastructure only).
 
 Source: DeepSpeed PR #8838 "Add Triton kernels for vocab-parallel logprobs,
-entropy and KL" -- the PR description's test list names duplicate and ignored
-top-k ids and a fully ignored row among the logprobs cases, so the logprobs op
+entropy and KL" -- the logprobs cases in the PR description's test list include
+repeated ids, ignored ids and rows whose ids are all ignored, so the logprobs op
 takes K ids per row.
 
 Reading taken (the pages list the cases, not the values):

@@ -1,7 +1,7 @@
 """GPU parity of the multi-id (top-k) logprobs against the fp64 oracle, through the C ABI.
 
-Cases (the pages' test list names duplicate and ignored top-k ids and a fully
-ignored row): duplicates, ignored slots, a fully ignored row, an out-of-range
+Cases (the pages' test list includes repeated ids, ignored ids and rows with every
+id ignored): duplicates, ignored slots, a fully ignored row, an out-of-range
 slot (NaN logp, NaN gradient row), a target on a masked column, a +1e4 row,
 ragged V, the element-wise (unaligned) load path, forced vocabulary splits, a
 3-D [B, S, V] view with strided ids, a broadcast upstream gradient, the largest

@@ -1,8 +1,8 @@
 // topk.hip -- multi-id (top-k) log-probabilities: K target ids per row.
 //
-// DeepSpeed PR #8838 "Add Triton kernels for vocab-parallel logprobs, entropy
-// and KL" lists duplicate and ignored top-k ids and a fully ignored row among
-// its logprobs test cases. With ids[n, k] (k < K) and upstream g[n, k]:
+// Among the logprobs test cases of DeepSpeed PR #8838 "Add Triton kernels for
+// vocab-parallel logprobs, entropy and KL" are repeated ids, ignored ids and
+// rows whose ids are all ignored. With ids[n, k] (k < K) and upstream g[n, k]:
 //
 //   forward    out[n, k] = (z_id - m) - log S          (0 for ignore_index,
 //                                                        NaN outside [0, V))
