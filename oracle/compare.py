@@ -9,8 +9,8 @@ Tolerances (stated for this path; the pages report errors, not a rule):
 * bf16 outputs pass when
     |x - rne(y)| <= ulp_bf16(rne(y))                     (strict), or
     |x - y| <= ulp_bf16(rne(y)) + 64 eps32 c             (conditioned),
-  with rne the round-to-nearest-even of y to bf16 (the bf16 gradient is the
-  RNE of the fp32 value, as the review comment of PR #8838 observes).
+  with rne(y) the bf16 value nearest to y, ties to even (a bf16 gradient is its
+  fp32 value rounded that way, as the review comment of PR #8838 observes).
 * fp16 outputs pass by the bf16 rule with fp16 rounding and spacing
     (|x - rne16(y)| <= ulp_f16(rne16(y)), or the conditioned form).
 * NaN positions must match exactly, and so must +inf / -inf positions.

@@ -5,7 +5,8 @@ Source: the JSD pull request whose text is pasted into DeepSpeed PR #8838
 ``jsd(student_logits, teacher_logits, beta)`` for GKD-style distillation,
 fp32 per token, gradients to both inputs, beta = 0 selecting forward KL and
 beta = 1 reverse KL as explicit endpoint branches, interior 0 < beta < 1
-computed from the two KL-to-mixture expectations after a statistics pass.
+computed, after a pass that gathers each input's statistics, from the KL of
+each input to the mixture.
 
 Reading taken (the page does not print the mixture): the generalized JSD of
 GKD-style distillation that the page names, with S = student, T = teacher,

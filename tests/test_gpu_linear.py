@@ -2,7 +2,7 @@
 
 Every comparison uses the standard rule of oracle.compare (fp32 outputs within 2e-5
 relative or 64 eps32 c; bf16 gradients within one bf16 ulp of the oracle's RNE value or
-that plus 64 eps32 c; NaN / inf in the same places), with the worst error-to-allowance
+that plus 64 eps32 c; NaN / inf positions equal), with the worst error-to-allowance
 ratio asserted <= 1 and the strict misses printed:
 
 * small ragged shape (300 tokens, hidden 200, vocabulary 3000: partial tiles in
