@@ -25,6 +25,7 @@ the strict-rule misses per op and config.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --calibrate          # plain copies of known size, for counter scaling
+    python bench.py --reference-rates    # torch's own streaming kernels at the headline size, as context
     python bench.py --summarize DIR stats|counters   # condense rocprofv3 output for profiles/
     python bench.py --counters FETCH WRITE CALFETCH CALWRITE   # calibrated HBM bytes per kernel
 """
@@ -730,6 +731,42 @@ def calibrate(device):
     print(json.dumps({"calibration_copy_bytes_each_way": T_BYTES, "launches": 5}))
 
 
+def reference_rates(device, reps=20):
+    """HBM rates of torch's own streaming kernels on one bf16 [8192, 75968] tensor (T bytes), as
+    context for the roofline fractions: an elementwise multiply (read T, write T), a device copy
+    (hipMemcpy, read T, write T), a fill (write T) and an elementwise multiply of two tensors (read
+    2 T, write T). Medians of `reps` launches timed with HIP events."""
+    import torch
+
+    n = T_BYTES // 2
+    a = torch.empty(n, dtype=torch.bfloat16, device=device).normal_()
+    b = torch.empty_like(a).normal_()
+    c = torch.empty_like(a)
+    torch.cuda.synchronize()
+
+    def med(fn):
+        for _ in range(5):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        s = torch.cuda.current_stream()
+        for x, y in ev:
+            x.record(s)
+            fn()
+            y.record(s)
+        torch.cuda.synchronize()
+        return sorted(x.elapsed_time(y) for x, y in ev)[reps // 2]
+
+    out = {}
+    for name, fn, nbytes in (("mul_scalar_read_write", lambda: torch.mul(a, 2.0, out=c), 2 * T_BYTES),
+                             ("device_copy_read_write", lambda: c.copy_(a), 2 * T_BYTES),
+                             ("fill_write", lambda: c.fill_(1.0), T_BYTES),
+                             ("mul_two_inputs_read2_write1", lambda: torch.mul(a, b, out=c), 3 * T_BYTES)):
+        ms = med(fn)
+        out[name] = {"ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "pct_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / PEAK_GBS, 1)}
+    print(json.dumps({"reference_rates_bf16_8192x75968": out}))
+
+
 # -------------------------------------------------------------------- profile summaries
 
 def _rocpd(outdir):
@@ -942,6 +979,8 @@ def main():
     ap.add_argument("--library-gemm", action="store_true",
                     help="also time torch's bf16 GEMM (hipBLASLt) on the linear-logp products, as context")
     ap.add_argument("--calibrate", action="store_true")
+    ap.add_argument("--reference-rates", action="store_true",
+                    help="only time torch's own streaming kernels on the headline tensor size, as context")
     ap.add_argument("--summarize", nargs=2, metavar=("DIR", "MODE"))
     ap.add_argument("--counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"))
     ap.add_argument("--counters-raw", nargs=4, metavar=("RD_DIR", "WR_DIR", "CAL_RD_DIR", "CAL_WR_DIR"),
@@ -971,6 +1010,9 @@ def main():
     device = torch.device("cuda:0")
     if args.calibrate:
         calibrate(device)
+        return
+    if args.reference_rates:
+        reference_rates(device)
         return
 
     log("generating the 8192x75968 bf16 pair on the host")
