@@ -342,7 +342,7 @@ def memory_report(ops, a, b, t, g):
 
 
 def pair1024_leg(device, steps, warmup, wl=None):
-    """The 1024 x 75968 bf16 pair (config 1: the shape of one tensor-parallel rank of a 151936-token
+    """The 1024 x 75968 bf16 pair (the shape of one of two tensor-parallel ranks of a 151936-token
     vocabulary): the four ops fwd+bwd, timed as they are (inputs of 156 MB each can sit in the
     256 MB Infinity Cache) and with the cache flushed before every op. The automatic launch does
     not split the vocabulary at 1024 rows (one workgroup per row already fills the chip; split
@@ -380,7 +380,7 @@ def pair1024_leg(device, steps, warmup, wl=None):
 
 
 def shifted_leg(device, steps, warmup, wl=None):
-    """Config 3: fp32 logits of two bases [4, 2049, 75968] read in place through the causal-shift
+    """fp32 logits of two bases [4, 2049, 75968] read in place through the causal-shift
     view base[:, :-1, :] (8192 rows, two row strides, no copy): entropy(A) and KL(A||B) fwd+bwd
     (gradients fp32, contiguous), with the extra peak memory of each."""
     import torch
@@ -648,11 +648,11 @@ def oracle_parity(device, wls, lin_wl, with_dw=True):
     from vocab_wide_softmax_amd import workloads as W
 
     out = {}
-    cases = (("config0_tiny_64x1024_fp32", "tiny", W.OPS, "f32", None, 0),
-             ("config0_tiny_64x1024_fp32_split16", "tiny", W.OPS, "f32", None, 16),
-             ("config1_pair1024_bf16", "pair1024", W.OPS, "bf16", 24, 0),
-             ("config2_pair8192_bf16", "pair8192", W.OPS, "bf16", 24, 0),
-             ("config3_shifted_fp32", "shifted", ("entropy", "kl_ab"), "f32", 12, 0))
+    cases = (("tiny_64x1024_fp32", "tiny", W.OPS, "f32", None, 0),
+             ("tiny_64x1024_fp32_split16", "tiny", W.OPS, "f32", None, 16),
+             ("pair_1024x75968_bf16", "pair1024", W.OPS, "bf16", 24, 0),
+             ("pair_8192x75968_bf16", "pair8192", W.OPS, "bf16", 24, 0),
+             ("shifted_fp32_4x2049x75968", "shifted", ("entropy", "kl_ab"), "f32", 12, 0))
     for label, key, ops, kind, k, split in cases:
         wl = wls[key]
         if wl.shifted:
@@ -689,7 +689,7 @@ def oracle_parity(device, wls, lin_wl, with_dw=True):
         del a, b, t
         torch.cuda.empty_cache()
         log("parity %s done" % label)
-    # config 4: the fused linear-logp in the benchmark's launch
+    # the fused linear-logp (8192 x 4096 x 151936) in the benchmark's launch
     h, Wm, t, g = lin_wl.h.to(device), lin_wl.W.to(device), lin_wl.t.to(device), lin_wl.g.to(device)
     lp, st = B.linear_logp_fwd(h, Wm, t)
     dh, dW = B.linear_logp_bwd(h, Wm, t, st, g)
@@ -709,7 +709,7 @@ def oracle_parity(device, wls, lin_wl, with_dw=True):
         ref, c = OL.linear_logp_bwd_dw_cond(hh, hw, ht, hg, vocab_rows=cols)
         r["dW"] = _rep(dW[torch.from_numpy(cols).to(device)].double().cpu().numpy(), ref, c, "bf16")
         r["dW_vocab_rows_compared"] = int(len(cols))
-    out["config4_linear_logp_8192x4096x151936_bf16"] = r
+    out["linear_logp_8192x4096x151936_bf16"] = r
     del h, Wm, t, g, lp, st, dh, dW
     torch.cuda.empty_cache()
     return out
