@@ -169,14 +169,13 @@ __device__ __forceinline__ void elem_grad(const RowBwd& r, float xa, float xb, b
   }
 }
 
-// A whole fp32 tile (columns [8 g0, 8 (g0 + BLOCK UB))): the backward is elementwise, so instead of
-// a lane's group of 8 columns (32 bytes, two 16-byte accesses that each cover every other 16-byte
-// piece of the wave's span) lane l takes 16-byte pieces l, l + BLOCK, ...: every access of the
-// wave covers one contiguous 1 KB.
-template <int OP, int BLOCK, int UB>
+// A whole fp32 tile of NP BLOCK 16-byte pieces (columns [8 g0, 8 g0 + 4 NP BLOCK)): the backward is
+// elementwise, so instead of a lane's group of 8 columns (32 bytes, two 16-byte accesses that each
+// cover every other 16-byte piece of the wave's span) lane l takes 16-byte pieces l, l + BLOCK, ...:
+// every access of the wave covers one contiguous 1 KB.
+template <int OP, int BLOCK, int NP>
 __device__ __forceinline__ void bwd_tile_f32(const BwdArgs& p, int64_t row, const char* ra, const char* rb, char* oa,
                                              char* ob, int32_t g0, int32_t V) {
-  constexpr int NP = 2 * UB;
   const int64_t q0 = 2 * (int64_t)g0 + threadIdx.x;  // this lane's first piece
   f32x4 xa[NP], xb[OP == kKL ? NP : 1];
 #pragma unroll
@@ -204,8 +203,11 @@ __device__ __forceinline__ void bwd_tile_f32(const BwdArgs& p, int64_t row, cons
   }
 }
 
-template <int OP, int DT, bool VEC, int BLOCK, int UB>
+// TG: groups of 8 columns per tile. The group path covers a tile with UB groups a lane (TG =
+// BLOCK UB on 16-bit data); whole fp32 tiles take 2 TG / BLOCK 16-byte pieces a lane.
+template <int OP, int DT, bool VEC, int BLOCK, int UB, int TG>
 __global__ __launch_bounds__(BLOCK) void bwd_kernel(BwdArgs p) {
+  static_assert(TG <= BLOCK * UB && (2 * TG) % BLOCK == 0, "tile");
   constexpr int ES = ElemSize<DT>::value;
   const int32_t tpr = p.tiles_per_row;
   const int64_t total = p.N * tpr;
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_kernel(BwdArgs p) {
   for (int64_t vb = blockIdx.x; vb < total; vb += gridDim.x) {
     const int64_t row = udiv(vb, tpr);
     const int32_t tile = (int32_t)(vb - row * tpr);
-    const int32_t g0 = tile * (BLOCK * UB);
+    const int32_t g0 = tile * TG;
     const char* ra = row_ptr<DT>(p.a, row);
     const char* rb = OP == kKL ? row_ptr<DT>(p.b, row) : nullptr;
     char* oa = p.da ? p.da + row * (int64_t)V * ES : nullptr;
@@ -223,12 +225,12 @@ __global__ __launch_bounds__(BLOCK) void bwd_kernel(BwdArgs p) {
     const int32_t g = g0 + threadIdx.x;
     float xa[UB][8], xb[OP == kKL ? UB : 1][8];
     if constexpr (DT == kF32 && VEC) {
-      if (g0 + BLOCK * UB <= g_full) {
-        bwd_tile_f32<OP, BLOCK, UB>(p, row, ra, rb, oa, ob, g0, V);
+      if (g0 + TG <= g_full) {
+        bwd_tile_f32<OP, BLOCK, 2 * TG / BLOCK>(p, row, ra, rb, oa, ob, g0, V);
         continue;
       }
     }
-    if (VEC && g0 + BLOCK * UB <= g_full) {
+    if (VEC && TG == BLOCK * UB && g0 + TG <= g_full) {
       // the whole tile's loads first, then the row constants: one memory latency per tile
       RawGroup<DT> wa[UB], wb[OP == kKL ? UB : 1];
 #pragma unroll
@@ -245,10 +247,12 @@ __global__ __launch_bounds__(BLOCK) void bwd_kernel(BwdArgs p) {
       }
       bwd_store<OP, DT, true, BLOCK, UB>(r, xa, xb_ref<OP, UB>(xa, xb), oa, ob, g, G, V, g_full);
     } else {
+      // groups of this tile only (lanes past a narrower tile's end take none)
+      const int32_t gt = min(G, g0 + TG);
       const RowBwd r = row_consts<OP>(p, row, V);
-      bwd_load<DT, false, BLOCK, UB>(ra, g, G, V, g_full, xa);
-      if constexpr (OP == kKL) bwd_load<DT, false, BLOCK, UB>(rb, g, G, V, g_full, xb);
-      bwd_store<OP, DT, false, BLOCK, UB>(r, xa, xb_ref<OP, UB>(xa, xb), oa, ob, g, G, V, g_full);
+      bwd_load<DT, false, BLOCK, UB>(ra, g, gt, V, g_full, xa);
+      if constexpr (OP == kKL) bwd_load<DT, false, BLOCK, UB>(rb, g, gt, V, g_full, xb);
+      bwd_store<OP, DT, false, BLOCK, UB>(r, xa, xb_ref<OP, UB>(xa, xb), oa, ob, g, gt, V, g_full);
     }
   }
 }
@@ -259,15 +263,19 @@ constexpr int kBwdBlock = 256;
 // on 16-bit data (4096-column tiles), 1 for KL, which reads two inputs, and for fp32 data
 // (2048-column tiles; on fp32 the single-input ops ran 11% slower with 2, KL 7% slower with 2).
 constexpr int bwd_ub(int op, int dt) { return op == kKL || dt == kF32 ? 1 : 2; }
-// Lanes per workgroup: 256, and 128 for fp32 KL (1024-column tiles, one 16-byte piece per input
-// and lane; 1.8% faster there than 256).
-constexpr int bwd_block(int op, int dt) { return op == kKL && dt == kF32 ? 128 : kBwdBlock; }
+// Lanes per workgroup: 256.
+constexpr int bwd_block(int, int) { return kBwdBlock; }
+// Groups per tile: BLOCK UB, except fp32 KL, whose 1024-column tiles give every lane one 16-byte
+// piece per input and gradient, as 16-bit KL tiles do (fp32 KL backward 1.71 -> 1.58 ms on the
+// 8192-row causal-shift view against 128-lane workgroups of two pieces a lane; 64 lanes and
+// looping over several tiles were slower still).
+constexpr int bwd_tile_groups(int op, int dt) { return op == kKL && dt == kF32 ? kBwdBlock / 2 : kBwdBlock * bwd_ub(op, dt); }
 
 template <int OP, int DT, bool VEC>
 hipError_t launch_bwd_t(const BwdArgs& p, hipStream_t stream) {
   const int64_t blocks = grid_cap(p.N * p.tiles_per_row);
-  hipLaunchKernelGGL((bwd_kernel<OP, DT, VEC, bwd_block(OP, DT), bwd_ub(OP, DT)>), dim3((uint32_t)blocks), dim3(bwd_block(OP, DT)), 0,
-                     stream, p);
+  hipLaunchKernelGGL((bwd_kernel<OP, DT, VEC, bwd_block(OP, DT), bwd_ub(OP, DT), bwd_tile_groups(OP, DT)>),
+                     dim3((uint32_t)blocks), dim3(bwd_block(OP, DT)), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -282,7 +290,7 @@ hipError_t launch_bwd_op(const BwdArgs& p, int dtype, bool vec, hipStream_t stre
 
 int32_t bwd_tiles_per_row(int op, int dtype, int64_t V) {
   const int64_t G = (V + 7) / 8;
-  const int64_t per = (int64_t)bwd_block(op, dtype) * bwd_ub(op, dtype);
+  const int64_t per = bwd_tile_groups(op, dtype);
   return (int32_t)((G + per - 1) / per);
 }
 
