@@ -577,7 +577,7 @@ VWS_API int vws_jsd_bwd(const vws_rows* s, const vws_rows* t, float beta, const 
   if (!aligned(stats, 4) || !aligned(g, 4) || !aligned(ds, es) || !aligned(dt, es)) return VWS_ELAYOUT;
   int64_t nv, bytes;
   if (!mul_ok(N, s->V, &nv) || !mul_ok(nv, es, &bytes)) return VWS_EINVAL;
-  const int32_t tpr = vws::jsd_tiles_per_row(s->V);
+  const int32_t tpr = vws::jsd_tiles_per_row(s->V, s->dtype);
   if (N * (int64_t)tpr > (int64_t)INT32_MAX) return VWS_EINVAL;
   vws::JsdArgs p{};
   p.s = rows_dev(s);

@@ -89,7 +89,7 @@ struct JsdArgs {
   char* dt;  // [N, V] contiguous, may be null
 };
 
-int32_t jsd_tiles_per_row(int64_t V);
+int32_t jsd_tiles_per_row(int64_t V, int dtype);
 hipError_t launch_jsd_div(const JsdArgs& p, int dtype, bool vec, hipStream_t stream);
 hipError_t launch_jsd_bwd(const JsdArgs& p, int dtype, bool vec, hipStream_t stream);
 
