@@ -504,7 +504,7 @@ VWS_API int vws_logprobs_topk_bwd(const vws_rows* z, const vws_ids_k* ids, int64
   if (!aligned(stats, 4) || !aligned(g, 4) || !aligned(dz, es)) return VWS_ELAYOUT;
   int64_t nv, bytes;
   if (!mul_ok(N, z->V, &nv) || !mul_ok(nv, es, &bytes)) return VWS_EINVAL;
-  const int32_t tpr = vws::topk_tiles_per_row(z->V, (int32_t)ids->K);
+  const int32_t tpr = vws::topk_tiles_per_row(z->V, (int32_t)ids->K, z->dtype);
   if (N * (int64_t)tpr > (int64_t)INT32_MAX) return VWS_EINVAL;
   vws::TopkArgs p = topk_args(z, ids, N, ignore_index);
   p.tiles_per_row = tpr;

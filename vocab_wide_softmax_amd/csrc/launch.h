@@ -69,7 +69,7 @@ struct TopkArgs {
   char* dz;  // [N, V] contiguous, dtype of the logits
 };
 
-int32_t topk_tiles_per_row(int64_t V, int32_t K);
+int32_t topk_tiles_per_row(int64_t V, int32_t K, int dtype);
 hipError_t launch_topk_gather(const TopkArgs& p, int dtype, hipStream_t stream);
 hipError_t launch_topk_bwd(const TopkArgs& p, int dtype, bool vec, hipStream_t stream);
 
