@@ -301,9 +301,10 @@ VWS_API int vws_jsd_bwd(const vws_rows* s, const vws_rows* t, float beta, const 
  *           (pass 0: forward, 1: backward), 256-byte aligned. The backward's holds one
  *           chunk's dz pair, 2 x N x chunk x 2 bytes, plus the fp32 sum of dh, N x H x 4
  *           bytes, when V spans more than one chunk (0.40 GB at 8192 x 4096 x 151936).
- *   split_hint  forward: vocabulary chunking as for the logits ops: 0 automatic (about two
- *           workgroups per CU for this N; the order in which a token's chunk partials
- *           merge then follows the batch size), k >= 1 k chunks, VWS_SPLIT_INVARIANT
+ *   split_hint  forward: vocabulary chunking as for the logits ops: 0 automatic (the
+ *           chunking that spreads the (token tile, vocabulary tile) products most evenly
+ *           over the CUs for this N; the order in which a token's chunk partials merge
+ *           then follows the batch size), k >= 1 k chunks, VWS_SPLIT_INVARIANT
  *           chunks of 1024 columns. The last two depend on V alone: a token's logp and
  *           stats are then the same bits in every batch (batch invariance); < -1 is
  *           VWS_EINVAL.
