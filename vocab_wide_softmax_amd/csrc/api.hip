@@ -115,8 +115,20 @@ int state_floats(int op) { return op == VWS_OP_KL ? 6 : 3; }
 // Segment length (in groups of 8 columns) of the batch-invariant split: 32768 columns.
 constexpr int64_t kInvariantGroups = 4096;
 
-// Most slots the unsplit forward writes itself (one per lane of its 256-lane workgroup).
+// Most slots the unsplit forward writes itself (one per lane of its first 256 lanes).
 constexpr int64_t kFwdTopkMaxK = 256;
+
+// Forward workgroup width: 512 lanes in the automatic split from kFwdWideRows rows up (rows are
+// then never split), 256 otherwise. Measured at V = 75968 bf16 (one-card A/Bs, Infinity Cache
+// flushed before each launch, us, 256 -> 512 lanes): 2048 rows logprobs / entropy / KL 57.3 /
+// 64.3 / 111.1 -> 54.9 / 56.5 / 104.7, 8192 rows 195 / 196 / 382 -> 193 / 192 / 371, and the
+// four-op step 3.50-3.53 -> 3.48-3.49 ms on three cards; at 1024 rows 32.7 / 34.8 / 57.8 ->
+// 34.2 / 33.9 / 59.4, so small batches keep 256, and so do the fixed splits, whose 32768-column
+// segments leave a 512-lane workgroup two batches a lane (the invariant step 3.56 -> 3.80 ms).
+// The width sets a row's element-to-lane map: a fixed split (VWS_SPLIT_INVARIANT, split_hint >= 1)
+// always takes 256 lanes, so its bits still depend on V alone.
+constexpr int64_t kFwdWideRows = 2048;
+bool fwd_wide(int64_t N, int split_hint) { return split_hint == 0 && N >= kFwdWideRows; }
 
 // Vocabulary parts per row for the forward (see vws_split_parts in vws.h).
 int parts_for(int op, int64_t N, int64_t V, int hint) {
@@ -205,7 +217,7 @@ int fwd_common(int op, const vws_rows* a, const vws_rows* b, const vws_ids* t, i
   p.stats = stats;
   p.ws = static_cast<float*>(ws);
   const bool vec = rows_vec_ok(a) && (op != VWS_OP_KL || rows_vec_ok(b));
-  hipError_t e = vws::launch_fwd(op, p, a->dtype, vec, static_cast<hipStream_t>(stream));
+  hipError_t e = vws::launch_fwd(op, p, a->dtype, vec, fwd_wide(N, split_hint), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? VWS_OK : VWS_EHIP;
 }
 

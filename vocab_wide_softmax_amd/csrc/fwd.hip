@@ -1,6 +1,7 @@
 // fwd.hip -- single-read forward of logprobs, entropy and KL(A||B).
 //
-// One workgroup streams one row (or one vocabulary part of one row). Each
+// One workgroup of 512 lanes (large batches in the automatic split) or 256
+// streams one row (or one vocabulary part of one row). Each
 // lane keeps the running state of device.h over the groups of 8 columns it
 // owns: group g of part [g0, g1) belongs to lane (g - g0) mod BLOCK, and a
 // lane takes its groups in increasing order, U groups per batch. The element
@@ -356,16 +357,17 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdArgs p) {
 // ---- host-side launch -----------------------------------------------------------------
 
 namespace {
-constexpr int kFwdBlock = 256;
+// Workgroup widths: 512 lanes (wide) or 256. The lane count fixes the element-to-lane map and so
+// a row's rounding; the host picks it (fwd_wide in the ABI layer) from the split mode and N only.
+constexpr int kFwdBlockWide = 512, kFwdBlockNarrow = 256;
 // Groups of 8 columns per lane per batch: 4 for one input, 2 for KL's two (the same bytes
 // in flight per batch; the fastest by measurement).
 constexpr int fwd_u(int op) { return op == kKL ? 2 : 4; }
 
-template <int OP, int DT, bool VEC>
+template <int OP, int DT, bool VEC, int BLOCK>
 hipError_t launch_fwd_t(const FwdArgs& p, hipStream_t stream) {
   const int64_t blocks = grid_cap(p.N * p.parts);
-  hipLaunchKernelGGL((fwd_kernel<OP, DT, VEC, kFwdBlock, fwd_u(OP)>), dim3((uint32_t)blocks), dim3(kFwdBlock), 0,
-                     stream, p);
+  hipLaunchKernelGGL((fwd_kernel<OP, DT, VEC, BLOCK, fwd_u(OP)>), dim3((uint32_t)blocks), dim3(BLOCK), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.parts == 1) return e;
   hipLaunchKernelGGL((combine_kernel<OP, DT>), dim3((uint32_t)grid_cap((p.N + 255) / 256)), dim3(256), 0, stream, p);
@@ -373,19 +375,23 @@ hipError_t launch_fwd_t(const FwdArgs& p, hipStream_t stream) {
 }
 
 template <int OP>
-hipError_t launch_fwd_op(const FwdArgs& p, int dtype, bool vec, hipStream_t stream) {
+hipError_t launch_fwd_op(const FwdArgs& p, int dtype, bool vec, bool wide, hipStream_t stream) {
   return dispatch_dtype(dtype, [&](auto dt) {
     constexpr int DT = decltype(dt)::value;
-    return vec ? launch_fwd_t<OP, DT, true>(p, stream) : launch_fwd_t<OP, DT, false>(p, stream);
+    if (wide)
+      return vec ? launch_fwd_t<OP, DT, true, kFwdBlockWide>(p, stream)
+                 : launch_fwd_t<OP, DT, false, kFwdBlockWide>(p, stream);
+    return vec ? launch_fwd_t<OP, DT, true, kFwdBlockNarrow>(p, stream)
+               : launch_fwd_t<OP, DT, false, kFwdBlockNarrow>(p, stream);
   });
 }
 }  // namespace
 
-hipError_t launch_fwd(int op, const FwdArgs& p, int dtype, bool vec, hipStream_t stream) {
+hipError_t launch_fwd(int op, const FwdArgs& p, int dtype, bool vec, bool wide, hipStream_t stream) {
   switch (op) {
-    case kLogprobs: return launch_fwd_op<kLogprobs>(p, dtype, vec, stream);
-    case kEntropy: return launch_fwd_op<kEntropy>(p, dtype, vec, stream);
-    default: return launch_fwd_op<kKL>(p, dtype, vec, stream);
+    case kLogprobs: return launch_fwd_op<kLogprobs>(p, dtype, vec, wide, stream);
+    case kEntropy: return launch_fwd_op<kEntropy>(p, dtype, vec, wide, stream);
+    default: return launch_fwd_op<kKL>(p, dtype, vec, wide, stream);
   }
 }
 

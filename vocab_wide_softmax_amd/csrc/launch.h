@@ -141,7 +141,8 @@ hipError_t launch_lin_bwd(LinArgs p, int split_hint, uint16_t* dh, uint16_t* dW,
 // keeps grid size x workgroup size below the 2^32 work-item limit.
 inline int64_t grid_cap(int64_t blocks) { return blocks < (1 << 20) ? (blocks > 0 ? blocks : 1) : (1 << 20); }
 
-hipError_t launch_fwd(int op, const FwdArgs& p, int dtype, bool vec, hipStream_t stream);
+// wide: 512-lane workgroups instead of 256 (a different element-to-lane map, so other rounding).
+hipError_t launch_fwd(int op, const FwdArgs& p, int dtype, bool vec, bool wide, hipStream_t stream);
 hipError_t launch_bwd(int op, const BwdArgs& p, int dtype, bool vec, hipStream_t stream);
 int32_t bwd_tiles_per_row(int op, int dtype, int64_t V);
 
