@@ -3,7 +3,9 @@
 fp16 (the JSD pull request on PR #8838 validates FP32/FP16/BF16 kernels):
 every op's outputs and fp16 gradients against the fp64 oracle (gradients
 rounded to nearest even in fp16), ragged V, special rows scaled to the fp16
-range, and the fp16 -> fp32 dtype invariance of the forward.
+range, and the fp16 -> fp32 dtype invariance of the forward, for both
+forward workgroup widths (the 512-lane one of large automatic batches is also
+held to the oracle on every element).
 
 Batch invariance (the remark on PR #8838 about checking batch invariance for
 RL rollouts): with split_hint = SPLIT_INVARIANT the vocabulary is cut into
@@ -95,6 +97,47 @@ def test_fp16_forward_matches_fp32_bitwise(device):
         for x16, x32 in zip(r16["grads"], r32["grads"]):
             rne = torch.from_numpy(x32).float().half().double().numpy()
             assert np.array_equal(x16, rne, equal_nan=True), op
+
+
+@pytest.mark.parametrize("v", [4104, 4099])
+def test_wide_forward_dtype_identity(device, v):
+    """From 2048 rows up the automatic forward runs 512-lane workgroups (another element -> lane
+    map than the 256-lane one the smaller batches above take): bf16 and fp16 inputs still give
+    the forward of the same values in fp32 bit for bit, and their gradients are the RNE of the
+    fp32 ones, on whole vector batches (v = 4104) and on the predicated path of rows whose
+    pitch is not a whole number of 16-byte groups (v = 4099)."""
+    a, b, t, g = _pair(2048, v, seed=9, scale=2.0)
+    a[0, 100:300] = NINF
+    b[1, 50:90] = NINF
+    a[2] += 3e3
+    b[2] += 3e3
+    a[3, ::3] = NINF
+    for lo in (torch.bfloat16, torch.float16):
+        al, bl = a.to(lo), b.to(lo)
+        print("wide forward identity", v, lo, flush=True)
+        for op in OPS:
+            rl = run_device(op, al.to(device), bl.to(device), t.to(device), g.to(device))
+            r32 = run_device(op, al.float().to(device), bl.float().to(device), t.to(device), g.to(device))
+            assert np.array_equal(rl["out"], r32["out"], equal_nan=True), (op, lo)
+            assert np.array_equal(rl["stats"], r32["stats"], equal_nan=True), (op, lo)
+            for xl, x32 in zip(rl["grads"], r32["grads"]):
+                rne = torch.from_numpy(x32).float().to(lo).double().numpy()
+                assert np.array_equal(xl, rne, equal_nan=True), (op, lo)
+
+
+def test_wide_forward_parity(device):
+    """The 512-lane forward (2048 rows, automatic split) against the fp64 oracle on every row
+    and element, fp32 logits with a ragged vocabulary (the predicated path) and special rows."""
+    a, b, t, g = _pair(2048, 4099, seed=10, scale=3.0)
+    a[0, 7:4000:5] = NINF
+    b[5] = NINF
+    t[6] = -100
+    a[7] += 1e4
+    b[7] += 1e4
+    for op in OPS:
+        dev = run_device(op, a.to(device), b.to(device), t.to(device), g.to(device))
+        ora = run_oracle(op, f64(a), f64(b), t.numpy(), g.double().numpy())
+        check_parity(dev, ora, "f32", "%s wide fp32 2048x4099" % op)
 
 
 def test_fp16_topk_and_jsd(device):
