@@ -75,13 +75,15 @@ def test_topk_all_elements(device, dtype, v, K):
     _run_and_check(z.to(device), ids.to(device), g.to(device), z, ids, g, "v=%d K=%d" % (v, K))
 
 
+@pytest.mark.parametrize("n", [40, 2048])
 @pytest.mark.parametrize("K", [256, 257])
-def test_topk_slot_limit_of_the_fused_forward(device, K):
+def test_topk_slot_limit_of_the_fused_forward(device, K, n):
     """Unsplit rows: K = 256 slots are written by the forward pass itself (one per lane), K = 257
-    by the statistics pass and the gather launch; every element against the oracle."""
-    z, ids, g = _case(40, 1024, K, seed=K, dtype=torch.bfloat16)
-    assert B.split_parts(B.OP_LOGPROBS, 40, 1024) == 1
-    _run_and_check(z.to(device), ids.to(device), g.to(device), z, ids, g, "K=%d" % K)
+    by the statistics pass and the gather launch; every element against the oracle. 40 rows run
+    the 256-lane forward, 2048 rows the 512-lane one (its first 256 lanes hold the slots)."""
+    z, ids, g = _case(n, 1024, K, seed=K + n, dtype=torch.bfloat16)
+    assert B.split_parts(B.OP_LOGPROBS, n, 1024) == 1
+    _run_and_check(z.to(device), ids.to(device), g.to(device), z, ids, g, "K=%d n=%d" % (K, n))
 
 
 @pytest.mark.parametrize("split", [3, 16])
