@@ -23,7 +23,10 @@ ratio asserted <= 1 and the strict misses printed:
   automatic chunking and in one chunk;
 * the batch-invariant forward chunkings (fixed 1024-column chunks, and a fixed
   chunk count): every element against the oracle, and sub-batches whose logp,
-  stats and dh equal the full batch's rows bit for bit.
+  stats and dh equal the full batch's rows bit for bit;
+* the two tile heights of dz and dh (256 tokens, and 128 where 256 would fill at
+  most half of the CUs; every smaller case above takes 128): sub-batches on the
+  other side of the switch give the full batch's dh bit for bit.
 """
 
 import numpy as np
@@ -231,6 +234,23 @@ def test_linear_batch_invariant(device, split):
         assert torch.equal(lp_s, logp[r0:r1]), (split, r0, r1)
         assert torch.equal(st_s, stats[r0:r1]), (split, r0, r1)
         assert torch.equal(dh_s.view(torch.int16), dh[r0:r1].view(torch.int16)), (split, r0, r1)
+
+
+def test_linear_tile_height_keeps_dh_bits(device):
+    """dz and dh take 128-token tiles where 256-token ones would fill at most half of the CUs. The
+    8448-token batch at H = 1024 takes 256-token tiles for dh and for the dz of its two whole
+    8192-column chunks (128-token ones for the 300-column last chunk); its 1000- and 517-token
+    sub-batches take 128-token tiles throughout. With the batch-invariant forward, each
+    sub-batch's logp, stats and dh rows must be the full batch's bits: the tile height changes
+    neither a token row's place in its MFMA block nor any entry's k-sequence."""
+    h, Wm, t, g = _small(n=8448, hidden=1024, v=16684, seed=23)
+    logp, stats, dh, _ = _run(h, Wm, t, g, device, need_w=False, split=B.SPLIT_INVARIANT)
+    for r0, r1 in ((0, 1000), (4000, 4517)):
+        print("tile height", r0, r1, flush=True)
+        lp_s, st_s, dh_s, _ = _run(h[r0:r1], Wm, t[r0:r1], g[r0:r1], device, need_w=False, split=B.SPLIT_INVARIANT)
+        assert torch.equal(lp_s, logp[r0:r1]), (r0, r1)
+        assert torch.equal(st_s, stats[r0:r1]), (r0, r1)
+        assert torch.equal(dh_s.view(torch.int16), dh[r0:r1].view(torch.int16)), (r0, r1)
 
 
 def test_linear_strided_rows_broadcast_g_and_partial_stage(device):

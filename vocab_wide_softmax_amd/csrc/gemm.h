@@ -413,7 +413,7 @@ __device__ __forceinline__ void mainloop_t(const Operand& A, const Operand& B, i
   // next stage, each interleaved with a slice's MFMAs.
   constexpr int SP = BUF ? C::PIECES : 1;
   constexpr int PL = C::LOADS_PER_STAGE / SP;
-  static_assert(SP >= 1 && SP <= KQ && C::LOADS_PER_STAGE % SP == 0 && PL <= C::MFMAS, "refill pieces");
+  static_assert(SP >= 1 && SP <= KQ && C::LOADS_PER_STAGE % SP == 0 && (SP == 1 || PL <= C::MFMAS), "refill pieces");
   int cur = 0;
   for (int s = 0; s < nk; ++s) {
 #pragma unroll

@@ -45,6 +45,13 @@ typedef Cfg<256, 256, 64, 2, 4, ROWK, ROWK, 2, 1, 2> CfgFwd;  // forward
 // each refill in two pieces, one per half-stage read: 8% faster than the shared loop.
 typedef Cfg<256, 256, 32, 4, 2, ROWK, KROW, 3, 2, 2> CfgNN2;  // dh = dz W
 typedef Cfg<256, 256, 32, 4, 2, KROW, KROW, 3, 2, 2> CfgTN2;  // dW = dz^T h
+// Small batches: dz and dh over 128-token tiles, which doubles their workgroups where the
+// 256-token tiles would fill at most half of the 256 CUs (kLinHalfRound tiles or fewer). A token
+// row keeps its place in its 32-row MFMA block and every entry its k-sequence, so dz and dh are
+// the same bits with either tile height (dh stays batch invariant).
+typedef Cfg<128, 256, 64, 2, 4, ROWK, ROWK, 2, 1, 1> CfgNTs;   // dz
+typedef Cfg<128, 256, 32, 2, 4, ROWK, KROW, 3, 2, 2> CfgNN2s;  // dh
+constexpr int64_t kLinHalfRound = 128;
 
 namespace gemm {
 __device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
@@ -528,15 +535,22 @@ int32_t lin_bwd_tiles_per_chunk(int64_t V, int split_hint) {
 hipError_t launch_lin_bwd(LinArgs p, int split_hint, uint16_t* dh, uint16_t* dW, hipStream_t stream) {
   const int64_t C = (int64_t)lin_bwd_tiles_per_chunk(p.V, split_hint) * CfgNT::BN;
   const int64_t nchunks = (p.V + C - 1) / C;
+  static_assert(CfgNTs::BN == CfgNT::BN && CfgNN2s::BN == CfgNN2::BN, "small-batch tiles differ in height only");
   const int64_t ntt = (p.N + CfgNT::BM - 1) / CfgNT::BM, nht = (p.H + CfgNN2::BN - 1) / CfgNN2::BN;
+  const int64_t ntt_s = (p.N + CfgNTs::BM - 1) / CfgNTs::BM;
+  const bool dh_small = ntt * nht <= kLinHalfRound;
   hipError_t e;
   for (int64_t c = 0; c < nchunks; ++c) {
     p.v0 = c * C;
     p.cw = p.V - p.v0 < C ? p.V - p.v0 : C;
     const int64_t nvt = (p.cw + CfgNT::BN - 1) / CfgNT::BN;
     const int64_t kz = (p.cw + 7) / 8 * 8;  // reduction length of dh: the zero-padded chunk width
-    hipLaunchKernelGGL((lin_dz_kernel<CfgNT>), dim3((uint32_t)(ntt * nvt)), dim3(CfgNT::NT), lds_bytes<CfgNT>(),
-                       stream, p);
+    if (ntt * nvt <= kLinHalfRound)
+      hipLaunchKernelGGL((lin_dz_kernel<CfgNTs>), dim3((uint32_t)(ntt_s * nvt)), dim3(CfgNTs::NT),
+                         lds_bytes<CfgNTs>(), stream, p);
+    else
+      hipLaunchKernelGGL((lin_dz_kernel<CfgNT>), dim3((uint32_t)(ntt * nvt)), dim3(CfgNT::NT), lds_bytes<CfgNT>(),
+                         stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t plane = p.dzl - p.dzh;
     if (dW) {
@@ -555,9 +569,12 @@ hipError_t launch_lin_bwd(LinArgs p, int split_hint, uint16_t* dh, uint16_t* dW,
       GemmArgs g{Operand{p.dzh, p.ldc, p.N, kz, plane}, Operand{p.W + p.v0 * p.ldw, p.ldw, p.H, p.cw}, dh, p.dh_acc,
                  p.H, p.N, p.H, kz, mode};
       if (mode == kDhFirst || mode == kDhAdd) g.ldc = p.H;
-      const int64_t blocks = ntt * nht;
-      hipLaunchKernelGGL((gemm_pair_kernel<CfgNN2>), dim3((uint32_t)blocks), dim3(CfgNN2::NT), lds_bytes<CfgNN2>(),
-                         stream, g);
+      if (dh_small)
+        hipLaunchKernelGGL((gemm_pair_kernel<CfgNN2s>), dim3((uint32_t)(ntt_s * nht)), dim3(CfgNN2s::NT),
+                           lds_bytes<CfgNN2s>(), stream, g);
+      else
+        hipLaunchKernelGGL((gemm_pair_kernel<CfgNN2>), dim3((uint32_t)(ntt * nht)), dim3(CfgNN2::NT),
+                           lds_bytes<CfgNN2>(), stream, g);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
