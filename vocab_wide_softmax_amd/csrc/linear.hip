@@ -17,8 +17,9 @@
 // pass (lin_dz_kernel, A = h rows, B = W rows, so a lane's 32 consecutive vocabulary columns
 // make coalesced stores of dz [N, chunk]), kept as a bf16 (hi, lo) pair; then dW of the chunk's
 // vocabulary rows = dz^T h, and dh += dz W_chunk summed in fp32 over the chunks, by
-// gemm_pair_kernel (both planes of dz contracted into one fp32 accumulator), reading the
-// transposed operands through gfx950's transposing LDS reads (gemm.h).
+// gemm_pair_kernel (both planes of dz contracted into one fp32 accumulator; a chunk's dW and dh
+// tiles share one grid, gemm_pair2_kernel, when both are wanted), reading the transposed
+// operands through gfx950's transposing LDS reads (gemm.h).
 #include <algorithm>
 
 #include "device.h"
@@ -365,14 +366,14 @@ __device__ __forceinline__ void pair_tile(int64_t b, int64_t ntm, int64_t ntn, i
   tn = b - tm * ntn;
 }
 
-// C = A B^T over K, A a split (hi, lo) pair; dW rows of a chunk (bf16 stores) and dh of a chunk
-// (stored, or added to the fp32 running sum over the chunks; the last chunk rounds the sum to bf16).
+// C = A B^T over K, A a split (hi, lo) pair, for the tile of block b; dW rows of a chunk (bf16
+// stores) and dh of a chunk (stored, or added to the fp32 running sum over the chunks; the last
+// chunk rounds the sum to bf16).
 template <class C>
-__global__ __launch_bounds__(C::NT) void gemm_pair_kernel(GemmArgs g) {
-  extern __shared__ __align__(16) char lds[];
+__device__ __forceinline__ void pair_block(const GemmArgs& g, int64_t b, char* lds) {
   const int64_t ntm = (g.M + C::BM - 1) / C::BM, ntn = (g.Nc + C::BN - 1) / C::BN;
   int64_t tm, tn;
-  pair_tile((int64_t)blockIdx.x, ntm, ntn, tm, tn);
+  pair_tile(b, ntm, ntn, tm, tn);
   const int64_t m0 = tm * C::BM, n0 = tn * C::BN;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -451,6 +452,26 @@ __global__ __launch_bounds__(C::NT) void gemm_pair_kernel(GemmArgs g) {
         }
       }
     }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void gemm_pair_kernel(GemmArgs g) {
+  extern __shared__ __align__(16) char lds[];
+  pair_block<C>(g, (int64_t)blockIdx.x, lds);
+}
+
+// A chunk's dW and dh contractions in one launch: blocks [0, nb1) take the tiles of g1 (dW), the
+// rest those of g2 (dh). The two read the same dz planes and write disjoint outputs, so running
+// them as one grid changes no result; it removes one kernel's last-round tail per chunk (the
+// dh tiles start on the CUs the dW tiles leave). nb1 is a multiple of 8, so a block's XCD
+// (b mod 8) is the same in either numbering.
+template <class C1, class C2>
+__global__ __launch_bounds__(C1::NT) void gemm_pair2_kernel(GemmArgs g1, GemmArgs g2, int64_t nb1) {
+  static_assert(C1::NT == C2::NT, "one workgroup size");
+  extern __shared__ __align__(16) char lds[];
+  const int64_t b = (int64_t)blockIdx.x;
+  if (b < nb1) pair_block<C1>(g1, b, lds);
+  else pair_block<C2>(g2, b - nb1, lds);
 }
 
 // ---- host-side launch ---------------------------------------------------------------------
@@ -553,28 +574,35 @@ hipError_t launch_lin_bwd(LinArgs p, int split_hint, uint16_t* dh, uint16_t* dW,
                          stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t plane = p.dzl - p.dzh;
+    // dW[v0 + v, k] = sum_n dz[n, v] h[n, k]: A(v, n) = dz[n, v] (KROW pair; its rows are the
+    // zero-padded width kz, so that every 8-row load stays inside the planes), B(k, n) = h[n, k] (KROW)
+    const GemmArgs gw{Operand{p.dzh, p.ldc, kz, p.N, plane}, Operand{p.h, p.ldh, p.H, p.N}, dW ? dW + p.v0 * p.H : nullptr, nullptr,
+                      p.H, p.cw, p.H, p.N, kDhStore};
+    const int64_t nbw = nvt * nht;
+    // dh[n, k] += sum_v dz[n, v] W[v0 + v, k]: A = dz (ROWK pair), B(k, v) = W[v0 + v, k] (KROW)
+    const int32_t mode = nchunks == 1 ? kDhStore : (c == 0 ? kDhFirst : (c + 1 < nchunks ? kDhAdd : kDhLast));
+    GemmArgs gh{Operand{p.dzh, p.ldc, p.N, kz, plane}, Operand{p.W + p.v0 * p.ldw, p.ldw, p.H, p.cw}, dh, p.dh_acc,
+                p.H, p.N, p.H, kz, mode};
+    if (mode == kDhFirst || mode == kDhAdd) gh.ldc = p.H;
+    if (dW && dh && !dh_small && nbw % 8 == 0) {
+      static_assert(CfgTN2::LDS_BYTES == CfgNN2::LDS_BYTES, "one LDS size");
+      hipLaunchKernelGGL((gemm_pair2_kernel<CfgTN2, CfgNN2>), dim3((uint32_t)(nbw + ntt * nht)), dim3(CfgTN2::NT),
+                         lds_bytes<CfgTN2>(), stream, gw, gh, nbw);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      continue;
+    }
     if (dW) {
-      // dW[v0 + v, k] = sum_n dz[n, v] h[n, k]: A(v, n) = dz[n, v] (KROW pair; its rows are the
-      // zero-padded width kz, so that every 8-row load stays inside the planes), B(k, n) = h[n, k] (KROW)
-      GemmArgs g{Operand{p.dzh, p.ldc, kz, p.N, plane}, Operand{p.h, p.ldh, p.H, p.N}, dW + p.v0 * p.H, nullptr,
-                 p.H, p.cw, p.H, p.N, kDhStore};
-      const int64_t blocks = nvt * nht;
-      hipLaunchKernelGGL((gemm_pair_kernel<CfgTN2>), dim3((uint32_t)blocks), dim3(CfgTN2::NT), lds_bytes<CfgTN2>(),
-                         stream, g);
+      hipLaunchKernelGGL((gemm_pair_kernel<CfgTN2>), dim3((uint32_t)nbw), dim3(CfgTN2::NT), lds_bytes<CfgTN2>(),
+                         stream, gw);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (dh) {
-      // dh[n, k] += sum_v dz[n, v] W[v0 + v, k]: A = dz (ROWK pair), B(k, v) = W[v0 + v, k] (KROW)
-      const int32_t mode = nchunks == 1 ? kDhStore : (c == 0 ? kDhFirst : (c + 1 < nchunks ? kDhAdd : kDhLast));
-      GemmArgs g{Operand{p.dzh, p.ldc, p.N, kz, plane}, Operand{p.W + p.v0 * p.ldw, p.ldw, p.H, p.cw}, dh, p.dh_acc,
-                 p.H, p.N, p.H, kz, mode};
-      if (mode == kDhFirst || mode == kDhAdd) g.ldc = p.H;
       if (dh_small)
         hipLaunchKernelGGL((gemm_pair_kernel<CfgNN2s>), dim3((uint32_t)(ntt_s * nht)), dim3(CfgNN2s::NT),
-                           lds_bytes<CfgNN2s>(), stream, g);
+                           lds_bytes<CfgNN2s>(), stream, gh);
       else
         hipLaunchKernelGGL((gemm_pair_kernel<CfgNN2>), dim3((uint32_t)(ntt * nht)), dim3(CfgNN2::NT),
-                           lds_bytes<CfgNN2>(), stream, g);
+                           lds_bytes<CfgNN2>(), stream, gh);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
