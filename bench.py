@@ -619,7 +619,8 @@ def _rep(x, y, c, kind):
     from oracle import compare
 
     r = compare.check(x, y, c, kind)
-    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+    return {k: (float("%.3g" % v) if k == "max_rel" else round(v, 4)) if isinstance(v, float) else v
+            for k, v in r.items()}
 
 
 def _oracle_op(op, a, b, t, g):

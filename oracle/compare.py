@@ -106,6 +106,10 @@ def check(x, y, c, kind):
     kind is "f32", "bf16" or "f16". Returns a dict with the element count, the
     number of elements missing the strict bound, the number failing both bounds,
     the NaN / inf placement mismatches, and the worst ratio of error to allowance.
+    For fp32 values it also reports max_rel, the largest |x - y| / |y| over finite
+    nonzero y: the form of the fp32 output errors against a float64 CPU reference
+    that the description of PR #8838 quotes under "Numerics" (None for bf16 and fp16,
+    whose relative error is the output rounding itself).
     """
     cfac = COND
     x = np.asarray(x, dtype=np.float64).ravel()
@@ -137,6 +141,10 @@ def check(x, y, c, kind):
     else:
         raise ValueError(kind)
     worst = float(np.max(err / allow)) if err.size else 0.0
+    max_rel = None
+    if kind == "f32":
+        nz = yf != 0
+        max_rel = float(np.max(np.abs(xf[nz] - yf[nz]) / np.abs(yf[nz]))) if np.any(nz) else 0.0
     return {
         "n": int(x.size),
         "strict_miss": int(np.count_nonzero(~strict_ok)),
@@ -144,4 +152,5 @@ def check(x, y, c, kind):
         "nan_mismatch": nan_mis,
         "inf_mismatch": inf_mis,
         "worst": worst,
+        "max_rel": max_rel,
     }

@@ -358,6 +358,22 @@ def test_check_accepts_exact_and_rejects_planted_errors():
     assert compare.check(off2, yb, np.zeros(3), "bf16")["fail"] == 3
 
 
+def test_check_reports_max_relative_error_of_fp32_values():
+    """max_rel is the largest |x - y| / |y| over finite nonzero y; zeros, inf and NaN take no part."""
+    y = np.array([2.0, -4.0, 0.0, np.inf, np.nan, 0.5])
+    x = y.copy()
+    x[0] = 2.0 * (1 + 3e-7)
+    x[1] = -4.0 * (1 - 1e-6)
+    x[2] = 1e-30
+    x[5] = 0.5 * (1 + 2e-7)
+    r = compare.check(x, y, np.abs(np.nan_to_num(y, posinf=0.0)), "f32")
+    assert abs(r["max_rel"] - 1e-6) < 1e-12
+    assert compare.check(y, y, np.zeros(6), "f32")["max_rel"] == 0.0
+    assert compare.check(np.zeros(2), np.zeros(2), np.zeros(2), "f32")["max_rel"] == 0.0
+    yb = compare.bf16_rne(np.array([1.0, 3.0]))
+    assert compare.check(yb, yb, np.zeros(2), "bf16")["max_rel"] is None
+
+
 # ------------------------------------------------------ planted-mistake detection
 
 def _entropy_bwd_dropped_H(z, g):
