@@ -24,6 +24,8 @@ ratio asserted <= 1 and the strict misses printed:
 * the batch-invariant forward chunkings (fixed 1024-column chunks, and a fixed
   chunk count): every element against the oracle, and sub-batches whose logp,
   stats and dh equal the full batch's rows bit for bit;
+* a chunk's dW and dh as one grid (4096 x 2304 x 8192) against each gradient alone:
+  the same bits;
 * the two tile heights of dz and dh (256 tokens, and 128 where 256 would fill at
   most half of the CUs; every smaller case above takes 128): sub-batches on the
   other side of the switch give the full batch's dh bit for bit.
@@ -124,6 +126,33 @@ def test_linear_gradient_subsets(device):
     _, _, none_h, dW_only = _run(h, Wm, t, g, device, need_h=False)
     assert none_w is None and none_h is None
     assert torch.equal(dh_both, dh_only) and torch.equal(dW_both, dW_only)
+
+
+def test_linear_grouped_dw_dh_grid_keeps_bits(device):
+    """4096 tokens, hidden 2304, vocabulary 8192: one chunk of 32 vocabulary tiles x 9 hidden
+    tiles (288 dW blocks, a multiple of 8) and 16 x 9 token tiles for dh (above the small-batch
+    switch), so a backward asking for both gradients runs them as one grid (dW tiles, then dh
+    tiles); asking for one at a time runs each alone. Both must give the same bits, and sampled
+    rows of both gradients must match the oracle."""
+    gen = torch.Generator().manual_seed(21)
+    h = torch.randn(4096, 2304, generator=gen).to(torch.bfloat16)
+    Wm = (0.03 * torch.randn(8192, 2304, generator=gen)).to(torch.bfloat16)
+    t = torch.randint(0, 8192, (4096,), generator=gen)
+    t[::53] = -100
+    g = torch.randn(4096, generator=gen)
+    _, _, dh_both, dW_both = _run(h, Wm, t, g, device)
+    _, _, dh_only, _ = _run(h, Wm, t, g, device, need_w=False)
+    _, _, _, dW_only = _run(h, Wm, t, g, device, need_h=False)
+    assert torch.equal(dh_both, dh_only) and torch.equal(dW_both, dW_only)
+    hh, hw, ht, hg = f64(h), f64(Wm), t.numpy(), g.double().numpy()
+    rows = np.array([0, 1, 777, 2048, 4095])
+    _assert_ok(compare.check(f64(dh_both[torch.from_numpy(rows).to(device)]),
+                             OL.linear_logp_bwd_dh(hh, hw, ht, hg, rows=rows),
+                             OL.cond_linear_dh(hh, hw, ht, hg, rows=rows), "bf16"), "grouped dh rows")
+    cols = np.unique(np.concatenate([ht[ht >= 0][:6], [0, 255, 256, 4097, 8191]]))
+    dw_ref, dw_c = OL.linear_logp_bwd_dw_cond(hh, hw, ht, hg, vocab_rows=cols)
+    _assert_ok(compare.check(f64(dW_both[torch.from_numpy(cols).to(device)]), dw_ref, dw_c, "bf16"),
+               "grouped dW rows")
 
 
 def test_linear_full_width_512_tokens(device):
